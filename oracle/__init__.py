@@ -1,0 +1,172 @@
+"""fp64 CPU oracle for gated-delta-rule draft verification (ctypes binding).
+
+TEST INFRASTRUCTURE ONLY: imported by tests/, by the smoke check and by the
+benchmark's CPU-baseline leg.  The product path (the HIP library and its
+Python binding) never imports, links or calls anything here, and nothing here
+imports the product path.
+
+Every function takes numpy arrays holding the exact values handed to the GPU
+(fp32, bf16 inputs widened exactly to fp32) and computes in fp64 by walking
+each root-to-node path token by token (see oracle.c for the definition and its
+citations).  ``Oracle(path)`` binds one compiled copy of oracle.c; the
+module-level functions use the default build, oracle/liboracle.so.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+from . import build as _build
+
+__all__ = ["Oracle", "default", "verify", "commit", "chain_decode", "verify_dfs",
+           "gather", "BAD_PARENT", "BAD_ACCEPTED", "BAD_SLOT"]
+
+_f32p = ctypes.POINTER(ctypes.c_float)
+_f64p = ctypes.POINTER(ctypes.c_double)
+_i32p = ctypes.POINTER(ctypes.c_int32)
+
+BAD_PARENT = 1
+BAD_ACCEPTED = 2
+BAD_SLOT = 4
+
+
+def _threads(n):
+    return int(n) if n else (os.cpu_count() or 1)
+
+
+def _f32(x):
+    return np.ascontiguousarray(x, dtype=np.float32)
+
+
+def _i32(x):
+    return np.ascontiguousarray(x, dtype=np.int32)
+
+
+def _p(x, t):
+    return None if x is None else x.ctypes.data_as(t)
+
+
+class Oracle:
+    """One compiled copy of oracle.c."""
+
+    def __init__(self, path: str):
+        lib = ctypes.CDLL(path)
+        i = ctypes.c_int
+        lib.oracle_verify.argtypes = [i, i, i, i, i, _f32p, _f32p, _f32p, _f32p, _f32p, _f32p,
+                                      _i32p, _f64p, _f64p, i]
+        lib.oracle_commit.argtypes = [i, i, i, i, i, _f32p, _f32p, _f32p, _f32p, _f32p, _i32p,
+                                      _i32p, _f64p, i]
+        lib.oracle_chain_decode.argtypes = [i, i, i, i, i, _f32p, _f32p, _f32p, _f32p, _f32p,
+                                            _f32p, _f64p, i]
+        lib.oracle_verify_dfs.argtypes = [i, i, i, i, i, _f32p, _f32p, _f32p, _f32p, _f32p,
+                                          _f32p, _i32p, _f64p, i]
+        lib.oracle_gather.argtypes = [i, i, i, i, i, i, i, _f32p, _i32p, _f32p, _f64p, _f32p, i]
+        for f in ("oracle_verify", "oracle_commit", "oracle_chain_decode",
+                  "oracle_verify_dfs", "oracle_gather"):
+            getattr(lib, f).restype = ctypes.c_int
+        self.lib = lib
+        self.path = path
+
+    def verify(self, q, k, v, a, beta, S0, parent=None, want_states=False, nthreads=None):
+        """All node outputs o[b, n, h, :] = S_n q_n (fp64), and optionally every
+        node state S_n.  parent=None means a chain.  Returns (o, states, status)."""
+        q, k, v, a, beta, S0 = map(_f32, (q, k, v, a, beta, S0))
+        B, T, H, dk = q.shape
+        dv = v.shape[-1]
+        par = None if parent is None else _i32(parent)
+        o = np.zeros((B, T, H, dv), dtype=np.float64)
+        st = np.zeros((B, T, H, dv, dk), dtype=np.float64) if want_states else None
+        status = self.lib.oracle_verify(B, T, H, dk, dv, _p(q, _f32p), _p(k, _f32p), _p(v, _f32p),
+                                        _p(a, _f32p), _p(beta, _f32p), _p(S0, _f32p),
+                                        _p(par, _i32p), _p(o, _f64p), _p(st, _f64p),
+                                        _threads(nthreads))
+        return o, st, status
+
+    def commit(self, k, v, a, beta, S0, accepted, parent=None, nthreads=None):
+        """Committed state per (b, h): the state at accepted[b], S0 when -1.
+        Returns (S_out fp64 [B, H, dv, dk], status)."""
+        k, v, a, beta, S0 = map(_f32, (k, v, a, beta, S0))
+        B, T, H, dk = k.shape
+        dv = v.shape[-1]
+        par = None if parent is None else _i32(parent)
+        acc = _i32(accepted)
+        S_out = np.zeros((B, H, dv, dk), dtype=np.float64)
+        status = self.lib.oracle_commit(B, T, H, dk, dv, _p(k, _f32p), _p(v, _f32p), _p(a, _f32p),
+                                        _p(beta, _f32p), _p(S0, _f32p), _p(par, _i32p),
+                                        _p(acc, _i32p), _p(S_out, _f64p), _threads(nthreads))
+        return S_out, status
+
+    def chain_decode(self, q, k, v, a, beta, S0, nthreads=None):
+        """Sequential decode with one running state: o_n read after token n."""
+        q, k, v, a, beta, S0 = map(_f32, (q, k, v, a, beta, S0))
+        B, T, H, dk = q.shape
+        dv = v.shape[-1]
+        o = np.zeros((B, T, H, dv), dtype=np.float64)
+        self.lib.oracle_chain_decode(B, T, H, dk, dv, _p(q, _f32p), _p(k, _f32p), _p(v, _f32p),
+                                     _p(a, _f32p), _p(beta, _f32p), _p(S0, _f32p), _p(o, _f64p),
+                                     _threads(nthreads))
+        return o
+
+    def verify_dfs(self, q, k, v, a, beta, S0, parent, nthreads=None):
+        """Branch-by-branch depth-first traversal, one state per tree edge."""
+        q, k, v, a, beta, S0 = map(_f32, (q, k, v, a, beta, S0))
+        B, T, H, dk = q.shape
+        dv = v.shape[-1]
+        par = _i32(parent)
+        o = np.zeros((B, T, H, dv), dtype=np.float64)
+        status = self.lib.oracle_verify_dfs(B, T, H, dk, dv, _p(q, _f32p), _p(k, _f32p),
+                                            _p(v, _f32p), _p(a, _f32p), _p(beta, _f32p),
+                                            _p(S0, _f32p), _p(par, _i32p), _p(o, _f64p),
+                                            _threads(nthreads))
+        return o, status
+
+    def gather(self, pool, slot, queries=None, want_states=True, nthreads=None):
+        """Reads at chosen pool slots: (o fp64 [B, P, H, Qn, dv] or None,
+        states fp32 [B, P, H, dv, dk] or None, status)."""
+        pool = _f32(pool)
+        slot = _i32(slot)
+        num_slots, H, dv, dk = pool.shape
+        B, P = slot.shape
+        qv = None if queries is None else _f32(queries)
+        Qn = 0 if qv is None else qv.shape[3]
+        o = None if qv is None else np.zeros((B, P, H, Qn, dv), dtype=np.float64)
+        st = np.zeros((B, P, H, dv, dk), dtype=np.float32) if want_states else None
+        status = self.lib.oracle_gather(B, P, H, dk, dv, num_slots, Qn, _p(pool, _f32p),
+                                        _p(slot, _i32p), _p(qv, _f32p), _p(o, _f64p),
+                                        _p(st, _f32p), _threads(nthreads))
+        return o, st, status
+
+
+_DEFAULT = None
+
+
+def default() -> Oracle:
+    """The oracle built from oracle.c into oracle/liboracle.so (built on first use)."""
+    global _DEFAULT
+    if _DEFAULT is None:
+        if not os.path.exists(_build.LIB):
+            _build.build()
+        _DEFAULT = Oracle(_build.LIB)
+    return _DEFAULT
+
+
+def verify(*args, **kw):
+    return default().verify(*args, **kw)
+
+
+def commit(*args, **kw):
+    return default().commit(*args, **kw)
+
+
+def chain_decode(*args, **kw):
+    return default().chain_decode(*args, **kw)
+
+
+def verify_dfs(*args, **kw):
+    return default().verify_dfs(*args, **kw)
+
+
+def gather(*args, **kw):
+    return default().gather(*args, **kw)

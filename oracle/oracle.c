@@ -1,0 +1,401 @@
+/*
+ * fp64 CPU oracle for draft verification through a gated-delta-rule layer.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may link, load or
+ * call this file: it is used by tests/, by the smoke check and by the
+ * benchmark's CPU-baseline leg, and by nothing else.  It shares no code with
+ * the HIP library.
+ *
+ * What it computes is the plain definition, walked token by token:
+ *
+ *   S_n = a_n * S_{p(n)} * (I - b_n k_n k_n^T) + b_n v_n k_n^T,   o_n = S_n q_n,
+ *   S_{p(n)} = S0 when p(n) = -1,
+ *
+ * with S a d_v x d_k matrix (row-major, S[i][j], i over values, j over keys).
+ * This is the gated delta rule that the Bole page (arXiv 2608.01651, section
+ * IV, context of Eq. (2)) says is executed sequentially over the draft tree;
+ * its closed form O = D_P Q S_pre + C (I+G)^{-1} D_beta (V - D_P K S_pre) of
+ * Eq. (2) uses the transposed orientation S_pre = S0^T.  The oracle never
+ * uses the closed form: every node's state is rebuilt from S0 along the
+ * node's root-to-node path.
+ *
+ * Commit (Bole page, summary: only the post-sampling selected state is
+ * materialised) is the walk's state at the accepted node; gather (ReaDy page,
+ * Fig. 2a-3: position-specific reads from committed recurrent states) is a
+ * copy of a pool entry plus o = S q for each query.
+ *
+ * Inputs are the exact fp32 values handed to the GPU (bf16 inputs arrive as
+ * their exact fp32 widening); all arithmetic is fp64.
+ *
+ * Status bits (returned, OR-ed): 1 = a parent index outside [-1, n-1],
+ * 2 = an accepted index outside [-1, T-1], 4 = a slot index outside
+ * [0, num_slots).  The outputs of an affected sequence (or position) are left
+ * untouched.
+ */
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define OR_BAD_PARENT 1
+#define OR_BAD_ACCEPTED 2
+#define OR_BAD_SLOT 4
+
+/* ---------------------------------------------------------------- threads */
+
+typedef struct {
+    void (*fn)(void* ctx, long item, double* work);
+    void* ctx;
+    long n_items;
+    long next;
+    long work_doubles;
+    pthread_mutex_t lock;
+} pool_t;
+
+static void* pool_worker(void* arg) {
+    pool_t* p = (pool_t*)arg;
+    double* work = (double*)malloc(sizeof(double) * (size_t)(p->work_doubles > 0 ? p->work_doubles : 1));
+    for (;;) {
+        pthread_mutex_lock(&p->lock);
+        long it = p->next++;
+        pthread_mutex_unlock(&p->lock);
+        if (it >= p->n_items) break;
+        p->fn(p->ctx, it, work);
+    }
+    free(work);
+    return NULL;
+}
+
+/* Run fn(ctx, item, work) for item in [0, n_items) on nthreads threads.  Each
+ * thread owns a private work buffer of work_doubles doubles. */
+static void run_items(void (*fn)(void*, long, double*), void* ctx, long n_items,
+                      long work_doubles, int nthreads) {
+    pool_t p;
+    p.fn = fn;
+    p.ctx = ctx;
+    p.n_items = n_items;
+    p.next = 0;
+    p.work_doubles = work_doubles;
+    pthread_mutex_init(&p.lock, NULL);
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads > 256) nthreads = 256;
+    if ((long)nthreads > n_items) nthreads = (int)(n_items > 0 ? n_items : 1);
+    pthread_t tid[256];
+    int started = 0;
+    for (int t = 1; t < nthreads; ++t)
+        if (pthread_create(&tid[t], NULL, pool_worker, &p) == 0) started = t;
+        else break;
+    pool_worker(&p);
+    for (int t = 1; t <= started; ++t) pthread_join(tid[t], NULL);
+    pthread_mutex_destroy(&p.lock);
+}
+
+/* ------------------------------------------------------- the definition */
+
+/* One token of the gated delta rule on S (dv x dk, row-major):
+ *   x = S k;   S <- a * (S - b x k^T) + b v k^T
+ * which is S <- a S (I - b k k^T) + b v k^T with x formed before the update. */
+static void gdr_token(double* S, int dk, int dv, const float* k, const float* v,
+                      double a, double b, double* x) {
+    for (int i = 0; i < dv; ++i) {
+        double s = 0.0;
+        for (int j = 0; j < dk; ++j) s += S[(size_t)i * dk + j] * (double)k[j];
+        x[i] = s;
+    }
+    for (int i = 0; i < dv; ++i) {
+        double bx = b * x[i];
+        double bv = b * (double)v[i];
+        double* row = S + (size_t)i * dk;
+        for (int j = 0; j < dk; ++j) {
+            double kj = (double)k[j];
+            row[j] = a * (row[j] - bx * kj) + bv * kj;
+        }
+    }
+}
+
+/* out[i] = sum_j S[i][j] * q[j] */
+static void read_state(const double* S, int dk, int dv, const float* q, double* out) {
+    for (int i = 0; i < dv; ++i) {
+        double s = 0.0;
+        for (int j = 0; j < dk; ++j) s += S[(size_t)i * dk + j] * (double)q[j];
+        out[i] = s;
+    }
+}
+
+/* parent of node n in sequence b; a NULL parent array means a chain. */
+static int parent_of(const int32_t* parent, int T, int b, int n) {
+    return parent ? parent[(size_t)b * T + n] : n - 1;
+}
+
+static int parents_valid(const int32_t* parent, int T, int b) {
+    if (!parent) return 1;
+    for (int n = 0; n < T; ++n) {
+        int p = parent[(size_t)b * T + n];
+        if (p < -1 || p >= n) return 0;
+    }
+    return 1;
+}
+
+/* Root-to-n path into path[0..len-1]; returns len (node count, root first). */
+static int root_path(const int32_t* parent, int T, int b, int n, int* path) {
+    int len = 0;
+    for (int m = n; m >= 0; m = parent_of(parent, T, b, m)) path[len++] = m;
+    for (int i = 0; i < len / 2; ++i) {
+        int t = path[i];
+        path[i] = path[len - 1 - i];
+        path[len - 1 - i] = t;
+    }
+    return len;
+}
+
+typedef struct {
+    int B, T, H, dk, dv;
+    const float *q, *k, *v, *a, *beta, *S0;
+    const int32_t* parent;
+    const int32_t* accepted;
+    double* o;
+    double* states;
+    double* S_out;
+    const unsigned char* seq_ok;
+} walk_ctx;
+
+/* Offsets of the [B, T, H, d] node tensors and [B, T, H] gates. */
+#define NODE_VEC(base, c, b, n, h, d) ((base) + ((((size_t)(b) * (c)->T + (n)) * (c)->H + (h)) * (size_t)(d)))
+#define NODE_GATE(base, c, b, n, h) ((base)[(((size_t)(b) * (c)->T + (n)) * (c)->H + (h))])
+
+/* Rebuild S at node n of (b, h) from S0 along the root-to-n path. */
+static void walk_to(const walk_ctx* c, int b, int h, int n, double* S, double* x, int* path) {
+    const size_t dd = (size_t)c->dk * c->dv;
+    const float* s0 = c->S0 + ((size_t)b * c->H + h) * dd;
+    for (size_t e = 0; e < dd; ++e) S[e] = (double)s0[e];
+    if (n < 0) return;
+    int len = root_path(c->parent, c->T, b, n, path);
+    for (int i = 0; i < len; ++i) {
+        int m = path[i];
+        gdr_token(S, c->dk, c->dv, NODE_VEC(c->k, c, b, m, h, c->dk), NODE_VEC(c->v, c, b, m, h, c->dv),
+                  (double)NODE_GATE(c->a, c, b, m, h), (double)NODE_GATE(c->beta, c, b, m, h), x);
+    }
+}
+
+static void verify_item(void* vctx, long item, double* work) {
+    const walk_ctx* c = (const walk_ctx*)vctx;
+    int b = (int)(item / c->H), h = (int)(item % c->H);
+    if (!c->seq_ok[b]) return;
+    const size_t dd = (size_t)c->dk * c->dv;
+    double* S = work;
+    double* x = S + dd;
+    int* path = (int*)(x + c->dv);
+    for (int n = 0; n < c->T; ++n) {
+        walk_to(c, b, h, n, S, x, path);
+        read_state(S, c->dk, c->dv, NODE_VEC(c->q, c, b, n, h, c->dk), NODE_VEC(c->o, c, b, n, h, c->dv));
+        if (c->states) memcpy(c->states + ((((size_t)b * c->T + n) * c->H + h) * dd), S, dd * sizeof(double));
+    }
+}
+
+static long walk_work(int T, int dk, int dv) {
+    /* S, x, then T ints of path (stored in doubles) */
+    return (long)dk * dv + dv + T + 1;
+}
+
+/*
+ * Verify every draft node: o[b, n, h, :] = S_n q_n for all nodes.
+ *   q, k: [B, T, H, dk]; v: [B, T, H, dv]; a, beta: [B, T, H]; S0: [B, H, dv, dk]
+ *   parent: [B, T] (parent[n] in [-1, n-1]) or NULL for a chain (parent[n] = n-1)
+ *   o: [B, T, H, dv] fp64; states: [B, T, H, dv, dk] fp64 or NULL
+ * Returns status bits (OR_BAD_PARENT).
+ */
+int oracle_verify(int B, int T, int H, int dk, int dv, const float* q, const float* k, const float* v,
+                  const float* a, const float* beta, const float* S0, const int32_t* parent, double* o,
+                  double* states, int nthreads) {
+    if (B <= 0 || T <= 0 || H <= 0) return 0;
+    unsigned char* ok = (unsigned char*)malloc((size_t)B);
+    int status = 0;
+    for (int b = 0; b < B; ++b) {
+        ok[b] = (unsigned char)parents_valid(parent, T, b);
+        if (!ok[b]) status |= OR_BAD_PARENT;
+    }
+    walk_ctx c = {B, T, H, dk, dv, q, k, v, a, beta, S0, parent, NULL, o, states, NULL, ok};
+    run_items(verify_item, &c, (long)B * H, walk_work(T, dk, dv), nthreads);
+    free(ok);
+    return status;
+}
+
+static void commit_item(void* vctx, long item, double* work) {
+    const walk_ctx* c = (const walk_ctx*)vctx;
+    int b = (int)(item / c->H), h = (int)(item % c->H);
+    if (!c->seq_ok[b]) return;
+    const size_t dd = (size_t)c->dk * c->dv;
+    double* S = work;
+    double* x = S + dd;
+    int* path = (int*)(x + c->dv);
+    walk_to(c, b, h, c->accepted[b], S, x, path);
+    memcpy(c->S_out + ((size_t)b * c->H + h) * dd, S, dd * sizeof(double));
+}
+
+/*
+ * Committed state at the accepted node: S_out[b, h] = S_{accepted[b]} of the
+ * walk, or S0[b, h] when accepted[b] = -1.  S_out: [B, H, dv, dk] fp64.
+ * Returns status bits (OR_BAD_PARENT, OR_BAD_ACCEPTED).
+ */
+int oracle_commit(int B, int T, int H, int dk, int dv, const float* k, const float* v, const float* a,
+                  const float* beta, const float* S0, const int32_t* parent, const int32_t* accepted,
+                  double* S_out, int nthreads) {
+    if (B <= 0 || H <= 0) return 0;
+    unsigned char* ok = (unsigned char*)malloc((size_t)B);
+    int status = 0;
+    for (int b = 0; b < B; ++b) {
+        int n = accepted[b];
+        int good_acc = (n >= -1 && n < T);
+        int good_par = (T <= 0) ? 1 : parents_valid(parent, T, b);
+        if (!good_acc) status |= OR_BAD_ACCEPTED;
+        if (!good_par) status |= OR_BAD_PARENT;
+        ok[b] = (unsigned char)(good_acc && good_par);
+    }
+    walk_ctx c = {B, T, H, dk, dv, NULL, k, v, a, beta, S0, parent, accepted, NULL, NULL, S_out, ok};
+    run_items(commit_item, &c, (long)B * H, walk_work(T > 0 ? T : 1, dk, dv), nthreads);
+    free(ok);
+    return status;
+}
+
+/* ------------------------------------------- independent cross-checks */
+
+typedef struct {
+    int B, T, H, dk, dv;
+    const float *q, *k, *v, *a, *beta, *S0;
+    const int32_t* parent;
+    double* o;
+} seq_ctx;
+
+/* Sequential chain decode: one running state, updated token by token,
+ * read after every token.  The ordinary autoregressive recurrence. */
+static void chain_item(void* vctx, long item, double* work) {
+    const seq_ctx* c = (const seq_ctx*)vctx;
+    int b = (int)(item / c->H), h = (int)(item % c->H);
+    const size_t dd = (size_t)c->dk * c->dv;
+    double* S = work;
+    double* x = S + dd;
+    const float* s0 = c->S0 + ((size_t)b * c->H + h) * dd;
+    for (size_t e = 0; e < dd; ++e) S[e] = (double)s0[e];
+    for (int n = 0; n < c->T; ++n) {
+        size_t nv = (((size_t)b * c->T + n) * c->H + h);
+        gdr_token(S, c->dk, c->dv, c->k + nv * c->dk, c->v + nv * c->dv, (double)c->a[nv], (double)c->beta[nv], x);
+        read_state(S, c->dk, c->dv, c->q + nv * c->dk, c->o + nv * c->dv);
+    }
+}
+
+int oracle_chain_decode(int B, int T, int H, int dk, int dv, const float* q, const float* k, const float* v,
+                        const float* a, const float* beta, const float* S0, double* o, int nthreads) {
+    if (B <= 0 || T <= 0 || H <= 0) return 0;
+    seq_ctx c = {B, T, H, dk, dv, q, k, v, a, beta, S0, NULL, o};
+    run_items(chain_item, &c, (long)B * H, (long)dk * dv + dv, nthreads);
+    return 0;
+}
+
+/* Branch-by-branch traversal (what tree speculation does without a closed
+ * form): depth-first over the tree, each child's state computed once from its
+ * parent's, with a stack of states along the current branch. */
+static void dfs_item(void* vctx, long item, double* work) {
+    const seq_ctx* c = (const seq_ctx*)vctx;
+    int b = (int)(item / c->H), h = (int)(item % c->H);
+    const int T = c->T;
+    const size_t dd = (size_t)c->dk * c->dv;
+    /* work: (T + 1) states, x, then int scratch: child lists and resume points */
+    double* stack = work;
+    double* x = stack + (size_t)(T + 1) * dd;
+    int* first_child = (int*)(x + c->dv);
+    int* next_sib = first_child + T + 1;
+    int* resume = next_sib + T + 1;
+    const int32_t* par = c->parent + (size_t)b * T;
+    /* child lists in increasing node order; virtual root T holds the roots */
+    for (int n = 0; n <= T; ++n) first_child[n] = -1;
+    for (int n = T - 1; n >= 0; --n) {
+        int p = par[n] < 0 ? T : par[n];
+        next_sib[n] = first_child[p];
+        first_child[p] = n;
+    }
+    const float* s0 = c->S0 + ((size_t)b * c->H + h) * dd;
+    for (size_t e = 0; e < dd; ++e) stack[e] = (double)s0[e];
+    int top = 0;
+    int cursor = first_child[T];
+    /* iterative DFS: descend into cursor, or climb when no child is left */
+    for (;;) {
+        if (cursor >= 0) {
+            int n = cursor;
+            resume[top] = next_sib[n];
+            memcpy(stack + (size_t)(top + 1) * dd, stack + (size_t)top * dd, dd * sizeof(double));
+            ++top;
+            size_t nv = (((size_t)b * T + n) * c->H + h);
+            double* S = stack + (size_t)top * dd;
+            gdr_token(S, c->dk, c->dv, c->k + nv * c->dk, c->v + nv * c->dv, (double)c->a[nv], (double)c->beta[nv], x);
+            read_state(S, c->dk, c->dv, c->q + nv * c->dk, c->o + nv * c->dv);
+            cursor = first_child[n];
+        } else {
+            if (top == 0) break;
+            --top;
+            cursor = resume[top];
+        }
+    }
+}
+
+int oracle_verify_dfs(int B, int T, int H, int dk, int dv, const float* q, const float* k, const float* v,
+                      const float* a, const float* beta, const float* S0, const int32_t* parent, double* o,
+                      int nthreads) {
+    if (B <= 0 || T <= 0 || H <= 0) return 0;
+    for (int b = 0; b < B; ++b)
+        if (!parents_valid(parent, T, b)) return OR_BAD_PARENT;
+    seq_ctx c = {B, T, H, dk, dv, q, k, v, a, beta, S0, parent, o};
+    long work = (long)(T + 1) * dk * dv + dv + 3L * (T + 1);
+    run_items(dfs_item, &c, (long)B * H, work, nthreads);
+    return 0;
+}
+
+/* ------------------------------------------------------------- gather */
+
+typedef struct {
+    int B, P, H, dk, dv, num_slots, Qn;
+    const float* pool;
+    const int32_t* slot;
+    const float* queries;
+    double* o;
+    float* states_out;
+} gather_ctx;
+
+static void gather_item(void* vctx, long item, double* work) {
+    const gather_ctx* c = (const gather_ctx*)vctx;
+    (void)work;
+    int h = (int)(item % c->H);
+    long bp = item / c->H; /* b * P + p */
+    int s = c->slot[bp];
+    if (s < 0 || s >= c->num_slots) return;
+    const size_t dd = (size_t)c->dk * c->dv;
+    const float* src = c->pool + ((size_t)s * c->H + h) * dd;
+    if (c->states_out) memcpy(c->states_out + ((size_t)bp * c->H + h) * dd, src, dd * sizeof(float));
+    if (c->o && c->queries) {
+        for (int i = 0; i < c->Qn; ++i) {
+            const float* qv = c->queries + (((size_t)bp * c->H + h) * c->Qn + i) * c->dk;
+            double* out = c->o + (((size_t)bp * c->H + h) * c->Qn + i) * c->dv;
+            for (int r = 0; r < c->dv; ++r) {
+                double acc = 0.0;
+                for (int j = 0; j < c->dk; ++j) acc += (double)src[(size_t)r * c->dk + j] * (double)qv[j];
+                out[r] = acc;
+            }
+        }
+    }
+}
+
+/*
+ * State reads at chosen positions.
+ *   pool: [num_slots, H, dv, dk]; slot: [B, P]; queries: [B, P, H, Qn, dk] or NULL
+ *   o: [B, P, H, Qn, dv] fp64 or NULL; states_out: [B, P, H, dv, dk] fp32 (exact copy) or NULL
+ * Returns status bits (OR_BAD_SLOT).
+ */
+int oracle_gather(int B, int P, int H, int dk, int dv, int num_slots, int Qn, const float* pool,
+                  const int32_t* slot, const float* queries, double* o, float* states_out, int nthreads) {
+    if (B <= 0 || P <= 0 || H <= 0) return 0;
+    int status = 0;
+    for (long i = 0; i < (long)B * P; ++i)
+        if (slot[i] < 0 || slot[i] >= num_slots) status |= OR_BAD_SLOT;
+    gather_ctx c = {B, P, H, dk, dv, num_slots, Qn, pool, slot, queries, o, states_out};
+    run_items(gather_item, &c, (long)B * P * H, 1, nthreads);
+    return status;
+}

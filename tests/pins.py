@@ -1,0 +1,275 @@
+"""Independent checks that pin the fp64 oracle to something other than itself.
+
+Each ``pin_*`` function takes an ``oracle.Oracle`` and raises AssertionError
+when the oracle disagrees with:
+  * a hand-worked example (tests/golden/tree4_d2_handworked.json),
+  * the closed form of the Bole page (arXiv 2608.01651, section IV, Eq. (2)),
+    evaluated here in numpy with a library linear solve,
+  * the commit-from-factors identity that the same section's "Lemma 1" and
+    Eq. (9) rest on (only P, K, U and the committed state are kept),
+  * brute-force matrix products of the recurrence on tiny sizes,
+  * special cases with closed forms (b = 0: pure decay; a = 1, b = 0: pure
+    read; b = 1 with a unit key: the delta rule overwrites the value at that
+    key).
+The same functions run against oracle builds with planted mistakes
+(test_oracle_mutants.py) to show that each plausible mistake fails one.
+"""
+from __future__ import annotations
+
+import json
+import os
+from fractions import Fraction
+
+import numpy as np
+
+from workloads import l2_normalise_f32, make_chain, make_tree
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+# ------------------------------------------------------------------ helpers
+
+def rel_err(x, ref):
+    x = np.asarray(x, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    den = np.max(np.abs(ref))
+    return float(np.max(np.abs(x - ref)) / (den if den > 0 else 1.0))
+
+
+def random_case(seed, B, T, H, dk, dv, topology="tree", s0_std=0.1, max_depth=8, max_fanout=4,
+                a=None, beta=None, unit_k=True):
+    rng = np.random.default_rng(seed)
+    S0 = (rng.standard_normal((B, H, dv, dk)) * s0_std).astype(np.float32)
+    q = l2_normalise_f32(rng.standard_normal((B, T, H, dk)).astype(np.float32))
+    k = rng.standard_normal((B, T, H, dk)).astype(np.float32)
+    if unit_k:
+        k = l2_normalise_f32(k)
+    v = rng.standard_normal((B, T, H, dv)).astype(np.float32)
+    aa = (1.0 / (1.0 + np.exp(rng.standard_normal((B, T, H))))).astype(np.float32)
+    bb = (1.0 / (1.0 + np.exp(-rng.standard_normal((B, T, H))))).astype(np.float32)
+    if a is not None:
+        aa = np.full((B, T, H), a, dtype=np.float32)
+    if beta is not None:
+        bb = np.full((B, T, H), beta, dtype=np.float32)
+    if topology == "chain":
+        par = make_chain(B, T)
+    else:
+        par = make_tree(rng, B, T, max_depth, max_fanout)
+    return dict(q=q, k=k, v=v, a=aa, beta=bb, S0=S0, parent=par)
+
+
+def path_of(par_row, n):
+    p = []
+    m = n
+    while m >= 0:
+        p.append(m)
+        m = int(par_row[m])
+    return p[::-1]
+
+
+def closed_form_head(q, k, v, a, beta, S0, par_row):
+    """Eq. (2) of the Bole page for one (sequence, head), fp64.
+
+    O = D_P Q S_pre + C (I + G)^{-1} D_beta (V - D_P K S_pre), with S_pre = S0^T
+    (Eq. (2) writes O = Q S_pre with S_pre of shape d_k x d_v; the recurrence
+    reads o = S q with S of shape d_v x d_k).  G and C are not printed on the
+    page; unrolling the recurrence gives, for m on the path of n,
+      C[n, m] = (P_n / P_m) q_n . k_m              (m = n included)
+      G[n, m] = beta_n (P_n / P_m) k_n . k_m       (m a strict ancestor)
+    Returns (O [T, dv], U [T, dv], P [T], G [T, T]).
+    """
+    T = q.shape[0]
+    q, k, v = (np.asarray(x, np.float64) for x in (q, k, v))
+    a = np.asarray(a, np.float64)
+    beta = np.asarray(beta, np.float64)
+    Spre = np.asarray(S0, np.float64).T
+    P = np.empty(T)
+    for n in range(T):
+        P[n] = np.prod([a[m] for m in path_of(par_row, n)])
+    C = np.zeros((T, T))
+    G = np.zeros((T, T))
+    for n in range(T):
+        for m in path_of(par_row, n):
+            C[n, m] = P[n] / P[m] * (q[n] @ k[m])
+            if m != n:
+                G[n, m] = beta[n] * P[n] / P[m] * (k[n] @ k[m])
+    DP = np.diag(P)
+    Db = np.diag(beta)
+    R = Db @ (v - DP @ k @ Spre)
+    U = np.linalg.solve(np.eye(T) + G, R)
+    O = DP @ q @ Spre + C @ U
+    return O, U, P, G
+
+
+def brute_force_states(k, v, a, beta, S0, par_row):
+    """S_n for every node by explicit matrices: S = a S_p (I - b k k^T) + b v k^T."""
+    T, dk = k.shape
+    k, v = np.asarray(k, np.float64), np.asarray(v, np.float64)
+    out = []
+    for n in range(T):
+        S = np.asarray(S0, np.float64).copy()
+        for m in path_of(par_row, n):
+            km = k[m][:, None]
+            S = a[m] * S @ (np.eye(dk) - beta[m] * km @ km.T) + beta[m] * v[m][:, None] @ km.T
+        out.append(S)
+    return np.stack(out)
+
+
+# --------------------------------------------------------------------- pins
+
+def load_golden():
+    with open(os.path.join(GOLDEN, "tree4_d2_handworked.json")) as f:
+        g = json.load(f)
+    fr = lambda x: np.vectorize(lambda s: float(Fraction(s)))(np.array(x, dtype=object)).astype(np.float64)
+    return g, fr
+
+
+def pin_golden(orc):
+    """Hand-worked 4-node tree at d = 2: every value exact (dyadic)."""
+    g, fr = load_golden()
+    T = len(g["parent"])
+    q = fr(g["q"]).reshape(1, T, 1, 2).astype(np.float32)
+    k = fr(g["k"]).reshape(1, T, 1, 2).astype(np.float32)
+    v = fr(g["v"]).reshape(1, T, 1, 2).astype(np.float32)
+    a = fr(g["a"]).reshape(1, T, 1).astype(np.float32)
+    beta = fr(g["beta"]).reshape(1, T, 1).astype(np.float32)
+    S0 = fr(g["S0"]).reshape(1, 1, 2, 2).astype(np.float32)
+    par = np.array(g["parent"], dtype=np.int32).reshape(1, T)
+    o, st, status = orc.verify(q, k, v, a, beta, S0, par, want_states=True)
+    assert status == 0
+    assert np.array_equal(o[0, :, 0, :], fr(g["o"])), (o[0, :, 0, :], fr(g["o"]))
+    assert np.array_equal(st[0, :, 0], fr(g["states"]))
+    for n in range(-1, T):
+        S, status = orc.commit(k, v, a, beta, S0, np.array([n], np.int32), par)
+        assert status == 0
+        want = fr(g["S0"]) if n < 0 else fr(g["states"])[n]
+        assert np.array_equal(S[0, 0], want), (n, S[0, 0], want)
+
+
+def pin_closed_form(orc, seed=11, B=2, T=20, H=2, dk=16, dv=12, topology="tree", tol=1e-10):
+    """Oracle outputs equal Eq. (2) evaluated with a library solve."""
+    c = random_case(seed, B, T, H, dk, dv, topology, max_depth=6)
+    o, _, status = orc.verify(**c)
+    assert status == 0
+    for b in range(B):
+        for h in range(H):
+            O, U, P, G = closed_form_head(c["q"][b, :, h], c["k"][b, :, h], c["v"][b, :, h],
+                                          c["a"][b, :, h], c["beta"][b, :, h], c["S0"][b, h].astype(np.float64),
+                                          c["parent"][b])
+            e = rel_err(o[b, :, h], O)
+            assert e <= tol, ("closed form", b, h, e)
+
+
+def pin_commit_from_factors(orc, seed=12, B=2, T=16, H=2, d=8, tol=1e-10):
+    """Committed state equals P_n* S0 + sum_{m on path} (P_n*/P_m) u_m k_m^T
+    with U from Eq. (2)'s solve (the factorised speculative states)."""
+    c = random_case(seed, B, T, H, d, d, "tree", max_depth=5)
+    rng = np.random.default_rng(seed + 1)
+    acc = rng.integers(0, T, size=B).astype(np.int32)
+    S, status = orc.commit(c["k"], c["v"], c["a"], c["beta"], c["S0"], acc, c["parent"])
+    assert status == 0
+    for b in range(B):
+        for h in range(H):
+            _, U, P, _ = closed_form_head(c["q"][b, :, h], c["k"][b, :, h], c["v"][b, :, h],
+                                          c["a"][b, :, h], c["beta"][b, :, h], c["S0"][b, h].astype(np.float64),
+                                          c["parent"][b])
+            n = int(acc[b])
+            want = P[n] * c["S0"][b, h].astype(np.float64)
+            for m in path_of(c["parent"][b], n):
+                want = want + (P[n] / P[m]) * np.outer(U[m], c["k"][b, m, h].astype(np.float64))
+            e = rel_err(S[b, h], want)
+            assert e <= tol, ("factors", b, h, e)
+
+
+def pin_brute_force(orc, seed=13, B=2, T=10, H=2, dk=6, dv=5, tol=1e-12):
+    """Every node state and output equals explicit matrix products on tiny sizes."""
+    c = random_case(seed, B, T, H, dk, dv, "tree", max_depth=5, unit_k=False)
+    o, st, status = orc.verify(**c, want_states=True)
+    assert status == 0
+    for b in range(B):
+        for h in range(H):
+            S = brute_force_states(c["k"][b, :, h], c["v"][b, :, h], c["a"][b, :, h].astype(np.float64),
+                                   c["beta"][b, :, h].astype(np.float64), c["S0"][b, h], c["parent"][b])
+            assert rel_err(st[b, :, h], S) <= tol
+            want_o = np.einsum("nij,nj->ni", S, c["q"][b, :, h].astype(np.float64))
+            assert rel_err(o[b, :, h], want_o) <= tol
+
+
+def pin_pure_decay(orc, seed=14, B=2, T=24, H=3, d=8, tol=1e-14):
+    """beta = 0: S_n = P_n S0 and o_n = P_n S0 q_n, P_n the gate product on the path."""
+    c = random_case(seed, B, T, H, d, d, "tree", beta=0.0)
+    o, st, status = orc.verify(**c, want_states=True)
+    assert status == 0
+    for b in range(B):
+        for h in range(H):
+            S0 = c["S0"][b, h].astype(np.float64)
+            for n in range(T):
+                P = 1.0
+                for m in path_of(c["parent"][b], n):
+                    P *= float(c["a"][b, m, h])
+                assert rel_err(st[b, n, h], P * S0) <= tol
+                assert rel_err(o[b, n, h], P * (S0 @ c["q"][b, n, h].astype(np.float64))) <= tol
+
+
+def pin_pure_read(orc, seed=15, B=2, T=12, H=2, d=16):
+    """a = 1, beta = 0: every node reads the committed state, o_n = S0 q_n."""
+    c = random_case(seed, B, T, H, d, d, "tree", a=1.0, beta=0.0)
+    o, _, status = orc.verify(**c)
+    assert status == 0
+    want = np.einsum("bhij,bnhj->bnhi", c["S0"].astype(np.float64), c["q"].astype(np.float64))
+    assert rel_err(o, want) <= 1e-15
+
+
+def pin_overwrite(orc, seed=16, B=2, T=12, H=2, d=16):
+    """beta_n = 1 with a unit key: S_n k_n = v_n for any a_n and parent state
+    (the delta rule replaces the value stored at key k_n).  With q_n = k_n the
+    node output is v_n.  Keys are unit in fp32, so |k|^2 = 1 within ~1e-7."""
+    c = random_case(seed, B, T, H, d, d, "tree", beta=1.0)
+    c["q"] = c["k"].copy()
+    o, st, status = orc.verify(**c, want_states=True)
+    assert status == 0
+    Sk = np.einsum("bnhij,bnhj->bnhi", st, c["k"].astype(np.float64))
+    assert rel_err(Sk, c["v"]) <= 1e-6
+    assert rel_err(o, c["v"]) <= 1e-6
+
+
+def pin_chain_equals_decode(orc, seed=17, B=2, T=9, H=3, d=8):
+    """A chain (explicit parent n-1, or no parent array) equals sequential
+    decode with one running state, bit for bit (same operation order)."""
+    c = random_case(seed, B, T, H, d, d, "chain")
+    o_dec = orc.chain_decode(c["q"], c["k"], c["v"], c["a"], c["beta"], c["S0"])
+    o_tree, _, s1 = orc.verify(**c)
+    c2 = dict(c)
+    c2["parent"] = None
+    o_chain, _, s2 = orc.verify(**c2)
+    assert s1 == 0 and s2 == 0
+    assert np.array_equal(o_tree, o_dec)
+    assert np.array_equal(o_chain, o_dec)
+
+
+def pin_tree_equals_dfs(orc, seed=18, B=3, T=40, H=2, d=8):
+    """Path walk per node equals branch-by-branch DFS traversal, bit for bit."""
+    c = random_case(seed, B, T, H, d, d, "tree")
+    o, _, s1 = orc.verify(**c)
+    o_dfs, s2 = orc.verify_dfs(**c)
+    assert s1 == 0 and s2 == 0
+    assert np.array_equal(o, o_dfs)
+
+
+def pin_gather(orc, seed=19):
+    """Gathered states are bit copies of pool[slot]; o = S q per query."""
+    rng = np.random.default_rng(seed)
+    pool = rng.standard_normal((7, 3, 16, 16)).astype(np.float32)
+    slot = np.array([[6, 0, 2], [2, 2, 5]], dtype=np.int32)
+    qs = rng.standard_normal((2, 3, 3, 5, 16)).astype(np.float32)
+    o, st, status = orc.gather(pool, slot, qs)
+    assert status == 0
+    for b in range(2):
+        for p in range(3):
+            assert np.array_equal(st[b, p], pool[slot[b, p]])
+            want = np.einsum("hij,hqj->hqi", pool[slot[b, p]].astype(np.float64), qs[b, p].astype(np.float64))
+            assert rel_err(o[b, p], want) <= 1e-15
+
+
+ALL_PINS = [pin_golden, pin_closed_form, pin_commit_from_factors, pin_brute_force, pin_pure_decay,
+            pin_pure_read, pin_overwrite, pin_chain_equals_decode, pin_tree_equals_dfs, pin_gather]

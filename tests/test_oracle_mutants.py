@@ -1,0 +1,45 @@
+"""Plant plausible mistakes in a copy of the oracle (on the CPU) and check that
+the pins catch every one: a pin set that a dropped term, a wrong sign, a
+transposed operand or a reversed path could slip through would not pin
+anything."""
+import os
+
+import pytest
+
+import pins
+from oracle import Oracle
+from oracle import build as obuild
+
+MUTANTS = {
+    "erase term dropped": ("row[j] = a * (row[j] - bx * kj) + bv * kj;", "row[j] = a * row[j] + bv * kj;"),
+    "erase sign flipped": ("row[j] = a * (row[j] - bx * kj) + bv * kj;", "row[j] = a * (row[j] + bx * kj) + bv * kj;"),
+    "decay skips the erase": ("row[j] = a * (row[j] - bx * kj) + bv * kj;", "row[j] = a * row[j] - bx * kj + bv * kj;"),
+    "write not gated by beta": ("double bv = b * (double)v[i];", "double bv = (double)v[i];"),
+    "state read transposed": ("for (int j = 0; j < dk; ++j) s += S[(size_t)i * dk + j] * (double)q[j];",
+                              "for (int j = 0; j < dk; ++j) s += S[(size_t)j * dk + i] * (double)q[j];"),
+    "path walked leaf first": ("for (int i = 0; i < len / 2; ++i) {", "for (int i = 0; i < 0; ++i) {"),
+    "erase uses the value": ("double bx = b * x[i];", "double bx = b * (double)v[i];"),
+    "chain parent off by one": (": n - 1;", ": n - 2;"),
+    "gather copies the wrong head": ("const float* src = c->pool + ((size_t)s * c->H + h) * dd;",
+                                     "const float* src = c->pool + ((size_t)s * c->H + (h + 1) % c->H) * dd;"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(tmp_path, name):
+    old, new = MUTANTS[name]
+    with open(obuild.SRC) as f:
+        src = f.read()
+    assert src.count(old) >= 1, "mutation site vanished from oracle.c"
+    mpath = os.path.join(str(tmp_path), "mutant.c")
+    with open(mpath, "w") as f:
+        f.write(src.replace(old, new))
+    lib = obuild.build(src=mpath, out=os.path.join(str(tmp_path), "libmutant.so"))
+    m = Oracle(lib)
+    caught = []
+    for pin in pins.ALL_PINS:
+        try:
+            pin(m)
+        except AssertionError:
+            caught.append(pin.__name__)
+    assert caught, "no pin caught: " + name
