@@ -55,7 +55,7 @@ class Oracle:
         lib = ctypes.CDLL(path)
         i = ctypes.c_int
         lib.oracle_verify.argtypes = [i, i, i, i, i, _f32p, _f32p, _f32p, _f32p, _f32p, _f32p,
-                                      _i32p, _f64p, _f64p, i]
+                                      _i32p, _f64p, _f64p, _f64p, i]
         lib.oracle_commit.argtypes = [i, i, i, i, i, _f32p, _f32p, _f32p, _f32p, _f32p, _i32p,
                                       _i32p, _f64p, i]
         lib.oracle_chain_decode.argtypes = [i, i, i, i, i, _f32p, _f32p, _f32p, _f32p, _f32p,
@@ -69,19 +69,24 @@ class Oracle:
         self.lib = lib
         self.path = path
 
-    def verify(self, q, k, v, a, beta, S0, parent=None, want_states=False, nthreads=None):
+    def verify(self, q, k, v, a, beta, S0, parent=None, want_states=False, want_u=False,
+               nthreads=None):
         """All node outputs o[b, n, h, :] = S_n q_n (fp64), and optionally every
-        node state S_n.  parent=None means a chain.  Returns (o, states, status)."""
+        node state S_n.  parent=None means a chain.  Returns (o, states, status),
+        or (o, u, states, status) with ``want_u`` (u_n the node corrections)."""
         q, k, v, a, beta, S0 = map(_f32, (q, k, v, a, beta, S0))
         B, T, H, dk = q.shape
         dv = v.shape[-1]
         par = None if parent is None else _i32(parent)
         o = np.zeros((B, T, H, dv), dtype=np.float64)
+        u = np.zeros((B, T, H, dv), dtype=np.float64) if want_u else None
         st = np.zeros((B, T, H, dv, dk), dtype=np.float64) if want_states else None
         status = self.lib.oracle_verify(B, T, H, dk, dv, _p(q, _f32p), _p(k, _f32p), _p(v, _f32p),
                                         _p(a, _f32p), _p(beta, _f32p), _p(S0, _f32p),
-                                        _p(par, _i32p), _p(o, _f64p), _p(st, _f64p),
+                                        _p(par, _i32p), _p(o, _f64p), _p(u, _f64p), _p(st, _f64p),
                                         _threads(nthreads))
+        if want_u:
+            return o, u, st, status
         return o, st, status
 
     def commit(self, k, v, a, beta, S0, accepted, parent=None, nthreads=None):

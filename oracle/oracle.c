@@ -94,14 +94,18 @@ static void run_items(void (*fn)(void*, long, double*), void* ctx, long n_items,
 
 /* One token of the gated delta rule on S (dv x dk, row-major):
  *   x = S k;   S <- a * (S - b x k^T) + b v k^T
- * which is S <- a S (I - b k k^T) + b v k^T with x formed before the update. */
+ * which is S <- a S (I - b k k^T) + b v k^T with x formed before the update.
+ * If u is not NULL it receives the token's correction u = b (v - a x), the
+ * vector with S_new = a S_old + u k^T. */
 static void gdr_token(double* S, int dk, int dv, const float* k, const float* v,
-                      double a, double b, double* x) {
+                      double a, double b, double* x, double* u) {
     for (int i = 0; i < dv; ++i) {
         double s = 0.0;
         for (int j = 0; j < dk; ++j) s += S[(size_t)i * dk + j] * (double)k[j];
         x[i] = s;
     }
+    if (u)
+        for (int i = 0; i < dv; ++i) u[i] = b * ((double)v[i] - a * x[i]);
     for (int i = 0; i < dv; ++i) {
         double bx = b * x[i];
         double bv = b * (double)v[i];
@@ -154,6 +158,7 @@ typedef struct {
     const int32_t* parent;
     const int32_t* accepted;
     double* o;
+    double* u;
     double* states;
     double* S_out;
     const unsigned char* seq_ok;
@@ -163,8 +168,9 @@ typedef struct {
 #define NODE_VEC(base, c, b, n, h, d) ((base) + ((((size_t)(b) * (c)->T + (n)) * (c)->H + (h)) * (size_t)(d)))
 #define NODE_GATE(base, c, b, n, h) ((base)[(((size_t)(b) * (c)->T + (n)) * (c)->H + (h))])
 
-/* Rebuild S at node n of (b, h) from S0 along the root-to-n path. */
-static void walk_to(const walk_ctx* c, int b, int h, int n, double* S, double* x, int* path) {
+/* Rebuild S at node n of (b, h) from S0 along the root-to-n path; u_n (the
+ * correction of the last token) goes to u when u is not NULL. */
+static void walk_to(const walk_ctx* c, int b, int h, int n, double* S, double* x, int* path, double* u) {
     const size_t dd = (size_t)c->dk * c->dv;
     const float* s0 = c->S0 + ((size_t)b * c->H + h) * dd;
     for (size_t e = 0; e < dd; ++e) S[e] = (double)s0[e];
@@ -173,7 +179,8 @@ static void walk_to(const walk_ctx* c, int b, int h, int n, double* S, double* x
     for (int i = 0; i < len; ++i) {
         int m = path[i];
         gdr_token(S, c->dk, c->dv, NODE_VEC(c->k, c, b, m, h, c->dk), NODE_VEC(c->v, c, b, m, h, c->dv),
-                  (double)NODE_GATE(c->a, c, b, m, h), (double)NODE_GATE(c->beta, c, b, m, h), x);
+                  (double)NODE_GATE(c->a, c, b, m, h), (double)NODE_GATE(c->beta, c, b, m, h), x,
+                  i == len - 1 ? u : NULL);
     }
 }
 
@@ -186,7 +193,7 @@ static void verify_item(void* vctx, long item, double* work) {
     double* x = S + dd;
     int* path = (int*)(x + c->dv);
     for (int n = 0; n < c->T; ++n) {
-        walk_to(c, b, h, n, S, x, path);
+        walk_to(c, b, h, n, S, x, path, c->u ? NODE_VEC(c->u, c, b, n, h, c->dv) : NULL);
         read_state(S, c->dk, c->dv, NODE_VEC(c->q, c, b, n, h, c->dk), NODE_VEC(c->o, c, b, n, h, c->dv));
         if (c->states) memcpy(c->states + ((((size_t)b * c->T + n) * c->H + h) * dd), S, dd * sizeof(double));
     }
@@ -201,12 +208,13 @@ static long walk_work(int T, int dk, int dv) {
  * Verify every draft node: o[b, n, h, :] = S_n q_n for all nodes.
  *   q, k: [B, T, H, dk]; v: [B, T, H, dv]; a, beta: [B, T, H]; S0: [B, H, dv, dk]
  *   parent: [B, T] (parent[n] in [-1, n-1]) or NULL for a chain (parent[n] = n-1)
- *   o: [B, T, H, dv] fp64; states: [B, T, H, dv, dk] fp64 or NULL
+ *   o: [B, T, H, dv] fp64; u: [B, T, H, dv] fp64 or NULL, the node corrections
+ *   u_n = beta_n (v_n - a_n S_p(n) k_n); states: [B, T, H, dv, dk] fp64 or NULL
  * Returns status bits (OR_BAD_PARENT).
  */
 int oracle_verify(int B, int T, int H, int dk, int dv, const float* q, const float* k, const float* v,
                   const float* a, const float* beta, const float* S0, const int32_t* parent, double* o,
-                  double* states, int nthreads) {
+                  double* u, double* states, int nthreads) {
     if (B <= 0 || T <= 0 || H <= 0) return 0;
     unsigned char* ok = (unsigned char*)malloc((size_t)B);
     int status = 0;
@@ -214,7 +222,7 @@ int oracle_verify(int B, int T, int H, int dk, int dv, const float* q, const flo
         ok[b] = (unsigned char)parents_valid(parent, T, b);
         if (!ok[b]) status |= OR_BAD_PARENT;
     }
-    walk_ctx c = {B, T, H, dk, dv, q, k, v, a, beta, S0, parent, NULL, o, states, NULL, ok};
+    walk_ctx c = {B, T, H, dk, dv, q, k, v, a, beta, S0, parent, NULL, o, u, states, NULL, ok};
     run_items(verify_item, &c, (long)B * H, walk_work(T, dk, dv), nthreads);
     free(ok);
     return status;
@@ -228,14 +236,15 @@ static void commit_item(void* vctx, long item, double* work) {
     double* S = work;
     double* x = S + dd;
     int* path = (int*)(x + c->dv);
-    walk_to(c, b, h, c->accepted[b], S, x, path);
+    walk_to(c, b, h, c->accepted[b], S, x, path, NULL);
     memcpy(c->S_out + ((size_t)b * c->H + h) * dd, S, dd * sizeof(double));
 }
 
 /*
  * Committed state at the accepted node: S_out[b, h] = S_{accepted[b]} of the
  * walk, or S0[b, h] when accepted[b] = -1.  S_out: [B, H, dv, dk] fp64.
- * Returns status bits (OR_BAD_PARENT, OR_BAD_ACCEPTED).
+ * Returns status bits (OR_BAD_PARENT when a node is accepted and the
+ * sequence's parent row is invalid, OR_BAD_ACCEPTED).
  */
 int oracle_commit(int B, int T, int H, int dk, int dv, const float* k, const float* v, const float* a,
                   const float* beta, const float* S0, const int32_t* parent, const int32_t* accepted,
@@ -246,12 +255,13 @@ int oracle_commit(int B, int T, int H, int dk, int dv, const float* k, const flo
     for (int b = 0; b < B; ++b) {
         int n = accepted[b];
         int good_acc = (n >= -1 && n < T);
-        int good_par = (T <= 0) ? 1 : parents_valid(parent, T, b);
+        /* the parent row is only needed (and only checked) when a node is accepted */
+        int good_par = (!good_acc || n < 0) ? 1 : parents_valid(parent, T, b);
         if (!good_acc) status |= OR_BAD_ACCEPTED;
         if (!good_par) status |= OR_BAD_PARENT;
         ok[b] = (unsigned char)(good_acc && good_par);
     }
-    walk_ctx c = {B, T, H, dk, dv, NULL, k, v, a, beta, S0, parent, accepted, NULL, NULL, S_out, ok};
+    walk_ctx c = {B, T, H, dk, dv, NULL, k, v, a, beta, S0, parent, accepted, NULL, NULL, NULL, S_out, ok};
     run_items(commit_item, &c, (long)B * H, walk_work(T > 0 ? T : 1, dk, dv), nthreads);
     free(ok);
     return status;
@@ -278,7 +288,8 @@ static void chain_item(void* vctx, long item, double* work) {
     for (size_t e = 0; e < dd; ++e) S[e] = (double)s0[e];
     for (int n = 0; n < c->T; ++n) {
         size_t nv = (((size_t)b * c->T + n) * c->H + h);
-        gdr_token(S, c->dk, c->dv, c->k + nv * c->dk, c->v + nv * c->dv, (double)c->a[nv], (double)c->beta[nv], x);
+        gdr_token(S, c->dk, c->dv, c->k + nv * c->dk, c->v + nv * c->dv, (double)c->a[nv], (double)c->beta[nv], x,
+                  NULL);
         read_state(S, c->dk, c->dv, c->q + nv * c->dk, c->o + nv * c->dv);
     }
 }
@@ -326,7 +337,8 @@ static void dfs_item(void* vctx, long item, double* work) {
             ++top;
             size_t nv = (((size_t)b * T + n) * c->H + h);
             double* S = stack + (size_t)top * dd;
-            gdr_token(S, c->dk, c->dv, c->k + nv * c->dk, c->v + nv * c->dv, (double)c->a[nv], (double)c->beta[nv], x);
+            gdr_token(S, c->dk, c->dv, c->k + nv * c->dk, c->v + nv * c->dv, (double)c->a[nv], (double)c->beta[nv], x,
+                      NULL);
             read_state(S, c->dk, c->dv, c->q + nv * c->dk, c->o + nv * c->dv);
             cursor = first_child[n];
         } else {

@@ -149,7 +149,7 @@ def pin_golden(orc):
 def pin_closed_form(orc, seed=11, B=2, T=20, H=2, dk=16, dv=12, topology="tree", tol=1e-10):
     """Oracle outputs equal Eq. (2) evaluated with a library solve."""
     c = random_case(seed, B, T, H, dk, dv, topology, max_depth=6)
-    o, _, status = orc.verify(**c)
+    o, u, _, status = orc.verify(**c, want_u=True)
     assert status == 0
     for b in range(B):
         for h in range(H):
@@ -158,6 +158,8 @@ def pin_closed_form(orc, seed=11, B=2, T=20, H=2, dk=16, dv=12, topology="tree",
                                           c["parent"][b])
             e = rel_err(o[b, :, h], O)
             assert e <= tol, ("closed form", b, h, e)
+            e = rel_err(u[b, :, h], U)
+            assert e <= tol, ("closed form U", b, h, e)
 
 
 def pin_commit_from_factors(orc, seed=12, B=2, T=16, H=2, d=8, tol=1e-10):
