@@ -1,0 +1,158 @@
+/*
+ * ldv.h - draft verification through a gated-delta-rule linear-attention
+ * layer on AMD Instinct MI355X (gfx950).
+ *
+ * The layer's recurrence, per head, over a draft tree in topological order:
+ *
+ *     S_n = a_n * S_p(n) * (I - beta_n k_n k_n^T) + beta_n v_n k_n^T,
+ *     o_n = S_n q_n,                 S_p(n) = S0 when p(n) = -1,
+ *
+ * with S a d_v x d_k matrix stored row-major ([d_v][d_k], row = value index).
+ * The Bole page (arXiv 2608.01651, section IV, Eq. (2)) gives the closed form
+ * that verifies every proposal node at once from the committed state; its
+ * S_pre is S0 transposed.  Eq. (7) of the same section splits the value
+ * columns into independent tiles; Eq. (9) and its "Lemma 1" keep only the
+ * node factors (gate products P, keys K, corrections U) plus the one
+ * committed state, so that only the accepted node's state is ever formed
+ * (the page's summary: "materializes only the post-sampling selected
+ * state").  The ReaDy page (arXiv 2610.20503, Fig. 2a, 3, 4) reads committed
+ * recurrent states at chosen positions for the drafter.
+ *
+ * Conventions shared by every call:
+ *   - Pointers are device memory owned by the caller (hipMalloc or a PyTorch
+ *     tensor).  The library allocates nothing and keeps no state, so calls
+ *     are thread-safe.  Tensors are dense and row-major in the shapes given.
+ *   - Every call only enqueues work on `stream` (a hipStream_t; NULL = the
+ *     null stream) and returns without synchronising.
+ *   - The return value reports argument errors found on the host before
+ *     anything is enqueued: LDV_OK, LDV_ERR_ARG (NULL required pointer,
+ *     negative size, bad dtype code, misaligned pointer), LDV_ERR_UNSUPPORTED
+ *     (a size outside what the kernels implement), LDV_ERR_LAUNCH (the HIP
+ *     launch failed).  A size of zero in B, T, H or P is a no-op returning
+ *     LDV_OK.
+ *   - Data errors can only be seen on the device: each kernel ORs
+ *     LDV_STATUS_* bits into *status (a device int; NULL = do not report) and
+ *     leaves the outputs of the affected sequence or position unwritten.
+ *   - Alignment: q, k, v, S0, o, u, S_out, pool, queries, states_out need 16
+ *     bytes; the [B, T, H] gate/log arrays, index arrays and status need 4.
+ *   - Supported sizes: d_k == d_v in {16, 32, 64, 128}; 1 <= T <= 64.
+ */
+#ifndef LDV_H
+#define LDV_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LDV_OK 0
+#define LDV_ERR_ARG (-1)
+#define LDV_ERR_UNSUPPORTED (-2)
+#define LDV_ERR_LAUNCH (-3)
+
+/* Bits ORed into *status by the kernels. */
+#define LDV_STATUS_BAD_PARENT 1   /* parent[b, n] outside [-1, n-1] */
+#define LDV_STATUS_BAD_ACCEPTED 2 /* accepted[b] outside [-1, T-1] */
+#define LDV_STATUS_BAD_SLOT 4     /* slot[b, p] outside [0, num_slots) */
+
+/* Element type of q / k / v / queries. */
+#define LDV_BF16 0
+#define LDV_F32 1
+
+#define LDV_MAX_T 64
+
+/*
+ * Verify a draft tree: for every node n of every (sequence b, head h),
+ *     o[b, n, h, :] = S_n q_n
+ * computed from the committed state S0 for all nodes at once (Bole page,
+ * section IV, Eq. (2), evaluated per value tile as in Eq. (7)).
+ *
+ *   q, k      [B, T, H, dk]  element type qkv_dtype
+ *   v         [B, T, H, dv]  element type qkv_dtype
+ *   a, beta   [B, T, H] fp32; a in [0, 1] (decay gate), beta in [0, 1]
+ *   S0        [B, H, dv, dk] fp32, the committed state (read only)
+ *   parent    [B, T] int32, parent[b, n] in [-1, n-1] (-1: child of S0);
+ *             nodes are in topological order, several roots are allowed
+ *   o         [B, T, H, dv] fp32 (written)
+ *   u_out     [B, T, H, dv] fp32, the node corrections U of Eq. (2)
+ *             (u_n = beta_n (v_n - a_n S_p(n) k_n)), written
+ *   logp_out  [B, T, H] fp32, log P_n = sum of log a over the root-to-n path,
+ *             each log a clamped below at -87 (a zero gate stays finite)
+ *   u_out and logp_out are the factors ldv_commit_state needs; pass both or
+ *   neither (NULL, NULL: no commit will follow).
+ * A sequence whose parent row is invalid gets LDV_STATUS_BAD_PARENT and none
+ * of its outputs are written.
+ */
+int ldv_verify_tree(int B, int T, int H, int dk, int dv, int qkv_dtype,
+                    const void* q, const void* k, const void* v,
+                    const float* a, const float* beta, const float* S0,
+                    const int32_t* parent,
+                    float* o, float* u_out, float* logp_out,
+                    int* status, void* stream);
+
+/*
+ * Verify a chain (a draft block): ldv_verify_tree with parent[b, n] = n - 1,
+ * no parent array needed.  The block-of-drafts case of the ReaDy page
+ * (Fig. 2a: verification determines the accepted prefix).
+ */
+int ldv_verify_chain(int B, int T, int H, int dk, int dv, int qkv_dtype,
+                     const void* q, const void* k, const void* v,
+                     const float* a, const float* beta, const float* S0,
+                     float* o, float* u_out, float* logp_out,
+                     int* status, void* stream);
+
+/*
+ * Commit: form only the state of the accepted node (Bole page, summary and
+ * section IV, Eq. (9) / "Lemma 1"):
+ *     n = accepted[b];  n = -1: S_out[b, h] = S0[b, h]
+ *     else S_out[b, h] = P_n S0[b, h] + sum_{m on root-to-n path} (P_n / P_m) u_m k_m^T
+ * with P = exp(logp) and u, logp as written by the verify call on the same
+ * k, parent and S0.
+ *
+ *   k         [B, T, H, dk] element type k_dtype
+ *   u         [B, T, H, dv] fp32, logp [B, T, H] fp32 (from verify)
+ *   parent    [B, T] int32 or NULL for a chain
+ *   accepted  [B] int32 in [-1, T-1]
+ *   S0        [B, H, dv, dk] fp32; S_out [B, H, dv, dk] fp32.  S_out == S0
+ *             (in place) is allowed and then heads with accepted = -1 are not
+ *             touched; any other overlap of S_out and S0 is undefined.
+ * Bad accepted[b] -> LDV_STATUS_BAD_ACCEPTED, bad parent on the sequence ->
+ * LDV_STATUS_BAD_PARENT; that sequence's S_out is left unwritten.
+ */
+int ldv_commit_state(int B, int T, int H, int dk, int dv, int k_dtype,
+                     const void* k, const float* u, const float* logp,
+                     const int32_t* parent, const int32_t* accepted,
+                     const float* S0, float* S_out,
+                     int* status, void* stream);
+
+/*
+ * Gather committed states at chosen positions and read them with drafter
+ * queries (ReaDy page, Fig. 2a: position-specific reads from committed
+ * recurrent states; Fig. 3: direct gathering without an intermediate copy):
+ *     s = slot[b, p]
+ *     o[b, p, h, i, :]        = pool[s, h] queries[b, p, h, i, :]   (i < Qn)
+ *     states_out[b, p, h]     = pool[s, h]                          (bit copy)
+ *
+ *   pool        [num_slots, H, dv, dk] fp32
+ *   slot        [B, P] int32 in [0, num_slots); duplicates allowed
+ *   queries     [B, P, H, Qn, dk] element type q_dtype, or NULL (Qn ignored)
+ *   o           [B, P, H, Qn, dv] fp32 or NULL (both queries and o, or neither)
+ *   states_out  [B, P, H, dv, dk] fp32 or NULL
+ * A bad slot -> LDV_STATUS_BAD_SLOT and that position's outputs are unwritten.
+ */
+int ldv_gather_states(int B, int P, int H, int dk, int dv, int num_slots, int Qn, int q_dtype,
+                      const float* pool, const int32_t* slot, const void* queries,
+                      float* o, float* states_out, int* status, void* stream);
+
+/* Text for an LDV_OK / LDV_ERR_* return code (static storage). */
+const char* ldv_status_string(int code);
+
+/* Library version: major * 10000 + minor * 100 + patch. */
+int ldv_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LDV_H */

@@ -1,0 +1,11 @@
+"""MI355X-native draft verification through a gated-delta-rule layer.
+
+The C ABI (include/ldv.h, libldv.so) holds the HIP kernels for gfx950; this
+package is its Python binding.  Importing the package loads the library and
+fails if it has not been built.
+"""
+from .ldv import (LDV_BF16, LDV_F32, MAX_T, STATUS_BAD_ACCEPTED, STATUS_BAD_PARENT,  # noqa: F401
+                  STATUS_BAD_SLOT, LdvError, commit_state, gather_states, load, status_string,
+                  verify_chain, verify_tree, version)
+
+load()

@@ -1,0 +1,151 @@
+// Batched state reads at chosen positions (gfx950).
+//
+// ReaDy page (arXiv 2610.20503): the drafter combines target features with
+// position-specific reads from committed recurrent states (Fig. 2a); the
+// state reader gathers the states directly, without an intermediate tensor
+// (Fig. 3), which is what cut its state-gathering latency (Fig. 4).  Here:
+//   s = slot[b, p];  o[b, p, h, i, :] = pool[s, h] q_i  for i < Qn;
+//   states_out[b, p, h] = pool[s, h]  (optional bit copy).
+//
+// One block of four waves per (sequence, position, head).  Each wave loads
+// its 16-row blocks of the fp32 state straight into MFMA A-operand registers
+// (64 contiguous bytes per row per load), writes the copy from the same
+// registers, and multiplies by the queries on MFMA with the state split into
+// bf16 hi + lo terms.  The read of the 64 KiB state dominates: the kernel is
+// bound by HBM.
+#include "ldv_device.hpp"
+#include "ldv_kernels.hpp"
+
+#include "../../include/ldv.h"
+
+namespace ldv {
+
+template <int D>
+struct GShape {
+    static constexpr int MBT = D / 16;             // 16-row blocks per state
+    static constexpr int NWA = MBT < 4 ? MBT : 4;  // waves holding rows
+    static constexpr int MBW = MBT / NWA;          // row blocks per wave
+    static constexpr int KS = (D + 31) / 32;       // MFMA k-steps
+};
+
+template <int D, bool F32Q>
+__global__ __launch_bounds__(256) void gather_kernel(const GatherArgs p) {
+    using S = GShape<D>;
+    constexpr int NWA = S::NWA, MBW = S::MBW, KS = S::KS;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int c = lane & 15, g = lane >> 4;
+    const int H = p.H;
+    const unsigned bid = xcd_remap(blockIdx.x, gridDim.x);
+    const int h = (int)(bid % H);
+    const size_t bp = bid / H;  // b * P + p
+
+    const int s = p.slot[bp];
+    if (s < 0 || s >= p.num_slots) {
+        if (tid == 0 && p.status && h == 0) atomicOr(p.status, LDV_STATUS_BAD_SLOT);
+        return;
+    }
+    if (wave >= NWA) return;
+    const float* src = p.pool + ((size_t)s * H + h) * D * D;
+
+    float4 st[MBW][KS][2];
+#pragma unroll
+    for (int mi = 0; mi < MBW; ++mi) {
+        const int row = (wave + NWA * mi) * 16 + c;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const int k0 = 32 * ks + 4 * g;
+            st[mi][ks][0] = (k0 < D) ? *reinterpret_cast<const float4*>(src + (size_t)row * D + k0)
+                                     : make_float4(0.f, 0.f, 0.f, 0.f);
+            st[mi][ks][1] = (k0 + 16 < D) ? *reinterpret_cast<const float4*>(src + (size_t)row * D + k0 + 16)
+                                          : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+    }
+    if (p.states_out) {
+        float* dst = p.states_out + ((size_t)bp * H + h) * D * D;
+#pragma unroll
+        for (int mi = 0; mi < MBW; ++mi) {
+            const int row = (wave + NWA * mi) * 16 + c;
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const int k0 = 32 * ks + 4 * g;
+                if (k0 < D) *reinterpret_cast<float4*>(dst + (size_t)row * D + k0) = st[mi][ks][0];
+                if (k0 + 16 < D) *reinterpret_cast<float4*>(dst + (size_t)row * D + k0 + 16) = st[mi][ks][1];
+            }
+        }
+    }
+    if (!p.queries || !p.o || p.Qn <= 0) return;
+
+    const size_t qo_base = ((size_t)bp * H + h) * (size_t)p.Qn;
+    for (int nb = 0; nb * 16 < p.Qn; ++nb) {
+        const int col = nb * 16 + c;  // query index held by this lane
+        const bool cval = col < p.Qn;
+        floatx4 acc[MBW];
+#pragma unroll
+        for (int mi = 0; mi < MBW; ++mi) acc[mi] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const int k0 = 32 * ks + 4 * g;
+            bf16x8 bq, bql;
+            if constexpr (F32Q) {
+                const float* qr = static_cast<const float*>(p.queries) + (qo_base + (cval ? col : 0)) * D;
+                float4 q0 = make_float4(0.f, 0.f, 0.f, 0.f), q1 = q0;
+                if (cval && k0 < D) q0 = *reinterpret_cast<const float4*>(qr + k0);
+                if (cval && k0 + 16 < D) q1 = *reinterpret_cast<const float4*>(qr + k0 + 16);
+                u16x4 h0, l0, h1, l1;
+                split4(q0, h0, l0);
+                split4(q1, h1, l1);
+                bq = join(h0, h1);
+                bql = join(l0, l1);
+            } else {
+                const unsigned short* qr =
+                    static_cast<const unsigned short*>(p.queries) + (qo_base + (cval ? col : 0)) * D;
+                const u16x4 c0 = (cval && k0 < D) ? load_u16x4(qr + k0) : zero4();
+                const u16x4 c1 = (cval && k0 + 16 < D) ? load_u16x4(qr + k0 + 16) : zero4();
+                bq = join(c0, c1);
+            }
+#pragma unroll
+            for (int mi = 0; mi < MBW; ++mi) {
+                u16x4 h0, l0, h1, l1;
+                split4(st[mi][ks][0], h0, l0);
+                split4(st[mi][ks][1], h1, l1);
+                const bf16x8 ah = join(h0, h1), al = join(l0, l1);
+                acc[mi] = mfma16x16x32(ah, bq, acc[mi]);
+                acc[mi] = mfma16x16x32(al, bq, acc[mi]);
+                if constexpr (F32Q) acc[mi] = mfma16x16x32(ah, bql, acc[mi]);
+            }
+        }
+        if (cval) {
+#pragma unroll
+            for (int mi = 0; mi < MBW; ++mi) {
+                const int row0 = (wave + NWA * mi) * 16 + 4 * g;
+                *reinterpret_cast<float4*>(p.o + (qo_base + col) * D + row0) =
+                    make_float4(acc[mi][0], acc[mi][1], acc[mi][2], acc[mi][3]);
+            }
+        }
+    }
+}
+
+template <int D, bool F32Q>
+static hipError_t launch_t(const GatherArgs& a, hipStream_t st) {
+    const long long nblk = (long long)a.B * a.P * a.H;
+    if (nblk <= 0) return hipSuccess;
+    hipLaunchKernelGGL((gather_kernel<D, F32Q>), dim3((unsigned)nblk), dim3(256), 0, st, a);
+    return hipGetLastError();
+}
+
+template <bool F32Q>
+static hipError_t launch_f(const GatherArgs& a, hipStream_t st) {
+    switch (a.D) {
+        case 16: return launch_t<16, F32Q>(a, st);
+        case 32: return launch_t<32, F32Q>(a, st);
+        case 64: return launch_t<64, F32Q>(a, st);
+        case 128: return launch_t<128, F32Q>(a, st);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_gather(const GatherArgs& a, bool f32_queries, hipStream_t stream) {
+    return f32_queries ? launch_f<true>(a, stream) : launch_f<false>(a, stream);
+}
+
+}  // namespace ldv

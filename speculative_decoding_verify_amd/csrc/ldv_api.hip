@@ -1,0 +1,112 @@
+// The C ABI: host-side argument checks, then one kernel launch per call.
+// Every check happens before any HIP call, so argument errors are reported
+// without touching a device.
+#include <stdint.h>
+
+#include "ldv_kernels.hpp"
+
+#include "../../include/ldv.h"
+
+#define LDV_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+bool aligned(const void* p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
+
+bool supported_d(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+
+// Shared checks of the verify calls.
+int check_verify(int B, int T, int H, int dk, int dv, int dt, const void* q, const void* k, const void* v,
+                 const float* a, const float* beta, const float* S0, const float* o, const float* u_out,
+                 const float* logp_out, const int* status) {
+    if (B < 0 || T < 0 || H < 0 || dk <= 0 || dv <= 0) return LDV_ERR_ARG;
+    if (dt != LDV_BF16 && dt != LDV_F32) return LDV_ERR_ARG;
+    if ((u_out == nullptr) != (logp_out == nullptr)) return LDV_ERR_ARG;
+    if (dk != dv || !supported_d(dk) || T > LDV_MAX_T) return LDV_ERR_UNSUPPORTED;
+    if (B == 0 || T == 0 || H == 0) return LDV_OK;
+    if (!q || !k || !v || !a || !beta || !S0 || !o) return LDV_ERR_ARG;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(S0, 16) || !aligned(o, 16) ||
+        !aligned(u_out, 16) || !aligned(a, 4) || !aligned(beta, 4) || !aligned(logp_out, 4) ||
+        !aligned(status, 4))
+        return LDV_ERR_ARG;
+    if ((long long)B * H * 2 > 0x7fffffffLL || (long long)B * T > 0x7fffffffLL) return LDV_ERR_UNSUPPORTED;
+    return 1;  // proceed
+}
+
+int verify_common(int B, int T, int H, int d, int dt, const void* q, const void* k, const void* v, const float* a,
+                  const float* beta, const float* S0, const int32_t* parent, float* o, float* u_out,
+                  float* logp_out, int* status, void* stream) {
+    ldv::VerifyArgs args{B, T, H, d, q, k, v, a, beta, S0, parent, o, u_out, logp_out, status};
+    hipError_t e = ldv::launch_verify(args, dt == LDV_F32, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? LDV_OK : LDV_ERR_LAUNCH;
+}
+
+}  // namespace
+
+LDV_EXPORT int ldv_verify_tree(int B, int T, int H, int dk, int dv, int qkv_dtype, const void* q, const void* k,
+                               const void* v, const float* a, const float* beta, const float* S0,
+                               const int32_t* parent, float* o, float* u_out, float* logp_out, int* status,
+                               void* stream) {
+    int rc = check_verify(B, T, H, dk, dv, qkv_dtype, q, k, v, a, beta, S0, o, u_out, logp_out, status);
+    if (rc != 1) return rc;
+    if (!parent || !aligned(parent, 4)) return LDV_ERR_ARG;
+    return verify_common(B, T, H, dk, qkv_dtype, q, k, v, a, beta, S0, parent, o, u_out, logp_out, status, stream);
+}
+
+LDV_EXPORT int ldv_verify_chain(int B, int T, int H, int dk, int dv, int qkv_dtype, const void* q, const void* k,
+                                const void* v, const float* a, const float* beta, const float* S0, float* o,
+                                float* u_out, float* logp_out, int* status, void* stream) {
+    int rc = check_verify(B, T, H, dk, dv, qkv_dtype, q, k, v, a, beta, S0, o, u_out, logp_out, status);
+    if (rc != 1) return rc;
+    return verify_common(B, T, H, dk, qkv_dtype, q, k, v, a, beta, S0, nullptr, o, u_out, logp_out, status,
+                         stream);
+}
+
+LDV_EXPORT int ldv_commit_state(int B, int T, int H, int dk, int dv, int k_dtype, const void* k, const float* u,
+                                const float* logp, const int32_t* parent, const int32_t* accepted,
+                                const float* S0, float* S_out, int* status, void* stream) {
+    if (B < 0 || T < 0 || H < 0 || dk <= 0 || dv <= 0) return LDV_ERR_ARG;
+    if (k_dtype != LDV_BF16 && k_dtype != LDV_F32) return LDV_ERR_ARG;
+    if (dk != dv || !supported_d(dk) || T > LDV_MAX_T) return LDV_ERR_UNSUPPORTED;
+    if (B == 0 || H == 0) return LDV_OK;
+    if (!accepted || !S0 || !S_out) return LDV_ERR_ARG;
+    if (T > 0 && (!k || !u || !logp)) return LDV_ERR_ARG;
+    if (!aligned(k, 16) || !aligned(u, 16) || !aligned(S0, 16) || !aligned(S_out, 16) || !aligned(logp, 4) ||
+        !aligned(parent, 4) || !aligned(accepted, 4) || !aligned(status, 4))
+        return LDV_ERR_ARG;
+    if ((long long)B * H * 4 > 0x7fffffffLL) return LDV_ERR_UNSUPPORTED;
+    ldv::CommitArgs args{B, T, H, dk, k, u, logp, parent, accepted, S0, S_out, status};
+    hipError_t e = ldv::launch_commit(args, k_dtype == LDV_F32, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? LDV_OK : LDV_ERR_LAUNCH;
+}
+
+LDV_EXPORT int ldv_gather_states(int B, int P, int H, int dk, int dv, int num_slots, int Qn, int q_dtype,
+                                 const float* pool, const int32_t* slot, const void* queries, float* o,
+                                 float* states_out, int* status, void* stream) {
+    if (B < 0 || P < 0 || H < 0 || dk <= 0 || dv <= 0 || num_slots < 0) return LDV_ERR_ARG;
+    if (q_dtype != LDV_BF16 && q_dtype != LDV_F32) return LDV_ERR_ARG;
+    if ((queries == nullptr) != (o == nullptr)) return LDV_ERR_ARG;
+    if (queries && Qn < 0) return LDV_ERR_ARG;
+    if (dk != dv || !supported_d(dk)) return LDV_ERR_UNSUPPORTED;
+    if (B == 0 || P == 0 || H == 0) return LDV_OK;
+    if (!pool || !slot) return LDV_ERR_ARG;
+    if (!aligned(pool, 16) || !aligned(queries, 16) || !aligned(o, 16) || !aligned(states_out, 16) ||
+        !aligned(slot, 4) || !aligned(status, 4))
+        return LDV_ERR_ARG;
+    if ((long long)B * P * H > 0x7fffffffLL) return LDV_ERR_UNSUPPORTED;
+    ldv::GatherArgs args{B, P, H, dk, num_slots, queries ? Qn : 0, pool, slot, queries, o, states_out, status};
+    hipError_t e = ldv::launch_gather(args, q_dtype == LDV_F32, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? LDV_OK : LDV_ERR_LAUNCH;
+}
+
+LDV_EXPORT const char* ldv_status_string(int code) {
+    switch (code) {
+        case LDV_OK: return "ok";
+        case LDV_ERR_ARG: return "invalid argument (null pointer, negative size, bad dtype or misaligned pointer)";
+        case LDV_ERR_UNSUPPORTED: return "unsupported size (need d_k == d_v in {16, 32, 64, 128} and T <= 64)";
+        case LDV_ERR_LAUNCH: return "HIP kernel launch failed";
+        default: return "unknown status code";
+    }
+}
+
+LDV_EXPORT int ldv_version(void) { return 100; }

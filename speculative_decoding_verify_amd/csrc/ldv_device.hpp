@@ -1,0 +1,117 @@
+// Device helpers shared by the verify, commit and gather kernels (gfx950).
+//
+// MFMA tile used throughout: v_mfma_f32_16x16x32_bf16.  For one wave (64
+// lanes, g = lane / 16, c = lane % 16):
+//   A operand (16 x 32): lane holds row c, eight k-slots 8g .. 8g+7
+//   B operand (32 x 16): lane holds column c, the same eight k-slots
+//   C/D (16 x 16, 4 VGPRs): lane holds column c, rows 4g .. 4g+3
+// The k-slots of A and B are paired identically, so any fixed map from
+// k-slot to the true contraction index, applied to both operands, gives the
+// same product.  The map used here makes each lane's eight values two runs of
+// four consecutive k (k0 = 32s + 4g and k0 + 16), so a wave reading 16 rows
+// of an fp32 matrix touches 64 contiguous bytes per row per load.
+//
+// fp32 operands are carried as two bf16 terms, x = hi + lo with
+// hi = bf16(x) and lo = bf16(x - hi) (both round-to-nearest-even); the pair
+// holds x to about 2^-16 relative.  A bf16 operand times (hi + lo) in two
+// MFMAs with fp32 accumulation keeps fp32-state products near fp32 accuracy.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ldv {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef unsigned short u16x4 __attribute__((ext_vector_type(4)));
+typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
+
+constexpr int kWave = 64;
+constexpr int kXcds = 8;  // MI355X: 8 accelerator complex dies, one L2 each
+
+__device__ __forceinline__ floatx4 mfma16x16x32(bf16x8 a, bf16x8 b, floatx4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ unsigned short bf16_bits(float x) {
+    __bf16 h = (__bf16)x;  // v_cvt_pk_bf16_f32: round to nearest even
+    return __builtin_bit_cast(unsigned short, h);
+}
+
+__device__ __forceinline__ float bf16_val(unsigned short b) {
+    return __uint_as_float(((unsigned)b) << 16);
+}
+
+// hi/lo bf16 split of four fp32 values.
+__device__ __forceinline__ void split4(const float4 x, u16x4& hi, u16x4& lo) {
+    const float xs[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        unsigned short h = bf16_bits(xs[e]);
+        hi[e] = h;
+        lo[e] = bf16_bits(xs[e] - bf16_val(h));
+    }
+}
+
+__device__ __forceinline__ bf16x8 join(const u16x4 a, const u16x4 b) {
+    u16x8 r;
+    r[0] = a[0]; r[1] = a[1]; r[2] = a[2]; r[3] = a[3];
+    r[4] = b[0]; r[5] = b[1]; r[6] = b[2]; r[7] = b[3];
+    return __builtin_bit_cast(bf16x8, r);
+}
+
+__device__ __forceinline__ u16x4 zero4() {
+    u16x4 z = {0, 0, 0, 0};
+    return z;
+}
+
+// Four bf16 values (8 bytes) from LDS or global memory.
+__device__ __forceinline__ u16x4 load_u16x4(const unsigned short* p) {
+    return *reinterpret_cast<const u16x4*>(p);
+}
+
+// A/B fragment of k-step s from a bf16 row of length D (row = &M[r][0]).
+template <int D>
+__device__ __forceinline__ bf16x8 frag_row(const unsigned short* row, int s, int g) {
+    const int k0 = 32 * s + 4 * g;
+    u16x4 c0 = (k0 < D) ? load_u16x4(row + k0) : zero4();
+    u16x4 c1 = (k0 + 16 < D) ? load_u16x4(row + k0 + 16) : zero4();
+    return join(c0, c1);
+}
+
+// Block index remap so that consecutive logical blocks share an XCD (and its
+// L2).  The dispatcher places hardware block i on XCD i % 8; logical blocks
+// [base(x), base(x) + count(x)) are given to the hardware blocks of XCD x.
+__device__ __forceinline__ unsigned xcd_remap(unsigned bid, unsigned nblocks) {
+    const unsigned x = bid % kXcds, t = bid / kXcds;
+    const unsigned per = nblocks / kXcds, rem = nblocks % kXcds;
+    return (x < rem) ? x * (per + 1) + t : rem * (per + 1) + (x - rem) * per + t;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, kWave));
+    return v;
+}
+
+__device__ __forceinline__ int wave_max_i(int v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v = max(v, __shfl_xor(v, off, kWave));
+    return v;
+}
+
+__device__ __forceinline__ uint64_t shfl_u64(uint64_t v, int src) {
+    unsigned lo = (unsigned)v, hi = (unsigned)(v >> 32);
+    lo = __shfl(lo, src, kWave);
+    hi = __shfl(hi, src, kWave);
+    return ((uint64_t)hi << 32) | lo;
+}
+
+// Index of the i-th set bit (i counted from 0) of a uniform 64-bit mask.
+__device__ __forceinline__ int nth_set_bit(uint64_t m, int i) {
+    for (int j = 0; j < i; ++j) m &= m - 1;
+    return __builtin_ctzll(m);
+}
+
+}  // namespace ldv

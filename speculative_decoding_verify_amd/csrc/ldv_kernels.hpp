@@ -1,0 +1,52 @@
+// Kernel argument blocks and launchers (host side of the HIP library).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ldv {
+
+struct VerifyArgs {
+    int B, T, H, D;
+    const void* q;
+    const void* k;
+    const void* v;
+    const float* a;
+    const float* beta;
+    const float* S0;
+    const int32_t* parent;  // NULL: chain
+    float* o;
+    float* u_out;     // may be NULL (together with logp_out)
+    float* logp_out;  // may be NULL
+    int* status;      // may be NULL
+};
+
+struct CommitArgs {
+    int B, T, H, D;
+    const void* k;
+    const float* u;
+    const float* logp;
+    const int32_t* parent;  // NULL: chain
+    const int32_t* accepted;
+    const float* S0;
+    float* S_out;
+    int* status;
+};
+
+struct GatherArgs {
+    int B, P, H, D, num_slots, Qn;
+    const float* pool;
+    const int32_t* slot;
+    const void* queries;  // may be NULL
+    float* o;             // may be NULL
+    float* states_out;    // may be NULL
+    int* status;
+};
+
+// Each launcher assumes arguments already validated by the C ABI layer and
+// returns the HIP launch status.
+hipError_t launch_verify(const VerifyArgs& a, bool f32_inputs, hipStream_t stream);
+hipError_t launch_commit(const CommitArgs& a, bool f32_k, hipStream_t stream);
+hipError_t launch_gather(const GatherArgs& a, bool f32_queries, hipStream_t stream);
+
+}  // namespace ldv

@@ -1,0 +1,220 @@
+"""Python binding of the ldv C ABI (include/ldv.h): argument marshalling only.
+
+Every step of the verify / commit / gather path runs in the HIP kernels of
+libldv.so.  This module checks tensor placement, dtype, shape and layout,
+allocates outputs that the caller did not pass, and hands raw device pointers
+and torch's current HIP stream to the library.  There is no fallback: if the
+library is missing, loading fails loudly.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libldv.so")
+
+LDV_OK, LDV_ERR_ARG, LDV_ERR_UNSUPPORTED, LDV_ERR_LAUNCH = 0, -1, -2, -3
+LDV_BF16, LDV_F32 = 0, 1
+STATUS_BAD_PARENT, STATUS_BAD_ACCEPTED, STATUS_BAD_SLOT = 1, 2, 4
+MAX_T = 64
+
+_lib = None
+
+
+class LdvError(RuntimeError):
+    def __init__(self, fn: str, code: int):
+        super().__init__("%s failed: %d (%s)" % (fn, code, status_string(code)))
+        self.code = code
+
+
+def load(path: Optional[str] = None) -> ctypes.CDLL:
+    """Load libldv.so (built by speculative_decoding_verify_amd/build.py)."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise ImportError("libldv.so not found at %s: build it with "
+                          "`python -c 'import __graft_entry__ as g; g.build()'`" % p)
+    lib = ctypes.CDLL(p)
+    i, vp, fp, ip = ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p
+    lib.ldv_verify_tree.argtypes = [i, i, i, i, i, i, vp, vp, vp, fp, fp, fp, ip, fp, fp, fp, ip, vp]
+    lib.ldv_verify_chain.argtypes = [i, i, i, i, i, i, vp, vp, vp, fp, fp, fp, fp, fp, fp, ip, vp]
+    lib.ldv_commit_state.argtypes = [i, i, i, i, i, i, vp, fp, fp, ip, ip, fp, fp, ip, vp]
+    lib.ldv_gather_states.argtypes = [i, i, i, i, i, i, i, i, fp, ip, vp, fp, fp, ip, vp]
+    for f in ("ldv_verify_tree", "ldv_verify_chain", "ldv_commit_state", "ldv_gather_states", "ldv_version"):
+        getattr(lib, f).restype = ctypes.c_int
+    lib.ldv_status_string.argtypes = [ctypes.c_int]
+    lib.ldv_status_string.restype = ctypes.c_char_p
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def status_string(code: int) -> str:
+    return load().ldv_status_string(int(code)).decode()
+
+
+# ------------------------------------------------------------- marshalling
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dev(t: torch.Tensor, name: str, dtype=None, shape=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if t.device.type != "cuda":
+        raise ValueError("%s must be on the GPU (got %s)" % (name, t.device))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError("%s must be %s (got %s)" % (name, dtype, t.dtype))
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError("%s must have shape %s (got %s)" % (name, tuple(shape), tuple(t.shape)))
+    return t
+
+
+def _qkv_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return LDV_BF16
+    if t.dtype == torch.float32:
+        return LDV_F32
+    raise TypeError("q/k/v/queries must be bfloat16 or float32 (got %s)" % t.dtype)
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _check(fn: str, rc: int):
+    if rc != LDV_OK:
+        raise LdvError(fn, rc)
+
+
+def _opt(t, name, dtype, shape, dev):
+    if t is None:
+        return torch.empty(shape, dtype=dtype, device=dev)
+    return _dev(t, name, dtype, shape)
+
+
+def _verify(fn, q, k, v, a, beta, S0, parent, o, u, logp, factors, status, stream):
+    _dev(q, "q")
+    B, T, H, dk = q.shape
+    code = _qkv_code(q)
+    _dev(k, "k", q.dtype, (B, T, H, dk))
+    _dev(v, "v", q.dtype)
+    if v.dim() != 4 or tuple(v.shape[:3]) != (B, T, H):
+        raise ValueError("v must have shape [B, T, H, dv]")
+    dv = v.shape[3]
+    _dev(a, "a", torch.float32, (B, T, H))
+    _dev(beta, "beta", torch.float32, (B, T, H))
+    _dev(S0, "S0", torch.float32, (B, H, dv, dk))
+    dev = q.device
+    o = _opt(o, "o", torch.float32, (B, T, H, dv), dev)
+    if factors:
+        u = _opt(u, "u", torch.float32, (B, T, H, dv), dev)
+        logp = _opt(logp, "logp", torch.float32, (B, T, H), dev)
+    else:
+        u = logp = None
+    if status is not None:
+        _dev(status, "status", torch.int32)
+    args = [B, T, H, dk, dv, code, _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(beta), _ptr(S0)]
+    if fn == "ldv_verify_tree":
+        _dev(parent, "parent", torch.int32, (B, T))
+        args.append(_ptr(parent))
+    args += [_ptr(o), _ptr(u), _ptr(logp), _ptr(status), _stream(stream)]
+    _check(fn, getattr(load(), fn)(*args))
+    return o, u, logp
+
+
+def verify_chain(q, k, v, a, beta, S0, o=None, u=None, logp=None, factors=True,
+                 status=None, stream=None):
+    """Verify a chain of T drafts per sequence (parent[n] = n - 1).
+
+    q, k [B, T, H, dk] and v [B, T, H, dv] (bf16 or fp32, same dtype);
+    a, beta [B, T, H] fp32; S0 [B, H, dv, dk] fp32.  Returns (o, u, logp):
+    o [B, T, H, dv] fp32 and, when ``factors``, the commit factors u
+    [B, T, H, dv] and logp [B, T, H] (else None)."""
+    return _verify("ldv_verify_chain", q, k, v, a, beta, S0, None, o, u, logp, factors, status, stream)
+
+
+def verify_tree(q, k, v, a, beta, S0, parent, o=None, u=None, logp=None, factors=True,
+                status=None, stream=None):
+    """Verify a draft tree per sequence; parent [B, T] int32, parent[n] in [-1, n-1]."""
+    return _verify("ldv_verify_tree", q, k, v, a, beta, S0, parent, o, u, logp, factors, status, stream)
+
+
+def commit_state(k, u, logp, accepted, S0, S_out=None, parent=None, status=None, stream=None):
+    """Materialise the accepted node's state.  ``S_out=S0`` commits in place.
+
+    k [B, T, H, dk] (bf16/fp32), u [B, T, H, dv] and logp [B, T, H] from the
+    verify call, accepted [B] int32 in [-1, T-1], parent [B, T] int32 or None
+    (chain).  Returns S_out [B, H, dv, dk] fp32."""
+    _dev(k, "k")
+    B, T, H, dk = k.shape
+    code = _qkv_code(k)
+    _dev(u, "u", torch.float32)
+    if u.dim() != 4 or tuple(u.shape[:3]) != (B, T, H):
+        raise ValueError("u must have shape [B, T, H, dv]")
+    dv = u.shape[3]
+    _dev(logp, "logp", torch.float32, (B, T, H))
+    _dev(accepted, "accepted", torch.int32, (B,))
+    _dev(S0, "S0", torch.float32, (B, H, dv, dk))
+    if parent is not None:
+        _dev(parent, "parent", torch.int32, (B, T))
+    S_out = _opt(S_out, "S_out", torch.float32, (B, H, dv, dk), k.device)
+    if S_out.data_ptr() != S0.data_ptr():
+        lo0, hi0 = S0.data_ptr(), S0.data_ptr() + S0.numel() * 4
+        lo1, hi1 = S_out.data_ptr(), S_out.data_ptr() + S_out.numel() * 4
+        if lo0 < hi1 and lo1 < hi0:
+            raise ValueError("S_out overlaps S0 without being S0")
+    if status is not None:
+        _dev(status, "status", torch.int32)
+    _check("ldv_commit_state", load().ldv_commit_state(
+        B, T, H, dk, dv, code, _ptr(k), _ptr(u), _ptr(logp), _ptr(parent), _ptr(accepted),
+        _ptr(S0), _ptr(S_out), _ptr(status), _stream(stream)))
+    return S_out
+
+
+def gather_states(pool, slot, queries=None, o=None, states_out=None, want_states=False,
+                  status=None, stream=None):
+    """Read pool states at slot[b, p]: o = pool[slot, h] q_i for each query and,
+    when ``want_states`` (or states_out is given), a bit copy of the states.
+
+    pool [num_slots, H, dv, dk] fp32; slot [B, P] int32; queries
+    [B, P, H, Qn, dk] bf16/fp32 or None.  Returns (o, states_out)."""
+    _dev(pool, "pool", torch.float32)
+    num_slots, H, dv, dk = pool.shape
+    _dev(slot, "slot", torch.int32)
+    B, P = slot.shape
+    dev = pool.device
+    code, Qn = LDV_BF16, 0
+    if queries is not None:
+        _dev(queries, "queries")
+        code = _qkv_code(queries)
+        if queries.dim() != 5 or tuple(queries.shape[:3]) != (B, P, H) or queries.shape[4] != dk:
+            raise ValueError("queries must have shape [B, P, H, Qn, dk]")
+        Qn = queries.shape[3]
+        o = _opt(o, "o", torch.float32, (B, P, H, Qn, dv), dev)
+    else:
+        o = None
+    if states_out is None and want_states:
+        states_out = torch.empty((B, P, H, dv, dk), dtype=torch.float32, device=dev)
+    elif states_out is not None:
+        _dev(states_out, "states_out", torch.float32, (B, P, H, dv, dk))
+    if status is not None:
+        _dev(status, "status", torch.int32)
+    _check("ldv_gather_states", load().ldv_gather_states(
+        B, P, H, dk, dv, num_slots, Qn, code, _ptr(pool), _ptr(slot), _ptr(queries), _ptr(o),
+        _ptr(states_out), _ptr(status), _stream(stream)))
+    return o, states_out
+
+
+def version() -> int:
+    return load().ldv_version()

@@ -1,0 +1,80 @@
+"""Helpers for the GPU parity tests: move seeded inputs to the device, call the
+HIP library through its binding, compare with the fp64 oracle."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+# max |gpu - oracle| / max |oracle| over an output tensor must not exceed this
+# (the bar for bf16 q/k/v with an fp32 state).
+TOL = 2e-3
+# the kernels carry fp32 state products as bf16 hi + lo terms (about 2^-16
+# relative); this tighter bound catches a lost lo term or a dropped factor,
+# which would still pass TOL.
+DESIGN_TOL = 2e-4
+
+
+def dev(x, dtype=None):
+    t = torch.from_numpy(np.ascontiguousarray(x)).cuda()
+    return t if dtype is None else t.to(dtype)
+
+
+def qkv_torch_dtype(name: str):
+    return torch.bfloat16 if name == "bf16" else torch.float32
+
+
+def to_device(x: dict, qkv: str) -> dict:
+    """Inputs from workloads.make_inputs (numpy) to device tensors."""
+    dt = qkv_torch_dtype(qkv)
+    d = {}
+    for key in ("q", "k", "v"):
+        d[key] = dev(x[key], dt)
+    for key in ("a", "beta", "S0"):
+        d[key] = dev(x[key])
+    d["parent"] = dev(x["parent"])
+    if "accepted" in x:
+        d["accepted"] = dev(x["accepted"])
+    if "pool" in x:
+        d["pool"] = dev(x["pool"])
+        d["slot"] = dev(x["slot"])
+        d["queries"] = dev(x["queries"], dt)
+    return d
+
+
+def host(t: torch.Tensor) -> np.ndarray:
+    return t.detach().double().cpu().numpy()
+
+
+def rel_err(x, ref) -> float:
+    x = np.asarray(x, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    den = np.max(np.abs(ref)) if ref.size else 0.0
+    return float(np.max(np.abs(x - ref)) / (den if den > 0 else 1.0)) if ref.size else 0.0
+
+
+def check(name, gpu, ref, tol=TOL, design_tol=DESIGN_TOL, group_axes=None):
+    """Assert the relative error of a whole output tensor (and, with
+    group_axes, of every (sequence, head) slice) is within tol and the design
+    bound.  Returns the whole-tensor error."""
+    g = host(gpu) if isinstance(gpu, torch.Tensor) else np.asarray(gpu, np.float64)
+    assert g.shape == ref.shape, (name, g.shape, ref.shape)
+    assert np.all(np.isfinite(g)), name + ": non-finite values"
+    e = rel_err(g, ref)
+    print("%-28s rel err %.3e" % (name, e), flush=True)
+    assert e <= tol, "%s: %.3e > %.1e" % (name, e, tol)
+    assert e <= design_tol, "%s: %.3e above the design bound %.1e" % (name, e, design_tol)
+    return e
+
+
+def log_p(a: np.ndarray, parent: np.ndarray) -> np.ndarray:
+    """sum of log a over each root-to-n path, fp64 ([B, T, H]), each log a
+    clamped below at -87 as the library defines its log P output."""
+    B, T, H = a.shape
+    with np.errstate(divide="ignore"):
+        la = np.maximum(np.log(a.astype(np.float64)), -87.0)
+    out = np.zeros((B, T, H))
+    for b in range(B):
+        for n in range(T):
+            p = int(parent[b, n])
+            out[b, n] = la[b, n] + (out[b, p] if p >= 0 else 0.0)
+    return out

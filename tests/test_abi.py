@@ -1,0 +1,94 @@
+"""The C-ABI library loads, exports every call include/ldv.h declares, and
+rejects bad arguments on the host before touching a device (CPU only)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ldv.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from speculative_decoding_verify_amd import ldv
+    return ldv.load()
+
+
+def declared():
+    with open(HEADER) as f:
+        text = f.read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(ldv_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_calls():
+    names = declared()
+    for n in ("ldv_verify_chain", "ldv_verify_tree", "ldv_commit_state", "ldv_gather_states"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared():
+        assert hasattr(lib, name), name
+
+
+def test_only_the_abi_is_exported():
+    out = os.popen("nm -D --defined-only %s" % os.path.join(ROOT, "speculative_decoding_verify_amd", "libldv.so")).read()
+    syms = {l.split()[-1] for l in out.splitlines() if " T " in l}
+    assert syms == set(declared()), syms ^ set(declared())
+
+
+FAKE = ctypes.c_void_p(0x10000)       # never dereferenced: checks fail first
+MIS = ctypes.c_void_p(0x10004)        # 4-byte aligned, not 16
+
+
+def verify_chain(lib, B=1, T=4, H=1, dk=128, dv=128, dt=0, q=FAKE, o=FAKE, u=None, lp=None, a=FAKE):
+    return lib.ldv_verify_chain(B, T, H, dk, dv, dt, q, FAKE, FAKE, a, FAKE, FAKE, o, u, lp, None, None)
+
+
+def test_verify_argument_codes(lib):
+    assert verify_chain(lib, B=-1) == -1
+    assert verify_chain(lib, dt=7) == -1
+    assert verify_chain(lib, q=None) == -1
+    assert verify_chain(lib, o=None) == -1
+    assert verify_chain(lib, q=MIS) == -1
+    assert verify_chain(lib, u=FAKE, lp=None) == -1
+    assert verify_chain(lib, T=65) == -2
+    assert verify_chain(lib, dk=96, dv=96) == -2
+    assert verify_chain(lib, dk=128, dv=64) == -2
+    assert verify_chain(lib, B=0) == 0
+    assert verify_chain(lib, T=0, q=None) == 0
+    # the tree call also needs a parent array
+    assert lib.ldv_verify_tree(1, 4, 1, 128, 128, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None,
+                               FAKE, None, None, None, None) == -1
+
+
+def test_commit_argument_codes(lib):
+    c = lambda **kw: lib.ldv_commit_state(kw.get("B", 1), kw.get("T", 4), 1, 128, 128, kw.get("dt", 0),
+                                          kw.get("k", FAKE), FAKE, FAKE, None, kw.get("acc", FAKE),
+                                          kw.get("S0", FAKE), kw.get("out", FAKE), None, None)
+    assert c(dt=3) == -1
+    assert c(acc=None) == -1
+    assert c(out=None) == -1
+    assert c(S0=MIS) == -1
+    assert c(T=65) == -2
+    assert c(B=0) == 0
+
+
+def test_gather_argument_codes(lib):
+    g = lambda **kw: lib.ldv_gather_states(kw.get("B", 1), 1, 1, kw.get("d", 128), kw.get("d", 128), 4, 16,
+                                           kw.get("dt", 0), kw.get("pool", FAKE), kw.get("slot", FAKE),
+                                           kw.get("q", FAKE), kw.get("o", FAKE), None, None, None)
+    assert g(pool=None) == -1
+    assert g(slot=None) == -1
+    assert g(q=None) == -1           # queries and o come together
+    assert g(d=48) == -2
+    assert g(dt=2) == -1
+    assert g(B=0) == 0
+
+
+def test_status_strings(lib):
+    lib.ldv_status_string.restype = ctypes.c_char_p
+    assert lib.ldv_status_string(0) == b"ok"
+    assert b"unsupported" in lib.ldv_status_string(-2)
