@@ -111,6 +111,9 @@ def main():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum CPU-oracle time")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device-to-device copy of BYTES bytes (5 times), to scale "
+                         "rocprofv3 FETCH_SIZE / WRITE_SIZE counters, and print its bandwidth")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path "
@@ -119,6 +122,21 @@ def main():
         sys.exit(2)
 
     import torch
+    if args.copy_calibration:
+        n = args.copy_calibration // 4
+        src = torch.ones(n, device="cuda")
+        dst = torch.empty(n, device="cuda")
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(5):
+            dst.copy_(src)
+        e1.record()
+        torch.cuda.synchronize()
+        t = e0.elapsed_time(e1) * 1e-3 / 5
+        print(json.dumps({"copy_bytes": n * 4, "copy_us": t * 1e6, "copy_GB_s_read_plus_write": 2 * n * 4 / t / 1e9}))
+        return
     import speculative_decoding_verify_amd as ldv
 
     wl = WORKLOADS[args.workload]

@@ -11,11 +11,13 @@
 //
 // The work is a streaming read of S0 and write of S_out (64 KiB each per head
 // at d = 128), so it is bound by HBM.  One block of 256 threads per
-// (sequence, head, row block of RB rows); each thread owns float4 chunks of
-// consecutive columns so that every wave reads and writes contiguous 1 KiB
-// runs.  The block first issues its S0 loads, then walks the parent row in
-// LDS from the accepted node to the root, stages w_m u_m (its RB rows) and
-// k_m (all columns) for the path in LDS, and applies the update.
+// (sequence, head, row block of up to 32 KiB); each thread owns float4 chunks
+// of consecutive columns so that every wave reads and writes contiguous 1 KiB
+// runs.  The block loads the parent row, then its S0 rows; walks the parent
+// row in LDS from the accepted node to the root while the state is in
+// flight; issues the loads of u, k and log P on the path; stages w_m u_m (its
+// rows) and k_m (all columns) for up to 16 path nodes at a time in LDS; and
+// applies the update.
 #include "ldv_device.hpp"
 #include "ldv_kernels.hpp"
 
@@ -25,24 +27,28 @@ namespace ldv {
 
 template <int D>
 struct CShape {
-    static constexpr int E = D * D < 4096 ? D * D : 4096;  // floats per block
-    static constexpr int RB = E / D;                       // rows per block
-    static constexpr int NRB = D / RB;                     // row blocks per head
     static constexpr int NTHR = 256;
-    static constexpr int F4 = (E / 4 + NTHR - 1) / NTHR;   // float4 chunks per thread
+    static constexpr int C4 = D / 4;                                  // float4 per state row (divides NTHR)
+    static constexpr int E4 = (D * D / 4 < 2048) ? D * D / 4 : 2048;  // float4 per block (<= 32 KiB)
+    static constexpr int RB = E4 / C4;                                // rows per block
+    static constexpr int NRB = D / RB;                                // row blocks per head
+    static constexpr int F4 = (E4 + NTHR - 1) / NTHR;                 // float4 per thread
+    static constexpr int PCH = 16;                                    // path nodes staged per pass
 };
 
 template <int D, bool F32K>
 __global__ __launch_bounds__(256) void commit_kernel(const CommitArgs p) {
     using S = CShape<D>;
-    constexpr int E = S::E, RB = S::RB, F4 = S::F4, NTHR = S::NTHR;
-    __shared__ __align__(16) float s_k[LDV_MAX_T * D];
-    __shared__ float s_uw[LDV_MAX_T * RB];
+    constexpr int C4 = S::C4, E4 = S::E4, RB = S::RB, F4 = S::F4, NTHR = S::NTHR, PCH = S::PCH;
+    constexpr int KI = (PCH * C4 + NTHR - 1) / NTHR;  // k chunks staged per thread and pass
+    constexpr int UI = (PCH * RB + NTHR - 1) / NTHR;  // u values staged per thread and pass
+    __shared__ float4 s_k[PCH * C4];  // k rows of up to PCH path nodes (fp32)
+    __shared__ float s_uw[PCH * RB];  // (P_n / P_m) u_m over this block's rows
     __shared__ int s_par[LDV_MAX_T];
     __shared__ int s_path[LDV_MAX_T];
     __shared__ int s_len, s_bad;
 
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int T = p.T, H = p.H;
     const unsigned bid = xcd_remap(blockIdx.x, gridDim.x);
     const int rb = (int)(bid % S::NRB);
@@ -55,35 +61,39 @@ __global__ __launch_bounds__(256) void commit_kernel(const CommitArgs p) {
         return;
     }
     if (nacc < 0 && p.S_out == p.S0) return;  // in place, nothing accepted: no traffic
-    const size_t base = ((size_t)b * H + h) * D * D + (size_t)rb * E;
-    const float4* src = reinterpret_cast<const float4*>(p.S0 + base);
-    float4* dst = reinterpret_cast<float4*>(p.S_out + base);
 
+    // Loads: the parent row, then this block's S0 rows; nothing waits for the
+    // parent row before the S0 loads are issued (branch-free, clamped index;
+    // a chain reads its log P array instead and discards the value).
+    const global_ptr<const int32_t> parp =
+        (global_ptr<const int32_t>)(p.parent ? p.parent : reinterpret_cast<const int32_t*>(p.logp));
+    const int par_ld = (T > 0) ? parp[(size_t)b * T + min(lane, T - 1)] : -1;
+    const size_t base = ((size_t)b * H + h) * D * D + (size_t)rb * RB * D;
+    const float* src = p.S0 + base;
+    float* dst = p.S_out + base;
     float4 sv[F4];
 #pragma unroll
     for (int i = 0; i < F4; ++i) {
         const int f = tid + NTHR * i;
-        if (f < E / 4) sv[i] = src[f];
+        if (F4 * NTHR == E4 || f < E4) sv[i] = ld_stream(src + 4 * f);
     }
+    asm volatile("" ::: "memory");  // keep the loads above ahead of any use of them
     if (nacc < 0) {  // nothing accepted, out of place: copy the committed state
 #pragma unroll
         for (int i = 0; i < F4; ++i) {
             const int f = tid + NTHR * i;
-            if (f < E / 4) dst[f] = sv[i];
+            if (F4 * NTHR == E4 || f < E4) st_stream(dst + 4 * f, sv[i]);
         }
         return;
     }
 
-    // parent row: validate (as verify does) and keep it in LDS
-    if (tid < kWave) {
-        const int n = tid;
-        const bool valid = n < T;
-        int par = -1;
-        if (valid) par = p.parent ? p.parent[(size_t)b * T + n] : n - 1;
-        const bool bad = valid && (par < -1 || par >= n);
+    // validate the parent row (as verify does) and walk from the accepted node
+    if (wave == 0) {
+        const int par = p.parent ? par_ld : lane - 1;
+        const bool bad = lane < T && (par < -1 || par >= lane);
         const uint64_t badm = __ballot(bad);
-        if (valid) s_par[n] = par;
-        if (tid == 0) {
+        if (lane < T) s_par[lane] = par;
+        if (lane == 0) {
             s_bad = badm != 0ull;
             if (badm != 0ull && p.status && h == 0 && rb == 0) atomicOr(p.status, LDV_STATUS_BAD_PARENT);
         }
@@ -97,52 +107,68 @@ __global__ __launch_bounds__(256) void commit_kernel(const CommitArgs p) {
     }
     __syncthreads();
     const int len = s_len;
-    const float lp_n = p.logp[((size_t)b * T + nacc) * H + h];
-    const float Pn = expf(lp_n);
+    const int col4 = tid % C4;  // this thread's chunks share one column group (C4 divides NTHR)
 
-    if constexpr (F32K) {
-        const float* kg = static_cast<const float*>(p.k);
-        for (int idx = tid; idx < len * (D / 4); idx += NTHR) {
-            const int i = idx / (D / 4), col = (idx % (D / 4)) * 4;
-            const int m = s_path[i];
-            *reinterpret_cast<float4*>(s_k + i * D + col) =
-                *reinterpret_cast<const float4*>(kg + (((size_t)b * T + m) * H + h) * D + col);
+    for (int c0 = 0; c0 < len; c0 += PCH) {
+        const int cl = min(PCH, len - c0);
+        // issue every load of this pass before using any of them
+        const float lp_n = p.logp[((size_t)b * T + nacc) * H + h];
+        float4 kf[KI];
+        u16x4 kb[KI];
+        float uval[UI], lval[UI];
+#pragma unroll
+        for (int j = 0; j < KI; ++j) {
+            const int idx = tid + NTHR * j, i = min(idx / C4, cl - 1), c4 = idx % C4;
+            const size_t krow = (((size_t)b * T + s_path[c0 + i]) * H + h) * D;
+            if constexpr (F32K) kf[j] = *reinterpret_cast<const float4*>(static_cast<const float*>(p.k) + krow + 4 * c4);
+            else kb[j] = load_u16x4(static_cast<const unsigned short*>(p.k) + krow + 4 * c4);
         }
-    } else {
-        const unsigned short* kg = static_cast<const unsigned short*>(p.k);
-        for (int idx = tid; idx < len * (D / 4); idx += NTHR) {
-            const int i = idx / (D / 4), col = (idx % (D / 4)) * 4;
-            const int m = s_path[i];
-            const u16x4 kv = load_u16x4(kg + (((size_t)b * T + m) * H + h) * D + col);
-            *reinterpret_cast<float4*>(s_k + i * D + col) =
-                make_float4(bf16_val(kv[0]), bf16_val(kv[1]), bf16_val(kv[2]), bf16_val(kv[3]));
+#pragma unroll
+        for (int j = 0; j < UI; ++j) {
+            const int idx = tid + NTHR * j, i = min(idx / RB, cl - 1), r = idx % RB;
+            const size_t node = ((size_t)b * T + s_path[c0 + i]) * H + h;
+            uval[j] = p.u[node * D + (size_t)rb * RB + r];
+            lval[j] = p.logp[node];
         }
+#pragma unroll
+        for (int j = 0; j < KI; ++j) {
+            const int idx = tid + NTHR * j;
+            if (idx < cl * C4) {
+                if constexpr (F32K) s_k[idx] = kf[j];
+                else s_k[idx] = make_float4(bf16_val(kb[j][0]), bf16_val(kb[j][1]), bf16_val(kb[j][2]), bf16_val(kb[j][3]));
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < UI; ++j) {
+            const int idx = tid + NTHR * j;
+            if (idx < cl * RB) s_uw[idx] = expf(lp_n - lval[j]) * uval[j];
+        }
+        if (c0 == 0) {
+            const float Pn = expf(lp_n);
+#pragma unroll
+            for (int i = 0; i < F4; ++i) sv[i] = make_float4(Pn * sv[i].x, Pn * sv[i].y, Pn * sv[i].z, Pn * sv[i].w);
+        }
+        __syncthreads();
+        for (int m = 0; m < cl; ++m) {
+            const float4 kk = s_k[m * C4 + col4];
+#pragma unroll
+            for (int i = 0; i < F4; ++i) {
+                const int f = tid + NTHR * i;
+                if (F4 * NTHR == E4 || f < E4) {
+                    const float w = s_uw[m * RB + f / C4];
+                    sv[i].x += w * kk.x;
+                    sv[i].y += w * kk.y;
+                    sv[i].z += w * kk.z;
+                    sv[i].w += w * kk.w;
+                }
+            }
+        }
+        __syncthreads();
     }
-    for (int idx = tid; idx < len * RB; idx += NTHR) {
-        const int i = idx / RB, r = idx % RB;
-        const int m = s_path[i];
-        const size_t node = ((size_t)b * T + m) * H + h;
-        const float w = expf(lp_n - p.logp[node]);
-        s_uw[i * RB + r] = w * p.u[node * D + (size_t)rb * RB + r];
-    }
-    __syncthreads();
-
 #pragma unroll
     for (int i = 0; i < F4; ++i) {
         const int f = tid + NTHR * i;
-        if (f < E / 4) {
-            const int row = f / (D / 4), col = (f % (D / 4)) * 4;
-            float4 acc = make_float4(Pn * sv[i].x, Pn * sv[i].y, Pn * sv[i].z, Pn * sv[i].w);
-            for (int m = 0; m < len; ++m) {
-                const float w = s_uw[m * RB + row];
-                const float4 kk = *reinterpret_cast<const float4*>(s_k + m * D + col);
-                acc.x += w * kk.x;
-                acc.y += w * kk.y;
-                acc.z += w * kk.z;
-                acc.w += w * kk.w;
-            }
-            dst[f] = acc;
-        }
+        if (F4 * NTHR == E4 || f < E4) st_stream(dst + 4 * f, sv[i]);
     }
 }
 

@@ -7,12 +7,13 @@
 //   s = slot[b, p];  o[b, p, h, i, :] = pool[s, h] q_i  for i < Qn;
 //   states_out[b, p, h] = pool[s, h]  (optional bit copy).
 //
-// One block of four waves per (sequence, position, head).  Each wave loads
-// its 16-row blocks of the fp32 state straight into MFMA A-operand registers
-// (64 contiguous bytes per row per load), writes the copy from the same
-// registers, and multiplies by the queries on MFMA with the state split into
-// bf16 hi + lo terms.  The read of the 64 KiB state dominates: the kernel is
-// bound by HBM.
+// One block of four waves per 64 rows of a (sequence, position, head) state
+// (two blocks per state at d = 128: small blocks with few registers keep more
+// loads in flight per CU).  Each wave loads its 16-row block of the fp32
+// state straight into MFMA A-operand registers (64 contiguous bytes per row
+// per load), writes the copy from the same registers, and multiplies by the
+// queries on MFMA with the state split into bf16 hi + lo terms.  The read of
+// the 64 KiB state dominates: the kernel is bound by HBM.
 #include "ldv_device.hpp"
 #include "ldv_kernels.hpp"
 
@@ -23,8 +24,9 @@ namespace ldv {
 template <int D>
 struct GShape {
     static constexpr int MBT = D / 16;             // 16-row blocks per state
-    static constexpr int NWA = MBT < 4 ? MBT : 4;  // waves holding rows
-    static constexpr int MBW = MBT / NWA;          // row blocks per wave
+    static constexpr int NWA = MBT < 4 ? MBT : 4;  // waves holding rows (one 16-row block each)
+    static constexpr int NSPLIT = MBT / NWA;       // blocks per (sequence, position, head)
+    static constexpr int MBW = 1;                  // row blocks per wave
     static constexpr int KS = (D + 31) / 32;       // MFMA k-steps
 };
 
@@ -36,49 +38,89 @@ __global__ __launch_bounds__(256) void gather_kernel(const GatherArgs p) {
     const int c = lane & 15, g = lane >> 4;
     const int H = p.H;
     const unsigned bid = xcd_remap(blockIdx.x, gridDim.x);
-    const int h = (int)(bid % H);
-    const size_t bp = bid / H;  // b * P + p
+    const int part = (int)(bid % S::NSPLIT);  // which 16 * NWA rows of the state
+    const int h = (int)((bid / S::NSPLIT) % H);
+    const size_t bp = bid / S::NSPLIT / H;  // b * P + p
 
     const int s = p.slot[bp];
     if (s < 0 || s >= p.num_slots) {
-        if (tid == 0 && p.status && h == 0) atomicOr(p.status, LDV_STATUS_BAD_SLOT);
+        if (tid == 0 && p.status && h == 0 && part == 0) atomicOr(p.status, LDV_STATUS_BAD_SLOT);
         return;
     }
     if (wave >= NWA) return;
     const float* src = p.pool + ((size_t)s * H + h) * D * D;
+    const bool reads = p.queries && p.o && p.Qn > 0;
+    const size_t qo_base = ((size_t)bp * H + h) * (size_t)p.Qn;
 
-    float4 st[MBW][KS][2];
-#pragma unroll
-    for (int mi = 0; mi < MBW; ++mi) {
-        const int row = (wave + NWA * mi) * 16 + c;
+    // queries of the first 16-column block (the common case is Qn <= 16)
+    // before the state, so that waiting for them leaves the state in flight.
+    // The loads are unconditional per lane (row clamped into range); lanes
+    // past Qn drop their values when the operand is formed.
+    u16x4 qc[KS][2];
+    float4 qf[KS][2];
+    if (reads) {
+        const size_t qrow = (qo_base + min(c, p.Qn - 1)) * D;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             const int k0 = 32 * ks + 4 * g;
-            st[mi][ks][0] = (k0 < D) ? *reinterpret_cast<const float4*>(src + (size_t)row * D + k0)
-                                     : make_float4(0.f, 0.f, 0.f, 0.f);
-            st[mi][ks][1] = (k0 + 16 < D) ? *reinterpret_cast<const float4*>(src + (size_t)row * D + k0 + 16)
+            if constexpr (F32Q) {
+                const float* qr = static_cast<const float*>(p.queries) + qrow;
+                if (k0 < D) qf[ks][0] = *reinterpret_cast<const float4*>(qr + k0);
+                if (k0 + 16 < D) qf[ks][1] = *reinterpret_cast<const float4*>(qr + k0 + 16);
+            } else {
+                const unsigned short* qr = static_cast<const unsigned short*>(p.queries) + qrow;
+                if (k0 < D) qc[ks][0] = load_u16x4(qr + k0);
+                if (k0 + 16 < D) qc[ks][1] = load_u16x4(qr + k0 + 16);
+            }
+        }
+    }
+    float4 st[MBW][KS][2];
+#pragma unroll
+    for (int mi = 0; mi < MBW; ++mi) {
+        const int row = ((part * NWA + wave) * MBW + mi) * 16 + c;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const int k0 = 32 * ks + 4 * g;
+            st[mi][ks][0] = (k0 < D) ? ld_stream(src + (size_t)row * D + k0) : make_float4(0.f, 0.f, 0.f, 0.f);
+            st[mi][ks][1] = (k0 + 16 < D) ? ld_stream(src + (size_t)row * D + k0 + 16)
                                           : make_float4(0.f, 0.f, 0.f, 0.f);
         }
     }
+    asm volatile("" ::: "memory");  // keep the loads above ahead of any use of them
     if (p.states_out) {
         float* dst = p.states_out + ((size_t)bp * H + h) * D * D;
 #pragma unroll
         for (int mi = 0; mi < MBW; ++mi) {
-            const int row = (wave + NWA * mi) * 16 + c;
+            const int row = ((part * NWA + wave) * MBW + mi) * 16 + c;
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
                 const int k0 = 32 * ks + 4 * g;
-                if (k0 < D) *reinterpret_cast<float4*>(dst + (size_t)row * D + k0) = st[mi][ks][0];
-                if (k0 + 16 < D) *reinterpret_cast<float4*>(dst + (size_t)row * D + k0 + 16) = st[mi][ks][1];
+                if (k0 < D) st_stream(dst + (size_t)row * D + k0, st[mi][ks][0]);
+                if (k0 + 16 < D) st_stream(dst + (size_t)row * D + k0 + 16, st[mi][ks][1]);
             }
         }
     }
-    if (!p.queries || !p.o || p.Qn <= 0) return;
+    if (!reads) return;
 
-    const size_t qo_base = ((size_t)bp * H + h) * (size_t)p.Qn;
     for (int nb = 0; nb * 16 < p.Qn; ++nb) {
         const int col = nb * 16 + c;  // query index held by this lane
         const bool cval = col < p.Qn;
+        if (nb > 0) {  // later 16-query blocks (Qn > 16)
+            const size_t qrow = (qo_base + min(col, p.Qn - 1)) * D;
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const int k0 = 32 * ks + 4 * g;
+                if constexpr (F32Q) {
+                    const float* qr = static_cast<const float*>(p.queries) + qrow;
+                    if (k0 < D) qf[ks][0] = *reinterpret_cast<const float4*>(qr + k0);
+                    if (k0 + 16 < D) qf[ks][1] = *reinterpret_cast<const float4*>(qr + k0 + 16);
+                } else {
+                    const unsigned short* qr = static_cast<const unsigned short*>(p.queries) + qrow;
+                    if (k0 < D) qc[ks][0] = load_u16x4(qr + k0);
+                    if (k0 + 16 < D) qc[ks][1] = load_u16x4(qr + k0 + 16);
+                }
+            }
+        }
         floatx4 acc[MBW];
 #pragma unroll
         for (int mi = 0; mi < MBW; ++mi) acc[mi] = floatx4{0.f, 0.f, 0.f, 0.f};
@@ -87,21 +129,14 @@ __global__ __launch_bounds__(256) void gather_kernel(const GatherArgs p) {
             const int k0 = 32 * ks + 4 * g;
             bf16x8 bq, bql;
             if constexpr (F32Q) {
-                const float* qr = static_cast<const float*>(p.queries) + (qo_base + (cval ? col : 0)) * D;
-                float4 q0 = make_float4(0.f, 0.f, 0.f, 0.f), q1 = q0;
-                if (cval && k0 < D) q0 = *reinterpret_cast<const float4*>(qr + k0);
-                if (cval && k0 + 16 < D) q1 = *reinterpret_cast<const float4*>(qr + k0 + 16);
+                const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
                 u16x4 h0, l0, h1, l1;
-                split4(q0, h0, l0);
-                split4(q1, h1, l1);
+                split4((cval && k0 < D) ? qf[ks][0] : z, h0, l0);
+                split4((cval && k0 + 16 < D) ? qf[ks][1] : z, h1, l1);
                 bq = join(h0, h1);
                 bql = join(l0, l1);
             } else {
-                const unsigned short* qr =
-                    static_cast<const unsigned short*>(p.queries) + (qo_base + (cval ? col : 0)) * D;
-                const u16x4 c0 = (cval && k0 < D) ? load_u16x4(qr + k0) : zero4();
-                const u16x4 c1 = (cval && k0 + 16 < D) ? load_u16x4(qr + k0 + 16) : zero4();
-                bq = join(c0, c1);
+                bq = join((cval && k0 < D) ? qc[ks][0] : zero4(), (cval && k0 + 16 < D) ? qc[ks][1] : zero4());
             }
 #pragma unroll
             for (int mi = 0; mi < MBW; ++mi) {
@@ -117,9 +152,8 @@ __global__ __launch_bounds__(256) void gather_kernel(const GatherArgs p) {
         if (cval) {
 #pragma unroll
             for (int mi = 0; mi < MBW; ++mi) {
-                const int row0 = (wave + NWA * mi) * 16 + 4 * g;
-                *reinterpret_cast<float4*>(p.o + (qo_base + col) * D + row0) =
-                    make_float4(acc[mi][0], acc[mi][1], acc[mi][2], acc[mi][3]);
+                const int row0 = ((part * NWA + wave) * MBW + mi) * 16 + 4 * g;
+                st_stream(p.o + (qo_base + col) * D + row0, make_float4(acc[mi][0], acc[mi][1], acc[mi][2], acc[mi][3]));
             }
         }
     }
@@ -127,7 +161,7 @@ __global__ __launch_bounds__(256) void gather_kernel(const GatherArgs p) {
 
 template <int D, bool F32Q>
 static hipError_t launch_t(const GatherArgs& a, hipStream_t st) {
-    const long long nblk = (long long)a.B * a.P * a.H;
+    const long long nblk = (long long)a.B * a.P * a.H * GShape<D>::NSPLIT;
     if (nblk <= 0) return hipSuccess;
     hipLaunchKernelGGL((gather_kernel<D, F32Q>), dim3((unsigned)nblk), dim3(256), 0, st, a);
     return hipGetLastError();

@@ -26,6 +26,15 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef unsigned short u16x4 __attribute__((ext_vector_type(4)));
 typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
+// 16 raw bytes as a native vector: copies stay in registers (HIP's uint4 is
+// a struct whose copies can be lowered to memcpy through private memory)
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// A pointer into global memory (address space 1): loads through it are
+// global_load instructions, never flat ones (a pending flat load makes the
+// compiler wait for every outstanding memory operation).
+template <typename T>
+using global_ptr = __attribute__((address_space(1))) T*;
 
 constexpr int kWave = 64;
 constexpr int kXcds = 8;  // MI355X: 8 accelerator complex dies, one L2 each
@@ -64,6 +73,52 @@ __device__ __forceinline__ bf16x8 join(const u16x4 a, const u16x4 b) {
 __device__ __forceinline__ u16x4 zero4() {
     u16x4 z = {0, 0, 0, 0};
     return z;
+}
+
+// hi/lo split of eight fp32 values (two runs of four) into MFMA operands.
+__device__ __forceinline__ void split8(const float4 a, const float4 b, bf16x8& hi, bf16x8& lo) {
+    u16x4 h0, l0, h1, l1;
+    split4(a, h0, l0);
+    split4(b, h1, l1);
+    hi = join(h0, h1);
+    lo = join(l0, l1);
+}
+
+// acc + A B for fp32 operands carried as hi + lo bf16 terms; the lo * lo term
+// (about 2^-16 of the others) is dropped.
+__device__ __forceinline__ floatx4 mma3(floatx4 acc, bf16x8 ah, bf16x8 al, bf16x8 bh, bf16x8 bl) {
+    acc = mfma16x16x32(ah, bh, acc);
+    acc = mfma16x16x32(ah, bl, acc);
+    return mfma16x16x32(al, bh, acc);
+}
+
+// Eight fp32 values of one matrix row as an A/B fragment of k-step s: the
+// runs k0 = 32 s + 4 g and k0 + 16; a run at or past `klim` reads as zero.
+__device__ __forceinline__ void frag_f32(const float* row, int s, int g, int klim, float4& a, float4& b) {
+    const int k0 = 32 * s + 4 * g;
+    const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
+    a = (k0 < klim) ? *reinterpret_cast<const float4*>(row + k0) : z;
+    b = (k0 + 16 < klim) ? *reinterpret_cast<const float4*>(row + k0 + 16) : z;
+}
+
+// The value of a float register in lane `src` (a compile-time or uniform
+// index), broadcast to the whole wave through a scalar register.
+__device__ __forceinline__ float readlane_f(float v, int src) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), src));
+}
+
+// Streaming accesses: data read or written exactly once per call (states,
+// outputs).  Outputs go through non-temporal stores, which let HBM mix the
+// write stream with the read stream at less loss; the state reads stay
+// ordinary loads (non-temporal loads measured slower on MI355X for this
+// path).
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float4 ld_stream(const float* p) { return *reinterpret_cast<const float4*>(p); }
+
+__device__ __forceinline__ void st_stream(float* p, const float4 v) {
+    const f32x4 w = {v.x, v.y, v.z, v.w};
+    __builtin_nontemporal_store(w, reinterpret_cast<global_ptr<f32x4>>((global_ptr<float>)p));
 }
 
 // Four bf16 values (8 bytes) from LDS or global memory.

@@ -13,24 +13,32 @@
 // recurrence):
 //   C[n, m] = (P_n / P_m) q_n . k_m        (m = n included)
 //   G[n, m] = beta_n (P_n / P_m) k_n . k_m (m a strict ancestor)
-// G is strictly lower in topological order, so (I + G) U = R is solved by
-// substitution; nodes of equal depth are independent, so the solve runs
-// level by level (at most 8 levels for the draft trees, T for a chain).
+// G is strictly lower in topological order.  X = (I + G)^{-1} and M = C X
+// depend only on Q, K, the gates and the topology; with them U = X R and
+// O = B0 + M R.
 //
 // One workgroup per (sequence, head, value tile of BV columns): G and C do
 // not depend on the value channel (Eq. (7) context), so value tiles are
-// independent.  Per block:
-//   1. issue the loads of its BV x D slice of S0 (fp32) straight into the
-//      registers of the MFMA B operand;
-//   2. stage Q, K (bf16) and the V tile in LDS; wave 0 turns the parent row
-//      into ancestor masks, depths and log P by pointer doubling;
-//   3. Q K^T and K K^T (MFMA), masked and decay-scaled into C and G in LDS;
-//   4. Q S0^T and K S0^T on MFMA, S0 split into bf16 hi + lo terms;
-//   5. B0 and R into LDS, then the level-by-level solve for U and O, with
-//      one wave per node and one lane per value column.
-// P_n / P_m is evaluated as exp(log P_n - log P_m), only for ancestor pairs
-// (so the exponent is <= 0 for gates in [0, 1]); log a is clamped at -87 so
-// that a zero gate gives a finite log.
+// independent.  Each wave owns 16 value rows of the tile.  Per block:
+//   1. issue the loads of q, k, v, the gates and the parent row, then of the
+//      block's S0 rows (fp32) straight into MFMA operand registers; the S0
+//      loads stay in flight through steps 2-4;
+//   2. stage Q, K (bf16) in LDS; wave 0 turns the parent row into ancestor
+//      masks and log P by pointer doubling;
+//   3. 16 x 16 blocks of Q K^T and K K^T on MFMA, masked and decay-scaled
+//      into C and G; the diagonal blocks of X are solved by forward
+//      substitution in registers, reading G from the MFMA accumulators with
+//      readlane;
+//   4. the off-diagonal blocks of X, X_ij = -X_ii sum_k G_ik X_kj (one stage
+//      per block diagonal), then M = C X, on MFMA;
+//   5. S0 Q^T and S0 K^T on MFMA (S0 split into bf16 hi + lo terms) give
+//      B0^T and R^T for the wave's rows;
+//   6. U^T = R^T X^T and O^T = B0^T + R^T M^T on MFMA; each lane then holds
+//      four consecutive values of one node and stores them as a float4.
+// Products with fp32 operands on both sides (X, M, R) carry both as hi + lo
+// bf16 terms (three MFMAs per step).  P_n / P_m is exp(log P_n - log P_m),
+// evaluated only for ancestor pairs (exponent <= 0 for gates in [0, 1]);
+// log a is clamped at -87 so that a zero gate gives a finite log.
 #include "ldv_device.hpp"
 #include "ldv_kernels.hpp"
 
@@ -38,53 +46,56 @@
 
 namespace ldv {
 
-template <int D>
+template <int D, int TM>
 struct VShape {
-    static constexpr int BV = D >= 64 ? 64 : D;  // value columns per block
-    static constexpr int NT = D / BV;            // value tiles per head
-    static constexpr int NW = BV / 16;           // waves per block
-    static constexpr int KS = (D + 31) / 32;     // MFMA k-steps over d_k
-    static constexpr int QKLD = D + 8;           // bf16 row stride of Q/K in LDS
-    static constexpr int BRLD = BV + 4;          // fp32 row stride of B0/R in LDS
+    // a 64-node block keeps the whole head (BV = 128, eight waves) when it
+    // can: its factor work is the largest, so it is done once per head
+    static constexpr int BV = (TM == 64 && D >= 128) ? 128 : (D >= 64 ? 64 : D);
+    static constexpr int NT = D / BV;         // value tiles per head
+    static constexpr int NW = BV / 16;        // waves per block
+    static constexpr int KS = (D + 31) / 32;  // MFMA k-steps over d_k
+    static constexpr int QKLD = D + 8;        // bf16 row stride of Q/K in LDS
+    static constexpr int FLD = TM + 4;        // fp32 row stride of the T x T factors and of R^T
+    static constexpr int NBM = TM / 16;       // 16-node blocks at most
 };
 
 template <int D, int TM, bool F32IN>
 struct VLds {
-    using S = VShape<D>;
-    static constexpr int NPLANE = F32IN ? 4 : 2;  // q, k (hi and lo for fp32 input)
+    using S = VShape<D, TM>;
+    static constexpr int NPLANE = F32IN ? 4 : 2;  // q, k (hi and lo planes for fp32 input)
     static constexpr size_t qk = (size_t)NPLANE * TM * S::QKLD * 2;
-    static constexpr size_t br = (size_t)2 * TM * S::BRLD * 4;
-    static constexpr size_t regionA = ((qk > br ? qk : br) + 15) / 16 * 16;
-    static constexpr size_t gc = (size_t)TM * TM * 8;
-    static constexpr size_t vt = ((size_t)TM * S::BV * (F32IN ? 4 : 2) + 15) / 16 * 16;
-    static constexpr size_t off_gc = regionA;
-    static constexpr size_t off_v = off_gc + gc;
-    static constexpr size_t off_anc = off_v + vt;          // uint64 [TM]
-    static constexpr size_t off_lvl = off_anc + 8 * TM;    // uint64 [TM + 1]
-    static constexpr size_t off_f = off_lvl + 8 * (TM + 8);  // float logp, P, beta [TM] each
-    static constexpr size_t off_i = off_f + 12 * TM;        // int maxdep, bad
+    static constexpr size_t rt = (size_t)S::BV * S::FLD * 4;  // R^T, after Q/K are dead
+    static constexpr size_t regionA = ((qk > rt ? qk : rt) + 15) / 16 * 16;
+    static constexpr size_t fac = (size_t)TM * S::FLD * 4;
+    static constexpr size_t off_g = regionA;    // G, later M
+    static constexpr size_t off_c = off_g + fac;
+    static constexpr size_t off_x = off_c + fac;
+    static constexpr size_t off_anc = off_x + fac;   // uint64 [TM]
+    static constexpr size_t off_f = off_anc + 8 * TM;  // float logp, P, beta [TM] each
+    static constexpr size_t off_i = off_f + 12 * TM;   // int: bad flag
     static constexpr size_t total = off_i + 16;
 };
 
 template <int D, int TM, bool F32IN>
-__global__ __launch_bounds__(VShape<D>::NW * kWave) void verify_kernel(const VerifyArgs p) {
-    using S = VShape<D>;
+__global__ __launch_bounds__((VShape<D, TM>::NW * kWave)) void verify_kernel(const VerifyArgs p) {
+    using S = VShape<D, TM>;
     using L = VLds<D, TM, F32IN>;
-    constexpr int BV = S::BV, NW = S::NW, KS = S::KS, QKLD = S::QKLD, BRLD = S::BRLD;
+    constexpr int BV = S::BV, NW = S::NW, KS = S::KS, QKLD = S::QKLD, FLD = S::FLD, NBM = S::NBM;
     constexpr int NTHR = NW * kWave;
-    constexpr int MBMAX = TM / 16;
+    constexpr int EPC = F32IN ? 4 : 8;                 // elements per 16-byte chunk
+    constexpr int CPR = D / EPC;                       // chunks per q/k row
+    constexpr int QKC = (TM * CPR + NTHR - 1) / NTHR;  // q (and k) chunks per thread
 
     __shared__ __align__(16) unsigned char smem[L::total];
     unsigned short* s_q = reinterpret_cast<unsigned short*>(smem);
     unsigned short* s_k = s_q + TM * QKLD;
     unsigned short* s_qlo = s_k + TM * QKLD;  // fp32 input only
     unsigned short* s_klo = s_qlo + TM * QKLD;
-    float* s_b0 = reinterpret_cast<float*>(smem);  // aliases Q/K after the products
-    float* s_r = s_b0 + TM * BRLD;                 // R, then U in place
-    float2* s_gc = reinterpret_cast<float2*>(smem + L::off_gc);  // (G, C)[n][m]
-    void* s_v = smem + L::off_v;
+    float* s_rt = reinterpret_cast<float*>(smem);  // R^T [BV][FLD], aliases Q/K once they are dead
+    float* s_g = reinterpret_cast<float*>(smem + L::off_g);  // G [TM][FLD], then M
+    float* s_c = reinterpret_cast<float*>(smem + L::off_c);  // C [TM][FLD]
+    float* s_x = reinterpret_cast<float*>(smem + L::off_x);  // X [TM][FLD]
     uint64_t* s_anc = reinterpret_cast<uint64_t*>(smem + L::off_anc);
-    uint64_t* s_lvl = reinterpret_cast<uint64_t*>(smem + L::off_lvl);
     float* s_logp = reinterpret_cast<float*>(smem + L::off_f);
     float* s_P = s_logp + TM;
     float* s_beta = s_P + TM;
@@ -99,70 +110,72 @@ __global__ __launch_bounds__(VShape<D>::NW * kWave) void verify_kernel(const Ver
     const int h = bh % H, b = bh / H;
     const int NB = (T + 15) >> 4;  // 16-node blocks in use
     const int T16 = NB * 16;
+    const int vrow0 = tile * BV + wave * 16;  // first value row (of S0, o, u) of this wave
 
-    // 1. this lane's S0 row (one MFMA B-operand column) for every k-step
-    const int jl = wave * 16 + c;  // column within the value tile
-    const float* s0row = p.S0 + (((size_t)b * H + h) * D + (size_t)tile * BV + jl) * D;
+    // 1. global loads.  Every small per-node input first, so that, loads
+    // completing in issue order, steps 2-4 can run while the S0 rows are in
+    // flight.  The loads are branch-free (indices clamped into range, values
+    // of rows past T dropped later by selects): a load under a branch, or a
+    // register overwritten while its load is pending, would make the
+    // compiler wait for every earlier memory operation.
+    u32x4 qreg[QKC], kreg[QKC];
+#pragma unroll
+    for (int i = 0; i < QKC; ++i) {
+        const int ch = tid + i * NTHR, row = min(ch / CPR, T - 1), col = (ch % CPR) * EPC;
+        const size_t off = ((((size_t)b * T + row) * H + h) * D + col) * (F32IN ? 4 : 2);
+        qreg[i] = *reinterpret_cast<const u32x4*>(static_cast<const char*>(p.q) + off);
+        kreg[i] = *reinterpret_cast<const u32x4*>(static_cast<const char*>(p.k) + off);
+    }
+    // v[n][vrow0 + 4g .. +3] for the node n = 16 nb + c this lane holds in step 5
+    u16x4 vb[NBM];
+    float4 vf[NBM];
+#pragma unroll
+    for (int nb = 0; nb < NBM; ++nb) {
+        const int n = min(nb * 16 + c, T - 1);
+        const size_t off = (((size_t)b * T + n) * H + h) * D + vrow0 + 4 * g;
+        if constexpr (F32IN) vf[nb] = *reinterpret_cast<const float4*>(static_cast<const float*>(p.v) + off);
+        else vb[nb] = load_u16x4(static_cast<const unsigned short*>(p.v) + off);
+    }
+    const int nl = min(lane, T - 1);
+    // a chain has no parent array: read the gate array instead (it has at
+    // least B * T entries) and discard the value
+    const global_ptr<const int32_t> parp =
+        (global_ptr<const int32_t>)(p.parent ? p.parent : reinterpret_cast<const int32_t*>(p.a));
+    const int par_ld = parp[(size_t)b * T + nl];
+    const size_t gi = ((size_t)b * T + nl) * H + h;
+    const float ga = p.a[gi];
+    const float gb = p.beta[gi];
+    // this lane's S0 row (A operand row c of the wave's 16-row block)
+    const float* s0row = p.S0 + (((size_t)b * H + h) * D + vrow0 + c) * D;
     float4 sreg[KS][2];
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
         const int k0 = 32 * s + 4 * g;
-        sreg[s][0] = (k0 < D) ? *reinterpret_cast<const float4*>(s0row + k0) : make_float4(0.f, 0.f, 0.f, 0.f);
-        sreg[s][1] = (k0 + 16 < D) ? *reinterpret_cast<const float4*>(s0row + k0 + 16)
-                                   : make_float4(0.f, 0.f, 0.f, 0.f);
+        sreg[s][0] = (k0 < D) ? ld_stream(s0row + k0) : make_float4(0.f, 0.f, 0.f, 0.f);
+        sreg[s][1] = (k0 + 16 < D) ? ld_stream(s0row + k0 + 16) : make_float4(0.f, 0.f, 0.f, 0.f);
     }
+    asm volatile("" ::: "memory");  // keep the loads above ahead of any use of them
+    const int par = p.parent ? par_ld : lane - 1;
 
     // 2a. Q, K rows into LDS (rows T .. T16-1 zero)
-    if constexpr (!F32IN) {
-        constexpr int CPR = D / 8;  // 16-byte chunks per row
-        const unsigned short* qg = static_cast<const unsigned short*>(p.q);
-        const unsigned short* kg = static_cast<const unsigned short*>(p.k);
-        for (int ch = tid; ch < T16 * CPR; ch += NTHR) {
-            const int row = ch / CPR, col = (ch % CPR) * 8;
-            uint4 qv = make_uint4(0, 0, 0, 0), kv = qv;
-            if (row < T) {
-                const size_t off = (((size_t)b * T + row) * H + h) * D + col;
-                qv = *reinterpret_cast<const uint4*>(qg + off);
-                kv = *reinterpret_cast<const uint4*>(kg + off);
+#pragma unroll
+    for (int i = 0; i < QKC; ++i) {
+        const int ch = tid + i * NTHR, row = ch / CPR, col = (ch % CPR) * EPC;
+        if (row < T16) {
+            const u32x4 z = {0u, 0u, 0u, 0u};
+            const u32x4 qv = row < T ? qreg[i] : z, kv = row < T ? kreg[i] : z;
+            if constexpr (!F32IN) {
+                *reinterpret_cast<u32x4*>(s_q + row * QKLD + col) = qv;
+                *reinterpret_cast<u32x4*>(s_k + row * QKLD + col) = kv;
+            } else {
+                u16x4 hi, lo;
+                split4(__builtin_bit_cast(float4, qv), hi, lo);
+                *reinterpret_cast<u16x4*>(s_q + row * QKLD + col) = hi;
+                *reinterpret_cast<u16x4*>(s_qlo + row * QKLD + col) = lo;
+                split4(__builtin_bit_cast(float4, kv), hi, lo);
+                *reinterpret_cast<u16x4*>(s_k + row * QKLD + col) = hi;
+                *reinterpret_cast<u16x4*>(s_klo + row * QKLD + col) = lo;
             }
-            *reinterpret_cast<uint4*>(s_q + row * QKLD + col) = qv;
-            *reinterpret_cast<uint4*>(s_k + row * QKLD + col) = kv;
-        }
-        constexpr int VPR = BV / 8;
-        const unsigned short* vg = static_cast<const unsigned short*>(p.v);
-        unsigned short* sv = static_cast<unsigned short*>(s_v);
-        for (int ch = tid; ch < T * VPR; ch += NTHR) {
-            const int row = ch / VPR, col = (ch % VPR) * 8;
-            const size_t off = (((size_t)b * T + row) * H + h) * D + (size_t)tile * BV + col;
-            *reinterpret_cast<uint4*>(sv + row * BV + col) = *reinterpret_cast<const uint4*>(vg + off);
-        }
-    } else {
-        constexpr int CPR = D / 4;
-        const float* qg = static_cast<const float*>(p.q);
-        const float* kg = static_cast<const float*>(p.k);
-        for (int ch = tid; ch < T16 * CPR; ch += NTHR) {
-            const int row = ch / CPR, col = (ch % CPR) * 4;
-            float4 qv = make_float4(0.f, 0.f, 0.f, 0.f), kv = qv;
-            if (row < T) {
-                const size_t off = (((size_t)b * T + row) * H + h) * D + col;
-                qv = *reinterpret_cast<const float4*>(qg + off);
-                kv = *reinterpret_cast<const float4*>(kg + off);
-            }
-            u16x4 hi, lo;
-            split4(qv, hi, lo);
-            *reinterpret_cast<u16x4*>(s_q + row * QKLD + col) = hi;
-            *reinterpret_cast<u16x4*>(s_qlo + row * QKLD + col) = lo;
-            split4(kv, hi, lo);
-            *reinterpret_cast<u16x4*>(s_k + row * QKLD + col) = hi;
-            *reinterpret_cast<u16x4*>(s_klo + row * QKLD + col) = lo;
-        }
-        constexpr int VPR = BV / 4;
-        const float* vg = static_cast<const float*>(p.v);
-        float* sv = static_cast<float*>(s_v);
-        for (int ch = tid; ch < T * VPR; ch += NTHR) {
-            const int row = ch / VPR, col = (ch % VPR) * 4;
-            const size_t off = (((size_t)b * T + row) * H + h) * D + (size_t)tile * BV + col;
-            *reinterpret_cast<float4*>(sv + row * BV + col) = *reinterpret_cast<const float4*>(vg + off);
         }
     }
 
@@ -170,33 +183,23 @@ __global__ __launch_bounds__(VShape<D>::NW * kWave) void verify_kernel(const Ver
     if (wave == 0) {
         const int n = lane;
         const bool valid = n < T;
-        int par = -1;
-        float la = 0.f, be = 0.f;
-        if (valid) {
-            par = p.parent ? p.parent[(size_t)b * T + n] : n - 1;
-            const size_t gi = ((size_t)b * T + n) * H + h;
-            la = fmaxf(logf(p.a[gi]), -87.f);
-            be = p.beta[gi];
-        }
         const bool bad = valid && (par < -1 || par >= n);
         const uint64_t badm = __ballot(bad);
-        // pointer doubling: (set, ls, dep) summarise the path segment from n
-        // up to (not including) jmp
+        const float la = valid ? fmaxf(logf(ga), -87.f) : 0.f;
+        // pointer doubling: (set, ls) summarise the path segment from n up to
+        // (not including) jmp
         uint64_t set = valid ? (1ull << n) : 0ull;
         int jmp = (valid && !bad) ? par : -1;
         float ls = la;
-        int dep = valid ? 1 : 0;
 #pragma unroll
         for (int it = 0; it < 6; ++it) {
             const int src = jmp >= 0 ? jmp : n;
             const uint64_t set_j = shfl_u64(set, src);
             const float ls_j = __shfl(ls, src, kWave);
-            const int dep_j = __shfl(dep, src, kWave);
             const int jmp_j = __shfl(jmp, src, kWave);
             if (jmp >= 0) {
                 set |= set_j;
                 ls += ls_j;
-                dep += dep_j;
                 jmp = jmp_j;
             }
         }
@@ -204,162 +207,275 @@ __global__ __launch_bounds__(VShape<D>::NW * kWave) void verify_kernel(const Ver
             s_anc[n] = valid ? (set & ~(1ull << n)) : 0ull;
             s_logp[n] = ls;
             s_P[n] = valid ? expf(ls) : 0.f;
-            s_beta[n] = be;
-        }
-        const int maxdep = wave_max_i(dep);
-        for (int lv = 1; lv <= maxdep; ++lv) {
-            const uint64_t m = __ballot(valid && dep == lv);
-            if (lane == 0) s_lvl[lv] = m;
+            s_beta[n] = valid ? gb : 0.f;
         }
         if (lane == 0) {
-            s_int[0] = maxdep;
-            s_int[1] = badm != 0ull;
+            s_int[0] = badm != 0ull;
             if (badm != 0ull && p.status && h == 0 && tile == 0) atomicOr(p.status, LDV_STATUS_BAD_PARENT);
         }
         if (badm == 0ull && valid && tile == 0 && p.logp_out) p.logp_out[((size_t)b * T + n) * H + h] = ls;
     }
     __syncthreads();
-    if (s_int[1]) return;  // invalid parent row: nothing is written
+    if (s_int[0]) return;  // invalid parent row: nothing is written
 
-    // 3. C and G: lower-triangular 16x16 blocks of Q K^T and K K^T
-    {
-        const int npairs = NB * (NB + 1) / 2;
-        for (int it = wave; it < 2 * npairs; it += NW) {
-            const int kind = it & 1;  // 0: Q K^T -> C, 1: K K^T -> G
-            const int pr = it >> 1;
-            int mb = 0;
-            while ((mb + 1) * (mb + 2) / 2 <= pr) ++mb;
-            const int nb = pr - mb * (mb + 1) / 2;
-            const unsigned short* arow = (kind ? s_k : s_q) + (mb * 16 + c) * QKLD;
-            const unsigned short* brow = s_k + (nb * 16 + c) * QKLD;
-            floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int s = 0; s < KS; ++s) {
-                const bf16x8 af = frag_row<D>(arow, s, g);
-                const bf16x8 bfr = frag_row<D>(brow, s, g);
-                acc = mfma16x16x32(af, bfr, acc);
-                if constexpr (F32IN) {
-                    const unsigned short* arow_lo = (kind ? s_klo : s_qlo) + (mb * 16 + c) * QKLD;
-                    const unsigned short* brow_lo = s_klo + (nb * 16 + c) * QKLD;
-                    acc = mfma16x16x32(af, frag_row<D>(brow_lo, s, g), acc);
-                    acc = mfma16x16x32(frag_row<D>(arow_lo, s, g), bfr, acc);
-                }
-            }
-            const int m = nb * 16 + c;
+    // 3. C and G blocks (mb, nb), nb <= mb, from Q K^T and K K^T; zero above
+    //    the block diagonal.  Items 0 .. NB-1 are the diagonal blocks: block
+    //    (i, i) goes to wave i % NW, which also solves the diagonal block of
+    //    X from its G registers.
+    for (int it = wave; it < NB * NB; it += NW) {
+        int mb, nb;
+        if (it < NB) {
+            mb = nb = it;
+        } else {
+            const int r = it - NB;  // ordered pairs mb != nb
+            mb = r / (NB - 1);
+            nb = r % (NB - 1);
+            if (nb >= mb) ++nb;
+        }
+        if (nb > mb) {  // above the diagonal: zero G (later M), C and X
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int n = mb * 16 + 4 * g + r;
-                float val = 0.f;
-                if (n < T && m < T) {
-                    const uint64_t anc = s_anc[n];
-                    if (kind == 0) {
-                        if (((anc | (1ull << n)) >> m) & 1ull) val = expf(s_logp[n] - s_logp[m]) * acc[r];
-                    } else {
-                        if ((anc >> m) & 1ull) val = s_beta[n] * expf(s_logp[n] - s_logp[m]) * acc[r];
-                    }
-                }
-                float* cell = reinterpret_cast<float*>(s_gc + n * TM + m);
-                cell[kind ? 0 : 1] = val;
+                const int n = mb * 16 + 4 * g + r, m = nb * 16 + c;
+                s_g[n * FLD + m] = 0.f;
+                s_c[n * FLD + m] = 0.f;
+                s_x[n * FLD + m] = 0.f;
+            }
+            continue;
+        }
+        floatx4 acc_c = {0.f, 0.f, 0.f, 0.f}, acc_g = acc_c;
+        const unsigned short* qrow = s_q + (mb * 16 + c) * QKLD;
+        const unsigned short* krow_a = s_k + (mb * 16 + c) * QKLD;
+        const unsigned short* krow_b = s_k + (nb * 16 + c) * QKLD;
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            const bf16x8 bk = frag_row<D>(krow_b, s, g);
+            const bf16x8 aq = frag_row<D>(qrow, s, g);
+            const bf16x8 ak = frag_row<D>(krow_a, s, g);
+            acc_c = mfma16x16x32(aq, bk, acc_c);
+            acc_g = mfma16x16x32(ak, bk, acc_g);
+            if constexpr (F32IN) {
+                const bf16x8 bkl = frag_row<D>(s_klo + (nb * 16 + c) * QKLD, s, g);
+                acc_c = mfma16x16x32(aq, bkl, acc_c);
+                acc_c = mfma16x16x32(frag_row<D>(s_qlo + (mb * 16 + c) * QKLD, s, g), bk, acc_c);
+                acc_g = mfma16x16x32(ak, bkl, acc_g);
+                acc_g = mfma16x16x32(frag_row<D>(s_klo + (mb * 16 + c) * QKLD, s, g), bk, acc_g);
             }
         }
-    }
-
-    // 4. state products Q S0^T and K S0^T for this wave's 16 value columns
-    floatx4 accq[MBMAX], acck[MBMAX];
-#pragma unroll
-    for (int mb = 0; mb < MBMAX; ++mb) {
-        accq[mb] = floatx4{0.f, 0.f, 0.f, 0.f};
-        acck[mb] = floatx4{0.f, 0.f, 0.f, 0.f};
-    }
-#pragma unroll
-    for (int s = 0; s < KS; ++s) {
-        u16x4 h0, l0, h1, l1;
-        split4(sreg[s][0], h0, l0);
-        split4(sreg[s][1], h1, l1);
-        const bf16x8 bh = join(h0, h1), bl = join(l0, l1);
-#pragma unroll
-        for (int mb = 0; mb < MBMAX; ++mb) {
-            if (mb < NB) {
-                const bf16x8 aq = frag_row<D>(s_q + (mb * 16 + c) * QKLD, s, g);
-                const bf16x8 ak = frag_row<D>(s_k + (mb * 16 + c) * QKLD, s, g);
-                accq[mb] = mfma16x16x32(aq, bh, accq[mb]);
-                accq[mb] = mfma16x16x32(aq, bl, accq[mb]);
-                acck[mb] = mfma16x16x32(ak, bh, acck[mb]);
-                acck[mb] = mfma16x16x32(ak, bl, acck[mb]);
-                if constexpr (F32IN) {
-                    accq[mb] = mfma16x16x32(frag_row<D>(s_qlo + (mb * 16 + c) * QKLD, s, g), bh, accq[mb]);
-                    acck[mb] = mfma16x16x32(frag_row<D>(s_klo + (mb * 16 + c) * QKLD, s, g), bh, acck[mb]);
-                }
-            }
-        }
-    }
-    // B0 = P (Q S0^T), R = beta (v - P (K S0^T)) at (node, column jl)
-    float b0v[MBMAX][4], rv[MBMAX][4];
-#pragma unroll
-    for (int mb = 0; mb < MBMAX; ++mb) {
+        // lane (c, g) holds rows n = 16 mb + 4 g + r, column m = 16 nb + c
+        const int m = nb * 16 + c;
+        const float lpm = s_logp[m];
+        float gv[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int n = mb * 16 + 4 * g + r;
-            b0v[mb][r] = 0.f;
-            rv[mb][r] = 0.f;
-            if (mb < NB && n < T) {
-                float vv;
-                if constexpr (F32IN) vv = static_cast<const float*>(s_v)[n * BV + jl];
-                else vv = bf16_val(static_cast<const unsigned short*>(s_v)[n * BV + jl]);
-                const float P = s_P[n];
-                b0v[mb][r] = P * accq[mb][r];
-                rv[mb][r] = s_beta[n] * (vv - P * acck[mb][r]);
-            }
+            const uint64_t anc = s_anc[n];
+            const bool on_path = m < T && n < T && (((anc | (1ull << n)) >> m) & 1ull);
+            const bool strict = on_path && m != n;
+            const float dec = on_path ? expf(s_logp[n] - lpm) : 0.f;
+            gv[r] = strict ? s_beta[n] * dec * acc_g[r] : 0.f;
+            s_c[n * FLD + m] = dec * acc_c[r];
+            s_g[n * FLD + m] = gv[r];
         }
-    }
-    __syncthreads();  // Q/K no longer read; C and G complete
+        if (mb == nb) {
+            // X_ii = (I + G_ii)^{-1}: lane j < 16 solves column j,
+            //   x[r] = [r == j] - sum_{t < r} G[r][t] x[t],
+            // with G[r][t] read from lane t + 16 (r / 4), register r % 4
+            float x[16];
 #pragma unroll
-    for (int mb = 0; mb < MBMAX; ++mb) {
+            for (int r = 0; r < 16; ++r) {
+                float acc = (r == c) ? 1.f : 0.f;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int n = mb * 16 + 4 * g + r;
-            if (mb < NB && n < T) {
-                s_b0[n * BRLD + jl] = b0v[mb][r];
-                s_r[n * BRLD + jl] = rv[mb][r];
+                for (int t = 0; t < r; ++t) acc -= readlane_f(gv[r & 3], t + 16 * (r >> 2)) * x[t];
+                x[r] = acc;
+            }
+            if (g == 0) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) s_x[(mb * 16 + r) * FLD + mb * 16 + c] = x[r];
             }
         }
     }
     __syncthreads();
 
-    // 5. (I + G) U = R and O = B0 + C U, level by level
-    const int maxdep = s_int[0];
-    for (int lv = 1; lv <= maxdep; ++lv) {
-        const uint64_t lvm = s_lvl[lv];
-        const int cnt = __builtin_popcountll(lvm);
-        for (int it = wave; it < cnt; it += NW) {
-            const int n = nth_set_bit(lvm, it);
-            if (lane < BV) {
-                const int j = lane;
-                float u = s_r[n * BRLD + j];
-                float o = s_b0[n * BRLD + j];
-                uint64_t an = s_anc[n];
-                while (an) {
-                    const int m = __builtin_ctzll(an);
-                    an &= an - 1;
-                    const float2 gc = s_gc[n * TM + m];
-                    const float um = s_r[m * BRLD + j];
-                    u -= gc.x * um;
-                    o += gc.y * um;
-                }
-                o += s_gc[n * TM + n].y * u;
-                s_r[n * BRLD + j] = u;
-                const size_t off = (((size_t)b * T + n) * H + h) * D + (size_t)tile * BV + j;
-                p.o[off] = o;
-                if (p.u_out) p.u_out[off] = u;
+    // 4a. off-diagonal blocks of X, one block diagonal d = i - j per stage:
+    //     X_ij = -X_ii S, S = sum_{k=j}^{i-1} G_ik X_kj
+    for (int d = 1; d < NB; ++d) {
+        for (int it = wave; it < NB - d; it += NW) {
+            const int j = it, i = it + d;
+            const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
+            floatx4 sacc = {0.f, 0.f, 0.f, 0.f};
+            const float* grow = s_g + (16 * i + c) * FLD;
+            const float* xcol = s_x + 16 * j + c;
+            // k-steps of 32 nodes over [16 j, 16 i); runs outside read as zero
+            for (int s = j / 2; 32 * s < 16 * i; ++s) {
+                const int k0 = 32 * s + 4 * g;
+                const bool v0 = k0 >= 16 * j && k0 < 16 * i;
+                const bool v1 = k0 + 16 >= 16 * j && k0 + 16 < 16 * i;
+                const float4 a0 = v0 ? *reinterpret_cast<const float4*>(grow + k0) : z;
+                const float4 a1 = v1 ? *reinterpret_cast<const float4*>(grow + k0 + 16) : z;
+                // B[k][n] = X[k][16 j + n]: four rows down one column
+                const float4 b0 = v0 ? make_float4(xcol[(k0 + 0) * FLD], xcol[(k0 + 1) * FLD], xcol[(k0 + 2) * FLD],
+                                                   xcol[(k0 + 3) * FLD])
+                                     : z;
+                const float4 b1 = v1 ? make_float4(xcol[(k0 + 16) * FLD], xcol[(k0 + 17) * FLD],
+                                                   xcol[(k0 + 18) * FLD], xcol[(k0 + 19) * FLD])
+                                     : z;
+                bf16x8 ah, al, bh, bl;
+                split8(a0, a1, ah, al);
+                split8(b0, b1, bh, bl);
+                sacc = mma3(sacc, ah, al, bh, bl);
             }
+            // S in C layout (lane (c, g): rows 4 g .. 4 g + 3 of column c) is
+            // already the B operand of a 16-deep product
+            bf16x8 sh, sl, ah, al;
+            split8(make_float4(sacc[0], sacc[1], sacc[2], sacc[3]), z, sh, sl);
+            split8(*reinterpret_cast<const float4*>(s_x + (16 * i + c) * FLD + 16 * i + 4 * g), z, ah, al);
+            floatx4 xacc = {0.f, 0.f, 0.f, 0.f};
+            xacc = mma3(xacc, ah, al, sh, sl);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) s_x[(16 * i + 4 * g + r) * FLD + 16 * j + c] = -xacc[r];
         }
         __syncthreads();
+    }
+
+    // 4b. M = C X on the blocks (i, j), j <= i, into the G area
+    //     (M_ij = sum_{k=j}^{i} C_ik X_kj; every X block is final, so G is
+    //     no longer read)
+    for (int it = wave; it < NB * (NB + 1) / 2; it += NW) {
+        int i = 0;
+        while ((i + 1) * (i + 2) / 2 <= it) ++i;
+        const int j = it - i * (i + 1) / 2;
+        const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
+        floatx4 macc = {0.f, 0.f, 0.f, 0.f};
+        const float* crow = s_c + (16 * i + c) * FLD;
+        const float* xcol = s_x + 16 * j + c;
+        for (int s = j / 2; 32 * s < 16 * (i + 1); ++s) {
+            const int k0 = 32 * s + 4 * g;
+            const bool v0 = k0 >= 16 * j && k0 < 16 * (i + 1);
+            const bool v1 = k0 + 16 >= 16 * j && k0 + 16 < 16 * (i + 1);
+            const float4 a0 = v0 ? *reinterpret_cast<const float4*>(crow + k0) : z;
+            const float4 a1 = v1 ? *reinterpret_cast<const float4*>(crow + k0 + 16) : z;
+            const float4 b0 = v0 ? make_float4(xcol[(k0 + 0) * FLD], xcol[(k0 + 1) * FLD], xcol[(k0 + 2) * FLD],
+                                               xcol[(k0 + 3) * FLD])
+                                 : z;
+            const float4 b1 = v1 ? make_float4(xcol[(k0 + 16) * FLD], xcol[(k0 + 17) * FLD],
+                                               xcol[(k0 + 18) * FLD], xcol[(k0 + 19) * FLD])
+                                 : z;
+            bf16x8 ah, al, bh, bl;
+            split8(a0, a1, ah, al);
+            split8(b0, b1, bh, bl);
+            macc = mma3(macc, ah, al, bh, bl);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) s_g[(16 * i + 4 * g + r) * FLD + 16 * j + c] = macc[r];
+    }
+
+    // 5. S0 Q^T and S0 K^T for the wave's 16 value rows (A = S0 rows, split
+    //    hi + lo; B = Q / K rows).  Lane (c, g) ends with value rows 4 g + r
+    //    and node n = 16 nb + c of each node block.
+    floatx4 accq[NBM], acck[NBM];
+#pragma unroll
+    for (int nb = 0; nb < NBM; ++nb) {
+        accq[nb] = floatx4{0.f, 0.f, 0.f, 0.f};
+        acck[nb] = floatx4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+        bf16x8 sh, sl;
+        split8(sreg[s][0], sreg[s][1], sh, sl);
+#pragma unroll
+        for (int nb = 0; nb < NBM; ++nb) {
+            if (nb < NB) {
+                const bf16x8 bq = frag_row<D>(s_q + (nb * 16 + c) * QKLD, s, g);
+                const bf16x8 bk = frag_row<D>(s_k + (nb * 16 + c) * QKLD, s, g);
+                accq[nb] = mfma16x16x32(sh, bq, accq[nb]);
+                accq[nb] = mfma16x16x32(sl, bq, accq[nb]);
+                acck[nb] = mfma16x16x32(sh, bk, acck[nb]);
+                acck[nb] = mfma16x16x32(sl, bk, acck[nb]);
+                if constexpr (F32IN) {
+                    accq[nb] = mfma16x16x32(sh, frag_row<D>(s_qlo + (nb * 16 + c) * QKLD, s, g), accq[nb]);
+                    acck[nb] = mfma16x16x32(sh, frag_row<D>(s_klo + (nb * 16 + c) * QKLD, s, g), acck[nb]);
+                }
+            }
+        }
+    }
+    // B0^T[i][n] = P_n (S0 q_n)[i];  R^T[i][n] = beta_n (v_n[i] - P_n (S0 k_n)[i])
+    floatx4 b0t[NBM];
+    float rtv[NBM][4];
+#pragma unroll
+    for (int nb = 0; nb < NBM; ++nb) {
+        const int n = nb * 16 + c;
+        const bool nv = nb < NB && n < T;
+        const float P = nv ? s_P[n] : 0.f, be = nv ? s_beta[n] : 0.f;
+        float vv[4];
+        if constexpr (F32IN) {
+            vv[0] = vf[nb].x;
+            vv[1] = vf[nb].y;
+            vv[2] = vf[nb].z;
+            vv[3] = vf[nb].w;
+        } else {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) vv[r] = bf16_val(vb[nb][r]);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            b0t[nb][r] = P * accq[nb][r];
+            rtv[nb][r] = nv ? be * (vv[r] - P * acck[nb][r]) : 0.f;
+        }
+    }
+    __syncthreads();  // Q/K dead in every wave; X and M complete
+#pragma unroll
+    for (int nb = 0; nb < NBM; ++nb) {
+        if (nb < NB) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) s_rt[(wave * 16 + 4 * g + r) * FLD + nb * 16 + c] = rtv[nb][r];
+        }
+    }
+    // the wave reads back only the R^T rows it wrote (LDS keeps one wave's
+    // operations in order)
+
+    // 6. U^T = R^T X^T and O^T = B0^T + R^T M^T (K = nodes, 32 per step)
+    const int ksteps = (T16 + 31) / 32;
+    const float* rrow = s_rt + (wave * 16 + c) * FLD;
+    floatx4 accu[NBM], acco[NBM];
+#pragma unroll
+    for (int nb = 0; nb < NBM; ++nb) {
+        accu[nb] = floatx4{0.f, 0.f, 0.f, 0.f};
+        acco[nb] = b0t[nb];
+    }
+    for (int s = 0; s < ksteps; ++s) {
+        float4 a0, a1;
+        frag_f32(rrow, s, g, T16, a0, a1);
+        bf16x8 rh, rl;
+        split8(a0, a1, rh, rl);
+#pragma unroll
+        for (int nb = 0; nb < NBM; ++nb) {
+            if (nb < NB) {
+                float4 x0, x1, m0, m1;
+                frag_f32(s_x + (nb * 16 + c) * FLD, s, g, T16, x0, x1);
+                frag_f32(s_g + (nb * 16 + c) * FLD, s, g, T16, m0, m1);
+                bf16x8 xh, xl, mh, ml;
+                split8(x0, x1, xh, xl);
+                split8(m0, m1, mh, ml);
+                accu[nb] = mma3(accu[nb], rh, rl, xh, xl);
+                acco[nb] = mma3(acco[nb], rh, rl, mh, ml);
+            }
+        }
+    }
+    // lane (c, g): node n = 16 nb + c, value rows vrow0 + 4 g .. +3
+#pragma unroll
+    for (int nb = 0; nb < NBM; ++nb) {
+        const int n = nb * 16 + c;
+        if (nb < NB && n < T) {
+            const size_t off = (((size_t)b * T + n) * H + h) * D + vrow0 + 4 * g;
+            st_stream(p.o + off, make_float4(acco[nb][0], acco[nb][1], acco[nb][2], acco[nb][3]));
+            if (p.u_out) st_stream(p.u_out + off, make_float4(accu[nb][0], accu[nb][1], accu[nb][2], accu[nb][3]));
+        }
     }
 }
 
 template <int D, int TM, bool F32IN>
 static hipError_t launch_t(const VerifyArgs& a, hipStream_t st) {
-    using S = VShape<D>;
+    using S = VShape<D, TM>;
     const long long nblk = (long long)a.B * a.H * S::NT;
     if (nblk <= 0) return hipSuccess;
     hipLaunchKernelGGL((verify_kernel<D, TM, F32IN>), dim3((unsigned)nblk), dim3(S::NW * kWave), 0, st, a);
