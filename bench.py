@@ -4,8 +4,9 @@ One step = ldv_verify_chain / ldv_verify_tree over every draft node of the
 batch, ldv_commit_state of the accepted node (in place), and, for workloads
 with drafter reads, ldv_gather_states (o = S q for every query) - one pass of
 the whole path over one batch of seeded synthetic inputs already resident in
-HBM.  Each kernel is bracketed by HIP events on the stream it runs on, inside
-the timed region, so the per-kernel durations come from the same run.
+HBM.  Each kernel is bracketed by HIP events (created without the
+system-scope fence) on the stream it runs on, inside the timed region, so
+the per-kernel durations come from the same run.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu]
 
@@ -82,6 +83,46 @@ def cpu_baseline(wl, x, seconds_min=10.0, seconds_cap=30.0):
                       "path walk, the accepted node committed%s), %.1f s" % (
                           done, wl.B, wl.H, ", 4 positions x 16 queries read per sequence" if wl.P else "",
                           t_total)}
+
+
+class HipEvents:
+    """HIP events recorded on a given stream, created without the system-scope
+    fence that a default event record adds (the fence flushes caches and
+    stretches the gaps between the kernels being timed)."""
+
+    DISABLE_SYSTEM_FENCE = 0x20000000  # hipEventDisableSystemFence
+
+    def __init__(self):
+        import ctypes
+        self.ct = ctypes
+        self.lib = ctypes.CDLL("libamdhip64.so")
+        vp = ctypes.c_void_p
+        self.lib.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(vp), ctypes.c_uint]
+        self.lib.hipEventRecord.argtypes = [vp, vp]
+        self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), vp, vp]
+        self.lib.hipEventDestroy.argtypes = [vp]
+
+    def create(self):
+        e = self.ct.c_void_p()
+        rc = self.lib.hipEventCreateWithFlags(self.ct.byref(e), self.DISABLE_SYSTEM_FENCE)
+        if rc != 0:
+            raise RuntimeError("hipEventCreateWithFlags failed: %d" % rc)
+        return e
+
+    def record(self, e, stream_handle):
+        rc = self.lib.hipEventRecord(e, self.ct.c_void_p(stream_handle))
+        if rc != 0:
+            raise RuntimeError("hipEventRecord failed: %d" % rc)
+
+    def elapsed_s(self, a, b):
+        f = self.ct.c_float()
+        rc = self.lib.hipEventElapsedTime(self.ct.byref(f), a, b)
+        if rc != 0:
+            raise RuntimeError("hipEventElapsedTime failed: %d" % rc)
+        return f.value * 1e-3
+
+    def destroy(self, e):
+        self.lib.hipEventDestroy(e)
 
 
 def traffic_from_profiles(kernel_name, src_files):
@@ -163,11 +204,13 @@ def main():
         go = torch.empty((wl.B, wl.P, wl.H, wl.Qn, wl.D), device="cuda")
     status = torch.zeros(1, dtype=torch.int32, device="cuda")
     stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream  # the stream the library launches on
+    hev = HipEvents()
 
     def step(i, ev=None):
         s = sets[i % NSETS]
         if ev is not None:
-            ev[0].record(stream)
+            hev.record(ev[0], sh)
         if chain:
             ldv.verify_chain(s["q"], s["k"], s["v"], s["a"], s["beta"], s["S0"], o=s["o"], u=s["u"],
                              logp=s["logp"], status=status)
@@ -175,15 +218,15 @@ def main():
             ldv.verify_tree(s["q"], s["k"], s["v"], s["a"], s["beta"], s["S0"], s["parent"], o=s["o"],
                             u=s["u"], logp=s["logp"], status=status)
         if ev is not None:
-            ev[1].record(stream)
+            hev.record(ev[1], sh)
         ldv.commit_state(s["k"], s["u"], s["logp"], s["acc"], s["S0"], S_out=s["S0"],
                          parent=None if chain else s["parent"], status=status)
         if ev is not None:
-            ev[2].record(stream)
+            hev.record(ev[2], sh)
         if wl.P > 0:
             ldv.gather_states(pool, slot, queries, o=go, status=status)
         if ev is not None:
-            ev[3].record(stream)
+            hev.record(ev[3], sh)
 
     for i in range(args.warmup):
         step(i)
@@ -191,17 +234,19 @@ def main():
     assert int(status.item()) == 0, "device status %d" % int(status.item())
 
     K = args.steps
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    evs = [[hev.create() for _ in range(4)] for _ in range(K)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(K):
         step(i, evs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    t_ver = np.array([evs[i][0].elapsed_time(evs[i][1]) for i in range(K)]) * 1e-3
-    t_com = np.array([evs[i][1].elapsed_time(evs[i][2]) for i in range(K)]) * 1e-3
-    t_gat = np.array([evs[i][2].elapsed_time(evs[i][3]) for i in range(K)]) * 1e-3
-    t_total = evs[0][0].elapsed_time(evs[K - 1][3]) * 1e-3
+    t_ver = np.array([hev.elapsed_s(evs[i][0], evs[i][1]) for i in range(K)])
+    t_com = np.array([hev.elapsed_s(evs[i][1], evs[i][2]) for i in range(K)])
+    t_gat = np.array([hev.elapsed_s(evs[i][2], evs[i][3]) for i in range(K)])
+    t_total = hev.elapsed_s(evs[0][0], evs[K - 1][3])
+    for e in (e for row in evs for e in row):
+        hev.destroy(e)
     ms_per_step = t_total / K * 1e3
     nodes = wl.B * wl.H * wl.T
     value = nodes * K / t_total
