@@ -24,14 +24,14 @@ namespace ldv {
 template <int D>
 struct GShape {
     static constexpr int MBT = D / 16;             // 16-row blocks per state
-    static constexpr int NWA = MBT < 4 ? MBT : 4;  // waves holding rows (one 16-row block each)
-    static constexpr int NSPLIT = MBT / NWA;       // blocks per (sequence, position, head)
-    static constexpr int MBW = 1;                  // row blocks per wave
+    static constexpr int NWA = MBT < 4 ? MBT : 4;  // waves per block
+    static constexpr int MBW = 1;                  // 16-row blocks per wave
+    static constexpr int NSPLIT = MBT / (NWA * MBW);  // blocks per (sequence, position, head)
     static constexpr int KS = (D + 31) / 32;       // MFMA k-steps
 };
 
 template <int D, bool F32Q>
-__global__ __launch_bounds__(256) void gather_kernel(const GatherArgs p) {
+__global__ __launch_bounds__((GShape<D>::NWA * kWave)) void gather_kernel(const GatherArgs p) {
     using S = GShape<D>;
     constexpr int NWA = S::NWA, MBW = S::MBW, KS = S::KS;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -47,7 +47,6 @@ __global__ __launch_bounds__(256) void gather_kernel(const GatherArgs p) {
         if (tid == 0 && p.status && h == 0 && part == 0) atomicOr(p.status, LDV_STATUS_BAD_SLOT);
         return;
     }
-    if (wave >= NWA) return;
     const float* src = p.pool + ((size_t)s * H + h) * D * D;
     const bool reads = p.queries && p.o && p.Qn > 0;
     const size_t qo_base = ((size_t)bp * H + h) * (size_t)p.Qn;
@@ -163,7 +162,7 @@ template <int D, bool F32Q>
 static hipError_t launch_t(const GatherArgs& a, hipStream_t st) {
     const long long nblk = (long long)a.B * a.P * a.H * GShape<D>::NSPLIT;
     if (nblk <= 0) return hipSuccess;
-    hipLaunchKernelGGL((gather_kernel<D, F32Q>), dim3((unsigned)nblk), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((gather_kernel<D, F32Q>), dim3((unsigned)nblk), dim3(GShape<D>::NWA * kWave), 0, st, a);
     return hipGetLastError();
 }
 
