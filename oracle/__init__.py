@@ -21,7 +21,8 @@ import numpy as np
 from . import build as _build
 
 __all__ = ["Oracle", "default", "verify", "commit", "chain_decode", "verify_dfs",
-           "gather", "BAD_PARENT", "BAD_ACCEPTED", "BAD_SLOT"]
+           "gather", "read_states", "select", "BAD_PARENT", "BAD_ACCEPTED", "BAD_SLOT",
+           "BAD_POSITION"]
 
 _f32p = ctypes.POINTER(ctypes.c_float)
 _f64p = ctypes.POINTER(ctypes.c_double)
@@ -30,6 +31,7 @@ _i32p = ctypes.POINTER(ctypes.c_int32)
 BAD_PARENT = 1
 BAD_ACCEPTED = 2
 BAD_SLOT = 4
+BAD_POSITION = 8
 
 
 def _threads(n):
@@ -63,8 +65,12 @@ class Oracle:
         lib.oracle_verify_dfs.argtypes = [i, i, i, i, i, _f32p, _f32p, _f32p, _f32p, _f32p,
                                           _f32p, _i32p, _f64p, i]
         lib.oracle_gather.argtypes = [i, i, i, i, i, i, i, _f32p, _i32p, _f32p, _f64p, _f32p, i]
+        lib.oracle_read_states.argtypes = [i, i, i, i, i, i, i, _f32p, _f32p, _f32p, _f32p, _f32p,
+                                           _i32p, _i32p, _f32p, _f64p, i]
+        lib.oracle_select.argtypes = [i, i, ctypes.c_long, _f32p, _i32p, _i32p, _i32p, _i32p,
+                                      _i32p, _i32p, i]
         for f in ("oracle_verify", "oracle_commit", "oracle_chain_decode",
-                  "oracle_verify_dfs", "oracle_gather"):
+                  "oracle_verify_dfs", "oracle_gather", "oracle_read_states", "oracle_select"):
             getattr(lib, f).restype = ctypes.c_int
         self.lib = lib
         self.path = path
@@ -143,6 +149,41 @@ class Oracle:
                                         _p(st, _f32p), _threads(nthreads))
         return o, st, status
 
+    def read_states(self, k, v, a, beta, S0, pos, queries, parent=None, nthreads=None):
+        """Reads of in-block states: o[b, p, h, i] = S_{pos[b, p]} q (S0 for
+        position -1).  Returns (o fp64 [B, P, H, Qn, dv], status)."""
+        k, v, a, beta, S0, qv = map(_f32, (k, v, a, beta, S0, queries))
+        B, T, H, dk = k.shape
+        dv = v.shape[-1]
+        pos = _i32(pos)
+        P, Qn = pos.shape[1], qv.shape[3]
+        par = None if parent is None else _i32(parent)
+        o = np.zeros((B, P, H, Qn, dv), dtype=np.float64)
+        status = self.lib.oracle_read_states(B, T, H, dk, dv, P, Qn, _p(k, _f32p), _p(v, _f32p),
+                                             _p(a, _f32p), _p(beta, _f32p), _p(S0, _f32p),
+                                             _p(par, _i32p), _p(pos, _i32p), _p(qv, _f32p),
+                                             _p(o, _f64p), _threads(nthreads))
+        return o, status
+
+    def select(self, logits, tokens, parent=None, nthreads=None):
+        """Greedy accepted-node selection.  logits [B, T+1, V] (fp32 values),
+        tokens [B, T].  Returns (target [B, T+1], accepted [B], acc_len [B],
+        bonus [B], status); entries of a sequence with an invalid parent row
+        are -2 in accepted, acc_len and bonus."""
+        lg = _f32(logits)
+        tok = _i32(tokens)
+        B, T1, V = lg.shape
+        T = T1 - 1
+        par = None if parent is None else _i32(parent)
+        target = np.zeros((B, T1), dtype=np.int32)
+        acc = np.full(B, -2, dtype=np.int32)
+        alen = np.full(B, -2, dtype=np.int32)
+        bonus = np.full(B, -2, dtype=np.int32)
+        status = self.lib.oracle_select(B, T, V, _p(lg, _f32p), _p(tok, _i32p), _p(par, _i32p),
+                                        _p(target, _i32p), _p(acc, _i32p), _p(alen, _i32p),
+                                        _p(bonus, _i32p), _threads(nthreads))
+        return target, acc, alen, bonus, status
+
 
 _DEFAULT = None
 
@@ -175,3 +216,11 @@ def verify_dfs(*args, **kw):
 
 def gather(*args, **kw):
     return default().gather(*args, **kw)
+
+
+def read_states(*args, **kw):
+    return default().read_states(*args, **kw)
+
+
+def select(*args, **kw):
+    return default().select(*args, **kw)

@@ -27,10 +27,19 @@
  * Inputs are the exact fp32 values handed to the GPU (bf16 inputs arrive as
  * their exact fp32 widening); all arithmetic is fp64.
  *
+ * Two steps around verify follow from the same definitions:
+ *   - reads inside the verified block (ReaDy page, Fig. 2a: the drafter reads
+ *     recurrent states at chosen positions): o = S_j q for a node j of the
+ *     block, S_j rebuilt by the same walk (S0 itself for j = -1);
+ *   - greedy accepted-node selection (Bole page, summary and section IV:
+ *     verification decides the accepted prefix, then only the selected state
+ *     is kept): walk down from the committed state, at each step taking the
+ *     child whose draft token equals the target's most likely token there.
+ *
  * Status bits (returned, OR-ed): 1 = a parent index outside [-1, n-1],
  * 2 = an accepted index outside [-1, T-1], 4 = a slot index outside
- * [0, num_slots).  The outputs of an affected sequence (or position) are left
- * untouched.
+ * [0, num_slots), 8 = a read position outside [-1, T-1].  The outputs of an
+ * affected sequence (or position) are left untouched.
  */
 #include <pthread.h>
 #include <stdint.h>
@@ -40,6 +49,7 @@
 #define OR_BAD_PARENT 1
 #define OR_BAD_ACCEPTED 2
 #define OR_BAD_SLOT 4
+#define OR_BAD_POSITION 8
 
 /* ---------------------------------------------------------------- threads */
 
@@ -409,5 +419,143 @@ int oracle_gather(int B, int P, int H, int dk, int dv, int num_slots, int Qn, co
         if (slot[i] < 0 || slot[i] >= num_slots) status |= OR_BAD_SLOT;
     gather_ctx c = {B, P, H, dk, dv, num_slots, Qn, pool, slot, queries, o, states_out};
     run_items(gather_item, &c, (long)B * P * H, 1, nthreads);
+    return status;
+}
+
+/* ------------------------------------------------ reads inside the block */
+
+typedef struct {
+    walk_ctx w;
+    int P, Qn;
+    const int32_t* pos;
+    const float* queries;
+    double* o;
+} read_ctx;
+
+static void read_item(void* vctx, long item, double* work) {
+    const read_ctx* c = (const read_ctx*)vctx;
+    const walk_ctx* w = &c->w;
+    int h = (int)(item % w->H);
+    long bp = item / w->H; /* b * P + p */
+    int b = (int)(bp / c->P);
+    int n = c->pos[bp];
+    if (n < -1 || n >= w->T || !w->seq_ok[b]) return;
+    const size_t dd = (size_t)w->dk * w->dv;
+    double* S = work;
+    double* x = S + dd;
+    int* path = (int*)(x + w->dv);
+    walk_to(w, b, h, n, S, x, path, NULL);
+    for (int i = 0; i < c->Qn; ++i)
+        read_state(S, w->dk, w->dv, c->queries + (((size_t)bp * w->H + h) * c->Qn + i) * w->dk,
+                   c->o + (((size_t)bp * w->H + h) * c->Qn + i) * w->dv);
+}
+
+/*
+ * Reads of states inside the verified block, without a commit:
+ *   o[b, p, h, i, :] = S_j q_{b,p,h,i},   j = pos[b, p] in [-1, T-1],
+ * S_j the walk's state at node j (S0 for j = -1).
+ *   k, v, a, beta, S0, parent: as for oracle_verify; pos: [B, P];
+ *   queries: [B, P, H, Qn, dk]; o: [B, P, H, Qn, dv] fp64.
+ * A position outside [-1, T-1] sets OR_BAD_POSITION and is skipped.  The
+ * parent row is needed (and checked) only when a valid position of the
+ * sequence is a node (>= 0); when it is invalid, OR_BAD_PARENT is set and
+ * nothing of that sequence is written.
+ */
+int oracle_read_states(int B, int T, int H, int dk, int dv, int P, int Qn, const float* k, const float* v,
+                       const float* a, const float* beta, const float* S0, const int32_t* parent,
+                       const int32_t* pos, const float* queries, double* o, int nthreads) {
+    if (B <= 0 || P <= 0 || H <= 0 || Qn <= 0) return 0;
+    unsigned char* ok = (unsigned char*)malloc((size_t)B);
+    int status = 0;
+    for (int b = 0; b < B; ++b) {
+        int needs_parent = 0;
+        for (int p = 0; p < P; ++p) {
+            int n = pos[(size_t)b * P + p];
+            if (n < -1 || n >= T) status |= OR_BAD_POSITION;
+            else if (n >= 0) needs_parent = 1;
+        }
+        ok[b] = (unsigned char)(!needs_parent || parents_valid(parent, T, b));
+        if (!ok[b]) status |= OR_BAD_PARENT;
+    }
+    read_ctx c = {{B, T, H, dk, dv, NULL, k, v, a, beta, S0, parent, NULL, NULL, NULL, NULL, NULL, ok},
+                  P, Qn, pos, queries, o};
+    run_items(read_item, &c, (long)B * P * H, walk_work(T > 0 ? T : 1, dk, dv), nthreads);
+    free(ok);
+    return status;
+}
+
+/* ------------------------------------------- accepted-node selection */
+
+/* Index of the largest value of x[0..V-1]; equal values go to the lowest
+ * index, NaN never wins (+0 and -0 are equal), and a row of NaN gives 0. */
+static int row_argmax(const float* x, long V) {
+    long best = -1;
+    float bv = 0.f;
+    for (long i = 0; i < V; ++i) {
+        float t = x[i];
+        if (t != t) continue;
+        if (best < 0 || t > bv) {
+            best = i;
+            bv = t;
+        }
+    }
+    return best < 0 ? 0 : (int)best;
+}
+
+typedef struct {
+    long V;
+    const float* logits;
+    int32_t* target;
+} argmax_ctx;
+
+static void argmax_item(void* vctx, long item, double* work) {
+    const argmax_ctx* c = (const argmax_ctx*)vctx;
+    (void)work;
+    c->target[item] = row_argmax(c->logits + (size_t)item * c->V, c->V);
+}
+
+/*
+ * Greedy selection of the accepted node.
+ *   logits: [B, T+1, V]; row 0 is the target's prediction at the committed
+ *     position, row n+1 its prediction after draft node n.
+ *   tokens: [B, T] the draft token of each node; parent: [B, T] or NULL (chain).
+ * Outputs: target[B, T+1] = argmax of each row (row_argmax rules);
+ *   accepted[b]: start at cur = -1 (the committed state); while some child c
+ *   of cur (parent[c] == cur) has tokens[c] == target[cur + 1], move to the
+ *   lowest-index such child; accepted[b] = the final cur (-1 if none).
+ *   acc_len[b] = number of nodes moved through (the accepted node's depth);
+ *   bonus[b] = target[b, accepted[b] + 1], the target's token after it.
+ *   acc_len and bonus may be NULL.
+ * An invalid parent row sets OR_BAD_PARENT and leaves accepted, acc_len and
+ * bonus of that sequence untouched (target is still written).
+ */
+int oracle_select(int B, int T, long V, const float* logits, const int32_t* tokens, const int32_t* parent,
+                  int32_t* target, int32_t* accepted, int32_t* acc_len, int32_t* bonus, int nthreads) {
+    if (B <= 0 || T < 0 || V <= 0) return 0;
+    argmax_ctx ac = {V, logits, target};
+    run_items(argmax_item, &ac, (long)B * (T + 1), 1, nthreads);
+    int status = 0;
+    for (int b = 0; b < B; ++b) {
+        if (!parents_valid(parent, T, b)) {
+            status |= OR_BAD_PARENT;
+            continue;
+        }
+        const int32_t* tg = target + (size_t)b * (T + 1);
+        int cur = -1, len = 0;
+        for (;;) {
+            int want = tg[cur + 1], next = -1;
+            for (int c = cur + 1; c < T; ++c)
+                if (parent_of(parent, T, b, c) == cur && tokens[(size_t)b * T + c] == want) {
+                    next = c;
+                    break;
+                }
+            if (next < 0) break;
+            cur = next;
+            ++len;
+        }
+        accepted[b] = cur;
+        if (acc_len) acc_len[b] = len;
+        if (bonus) bonus[b] = tg[cur + 1];
+    }
     return status;
 }

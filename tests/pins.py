@@ -11,6 +11,15 @@ when the oracle disagrees with:
   * special cases with closed forms (b = 0: pure decay; a = 1, b = 0: pure
     read; b = 1 with a unit key: the delta rule overwrites the value at that
     key).
+For the reads of in-block states and the accepted-node selection:
+  * the hand-worked tree above and a hand-worked selection example
+    (tests/golden/select_forest6_handworked.json),
+  * the factorised state P_j S0 + sum (P_j/P_m) u_m k_m^T with U from the
+    library solve, and brute-force matrices,
+  * a set-based restatement of the greedy walk (a node is accepted iff every
+    node on its path is the first child whose token the target predicts) with
+    an argmax written as a minimum over sort keys, and numpy's argmax on
+    chains.
 The same functions run against oracle builds with planted mistakes
 (test_oracle_mutants.py) to show that each plausible mistake fails one.
 """
@@ -273,5 +282,155 @@ def pin_gather(orc, seed=19):
             assert rel_err(o[b, p], want) <= 1e-15
 
 
+def pin_read_golden(orc):
+    """Reads of the hand-worked tree's states: o = S_j q, exact (dyadic)."""
+    g, fr = load_golden()
+    T = len(g["parent"])
+    k = fr(g["k"]).reshape(1, T, 1, 2).astype(np.float32)
+    v = fr(g["v"]).reshape(1, T, 1, 2).astype(np.float32)
+    a = fr(g["a"]).reshape(1, T, 1).astype(np.float32)
+    beta = fr(g["beta"]).reshape(1, T, 1).astype(np.float32)
+    S0 = fr(g["S0"]).reshape(1, 1, 2, 2).astype(np.float32)
+    par = np.array(g["parent"], dtype=np.int32).reshape(1, T)
+    pos = np.array([[-1, 1, 3, 2, 0]], dtype=np.int32)
+    qs = np.array([[1, 0], [0, 1], [1, -2]], dtype=np.float32)
+    queries = np.broadcast_to(qs, (1, pos.shape[1], 1, 3, 2)).copy()
+    o, status = orc.read_states(k, v, a, beta, S0, pos, queries, par)
+    assert status == 0
+    states = fr(g["states"])
+    for p, n in enumerate(pos[0]):
+        S = fr(g["S0"]) if n < 0 else states[n]
+        want = S @ qs.T.astype(np.float64)
+        assert np.array_equal(o[0, p, 0], want.T), (n, o[0, p, 0], want.T)
+
+
+def pin_read_from_factors(orc, seed=21, B=2, T=16, H=2, d=8, P=6, Qn=3, tol=1e-10):
+    """In-block reads equal P_j S0 q + sum_{m on path(j)} (P_j/P_m)(k_m . q) u_m,
+    U from Eq. (2)'s library solve; position -1 reads S0 itself."""
+    c = random_case(seed, B, T, H, d, d, "tree", max_depth=5)
+    rng = np.random.default_rng(seed + 1)
+    pos = rng.integers(-1, T, size=(B, P)).astype(np.int32)
+    pos[0, 0] = -1
+    queries = rng.standard_normal((B, P, H, Qn, d)).astype(np.float32)
+    o, status = orc.read_states(c["k"], c["v"], c["a"], c["beta"], c["S0"], pos, queries, c["parent"])
+    assert status == 0
+    for b in range(B):
+        for h in range(H):
+            _, U, Pn, _ = closed_form_head(c["q"][b, :, h], c["k"][b, :, h], c["v"][b, :, h],
+                                           c["a"][b, :, h], c["beta"][b, :, h],
+                                           c["S0"][b, h].astype(np.float64), c["parent"][b])
+            S0 = c["S0"][b, h].astype(np.float64)
+            for p in range(P):
+                j = int(pos[b, p])
+                q = queries[b, p, h].astype(np.float64)  # [Qn, d]
+                if j < 0:
+                    want = q @ S0.T
+                else:
+                    want = Pn[j] * (q @ S0.T)
+                    for m in path_of(c["parent"][b], j):
+                        km = c["k"][b, m, h].astype(np.float64)
+                        want = want + (Pn[j] / Pn[m]) * np.outer(q @ km, U[m])
+                e = rel_err(o[b, p, h], want)
+                assert e <= tol, ("read factors", b, h, p, e)
+
+
+def pin_read_brute_force(orc, seed=22, B=2, T=9, H=2, dk=6, dv=5, P=5, Qn=2, tol=1e-12):
+    """In-block reads equal explicit matrix products on tiny sizes."""
+    c = random_case(seed, B, T, H, dk, dv, "tree", max_depth=4, unit_k=False)
+    rng = np.random.default_rng(seed + 1)
+    pos = rng.integers(-1, T, size=(B, P)).astype(np.int32)
+    queries = rng.standard_normal((B, P, H, Qn, dk)).astype(np.float32)
+    o, status = orc.read_states(c["k"], c["v"], c["a"], c["beta"], c["S0"], pos, queries, c["parent"])
+    assert status == 0
+    for b in range(B):
+        for h in range(H):
+            S = brute_force_states(c["k"][b, :, h], c["v"][b, :, h], c["a"][b, :, h].astype(np.float64),
+                                   c["beta"][b, :, h].astype(np.float64), c["S0"][b, h], c["parent"][b])
+            for p in range(P):
+                j = int(pos[b, p])
+                Sj = c["S0"][b, h].astype(np.float64) if j < 0 else S[j]
+                want = queries[b, p, h].astype(np.float64) @ Sj.T
+                assert rel_err(o[b, p, h], want) <= tol
+
+
+def _argmax_by_keys(row):
+    """Index of the winner: the minimum of (is NaN, -value, index)."""
+    keys = [(bool(np.isnan(x)), 0.0 if np.isnan(x) else -float(x), i) for i, x in enumerate(row)]
+    return min(keys)[2]
+
+
+def _select_by_sets(target, tokens, par_row):
+    """Accepted node as the deepest node whose whole path is 'taken': node m is
+    taken iff tokens[m] == target[parent(m) + 1] and no lower-index sibling has
+    the same token.  The taken-path nodes form one chain."""
+    T = len(tokens)
+    taken = []
+    for m in range(T):
+        p = int(par_row[m])
+        first = all(not (int(par_row[s]) == p and tokens[s] == tokens[m]) for s in range(m))
+        taken.append(tokens[m] == target[p + 1] and first)
+    ok = [all(taken[x] for x in path_of(par_row, n)) for n in range(T)]
+    deepest, depth = -1, 0
+    for n in range(T):
+        d = len(path_of(par_row, n))
+        if ok[n]:
+            assert d != depth or n == deepest, "two accepted paths"
+            if d > depth:
+                deepest, depth = n, d
+    return deepest, depth
+
+
+def pin_select_golden(orc):
+    """Hand-worked selection with equal maxima, NaN, -inf and signed zeros."""
+    with open(os.path.join(GOLDEN, "select_forest6_handworked.json")) as f:
+        g = json.load(f)
+    logits = np.array([[float(x) for x in row] for row in g["logits"]], dtype=np.float32)[None]
+    tokens = np.array([g["tokens"]], dtype=np.int32)
+    par = np.array([g["parent"]], dtype=np.int32)
+    target, acc, alen, bonus, status = orc.select(logits, tokens, par)
+    assert status == 0
+    assert target[0].tolist() == g["target"], target
+    assert (int(acc[0]), int(alen[0]), int(bonus[0])) == (g["accepted"], g["accepted_len"], g["bonus"])
+
+
+def pin_select_sets(orc, seed=23, B=24, T=12, V=4):
+    """Greedy walk equals the set-based restatement, on small vocabularies with
+    many equal logits, NaN and matching siblings."""
+    rng = np.random.default_rng(seed)
+    par = make_tree(rng, B, T, 5, 3)
+    tokens = rng.integers(0, V, size=(B, T)).astype(np.int32)
+    logits = rng.integers(-2, 3, size=(B, T + 1, V)).astype(np.float32)
+    logits[rng.random(logits.shape) < 0.1] = np.nan
+    target, acc, alen, bonus, status = orc.select(logits, tokens, par)
+    assert status == 0
+    for b in range(B):
+        want_t = [_argmax_by_keys(logits[b, r]) for r in range(T + 1)]
+        assert target[b].tolist() == want_t
+        n, d = _select_by_sets(want_t, tokens[b].tolist(), par[b])
+        assert (int(acc[b]), int(alen[b]), int(bonus[b])) == (n, d, want_t[n + 1]), (b, acc[b], n)
+
+
+def pin_select_chain(orc, seed=24, B=16, T=10, V=50):
+    """On a chain the accepted length is the leading run of nodes whose token
+    is numpy's argmax of the row before them."""
+    rng = np.random.default_rng(seed)
+    logits = rng.standard_normal((B, T + 1, V)).astype(np.float32)
+    tokens = rng.integers(0, V, size=(B, T)).astype(np.int32)
+    for b in range(B):  # plant agreement on a random prefix
+        for n in range(int(rng.integers(0, T + 1))):
+            tokens[b, n] = int(np.argmax(logits[b, n]))
+    for par in (None, make_chain(B, T)):
+        target, acc, alen, bonus, status = orc.select(logits, tokens, par)
+        assert status == 0
+        am = np.argmax(logits, axis=-1)
+        assert np.array_equal(target, am)
+        run = np.cumprod(tokens == am[:, :T], axis=1).sum(axis=1)
+        assert np.array_equal(alen, run)
+        assert np.array_equal(acc, run - 1)
+        assert np.array_equal(bonus, am[np.arange(B), run])
+
+
 ALL_PINS = [pin_golden, pin_closed_form, pin_commit_from_factors, pin_brute_force, pin_pure_decay,
-            pin_pure_read, pin_overwrite, pin_chain_equals_decode, pin_tree_equals_dfs, pin_gather]
+            pin_pure_read, pin_overwrite, pin_chain_equals_decode, pin_tree_equals_dfs, pin_gather,
+            pin_read_golden, pin_read_from_factors, pin_read_brute_force, pin_select_golden,
+            pin_select_sets, pin_select_chain]

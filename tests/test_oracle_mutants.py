@@ -22,6 +22,11 @@ MUTANTS = {
     "chain parent off by one": (": n - 1;", ": n - 2;"),
     "gather copies the wrong head": ("const float* src = c->pool + ((size_t)s * c->H + h) * dd;",
                                      "const float* src = c->pool + ((size_t)s * c->H + (h + 1) % c->H) * dd;"),
+    "block read at the parent's state": ("walk_to(w, b, h, n, S, x, path, NULL);",
+                                         "walk_to(w, b, h, n >= 0 ? parent_of(w->parent, w->T, b, n) : n, S, x, path, NULL);"),
+    "argmax keeps the last maximum": ("if (best < 0 || t > bv) {", "if (best < 0 || t >= bv) {"),
+    "walk takes the last matching child": ("next = c;\n                    break;", "next = c;"),
+    "bonus read one row early": ("if (bonus) bonus[b] = tg[cur + 1];", "if (bonus) bonus[b] = tg[cur < 0 ? 0 : cur];"),
 }
 
 

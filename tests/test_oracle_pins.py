@@ -75,3 +75,38 @@ def test_forest_roots(orc):
     O, _, _, _ = pins.closed_form_head(c["q"][0, :, 0], c["k"][0, :, 0], c["v"][0, :, 0], c["a"][0, :, 0],
                                        c["beta"][0, :, 0], c["S0"][0, 0], c["parent"][0])
     assert pins.rel_err(o[0, :, 0], O) <= 1e-10
+
+
+def test_read_bad_position_reported_and_skipped(orc):
+    c = pins.random_case(45, 2, 6, 2, 8, 8, "tree")
+    pos = np.array([[0, 6, -1], [-2, 5, 2]], np.int32)
+    qs = np.ones((2, 3, 2, 2, 8), np.float32)
+    o, status = orc.read_states(c["k"], c["v"], c["a"], c["beta"], c["S0"], pos, qs, c["parent"])
+    assert status == 8
+    assert np.all(o[0, 1] == 0) and np.all(o[1, 0] == 0)
+    assert np.any(o[0, 0] != 0) and np.any(o[0, 2] != 0) and np.any(o[1, 1] != 0)
+
+
+def test_read_parent_checked_only_for_node_positions(orc):
+    c = pins.random_case(46, 2, 6, 2, 8, 8, "tree")
+    c["parent"][:, 3] = 5                      # invalid in both sequences
+    pos = np.array([[-1, -1], [-1, 2]], np.int32)
+    qs = np.ones((2, 2, 2, 1, 8), np.float32)
+    o, status = orc.read_states(c["k"], c["v"], c["a"], c["beta"], c["S0"], pos, qs, c["parent"])
+    assert status == 1
+    want = np.einsum("hij,j->hi", c["S0"][0].astype(np.float64), np.ones(8))
+    assert np.array_equal(o[0, 0, :, 0], want) and np.array_equal(o[0, 1, :, 0], want)
+    assert np.all(o[1] == 0)                   # the whole sequence is skipped
+
+
+def test_select_bad_parent_leaves_sequence_untouched(orc):
+    rng = np.random.default_rng(47)
+    logits = rng.standard_normal((3, 5, 9)).astype(np.float32)
+    tokens = rng.integers(0, 9, size=(3, 4)).astype(np.int32)
+    par = np.tile(np.array([-1, 0, 1, 2], np.int32), (3, 1))
+    par[1, 2] = 2
+    target, acc, alen, bonus, status = orc.select(logits, tokens, par)
+    assert status == 1
+    assert np.array_equal(target, np.argmax(logits, axis=-1))
+    assert acc[1] == -2 and alen[1] == -2 and bonus[1] == -2
+    assert acc[0] >= -1 and acc[2] >= -1

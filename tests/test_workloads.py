@@ -50,3 +50,28 @@ def test_gather_inputs():
         s = x["slot"][b]
         assert len(set(s.tolist())) == 4 and np.all((s >= b * 16) & (s < b * 16 + 16))
     assert x["queries"].shape == (3, 4, 2, 16, 128)
+
+
+def test_block_read_inputs():
+    from workloads import WORKLOADS, make_block_read_inputs
+    wl = WORKLOADS["hybrid27b-chain-gather"].replace(B=6)
+    r = make_block_read_inputs(wl)
+    assert r["pos"].shape == (6, 4) and r["queries"].shape == (6, 4, 32, 16, 128)
+    for row in r["pos"]:
+        assert len(set(row.tolist())) == 4 and row.min() >= 0 and row.max() < wl.T
+    r2 = make_block_read_inputs(wl)
+    assert np.array_equal(r["pos"], r2["pos"]) and np.array_equal(r["queries"], r2["queries"])
+
+
+def test_select_inputs_plant_the_drawn_path():
+    from workloads import WORKLOADS, make_inputs, make_select_inputs
+    wl = WORKLOADS["tree64"].replace(B=4, V=1000)
+    x = make_inputs(wl, with_gather=False)
+    s = make_select_inputs(wl, x["parent"], x["accepted"])
+    assert s["tokens"].shape == (4, 64) and s["logits"].shape == (4, 65, 1000)
+    for b in range(4):
+        n = int(x["accepted"][b])
+        while n >= 0:
+            p = int(x["parent"][b, n])
+            assert s["logits"][b, p + 1, s["tokens"][b, n]] == 8.0
+            n = p

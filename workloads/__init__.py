@@ -20,6 +20,18 @@ Distributions (the second argument of N(mu, s) is the standard deviation):
   S0      N(0, s0_std)                     fp32, [B, H, dv, dk]
 The draw order per workload is fixed: S0, q, k, v, a, beta, parent,
 acceptance, then (gather only) pool, slots, queries.
+
+Two further input sets come from generators of their own, seeded from the
+workload seed and a fixed stream tag, so they leave the draws above alone:
+  block reads    positions [B, P]: P distinct nodes of the block per sequence
+                 (uniform without replacement); queries [B, P, H, Qn, d] as
+                 for the gather
+  selection      draft tokens [B, T] uniform over a vocabulary of V; target
+                 logits [B, T+1, V] N(0, 1), cast like q/k/v, with the token of
+                 every node on the root path of the drawn accepted node set to
+                 8 in the row that predicts it (so the target agrees with the
+                 draft along that path; which node is accepted is still decided
+                 by the selection itself)
 """
 from __future__ import annotations
 
@@ -30,7 +42,11 @@ import numpy as np
 
 __all__ = ["Workload", "WORKLOADS", "make_inputs", "bf16_round",
            "make_tree", "make_chain", "draw_acceptance", "tree_depths",
-           "l2_normalise_f32"]
+           "l2_normalise_f32", "make_block_read_inputs", "make_select_inputs"]
+
+# stream tags of the generators that do not share the main draw sequence
+_READ_STREAM = 101
+_SELECT_STREAM = 102
 
 
 @dataclasses.dataclass(frozen=True)
@@ -52,6 +68,8 @@ class Workload:
     Qn: int = 0       # query vectors per (sequence, position, head)
     max_depth: int = 8
     max_fanout: int = 4
+    # vocabulary of the target logits for accepted-node selection (0 = none)
+    V: int = 0
 
     def replace(self, **kw) -> "Workload":
         return dataclasses.replace(self, **kw)
@@ -65,20 +83,20 @@ WORKLOADS = {
     "gdn1.3b-chain": Workload(
         "gdn1.3b-chain", "GDN-1.3B-shaped layer, chain verify: B16 H16 d128, chain of 8",
         B=16, H=16, D=128, T=8, topology="chain", qkv="bf16", s0_std=0.05,
-        accept="geometric", seed=2),
+        accept="geometric", seed=2, V=32000),
     "tree64": Workload(
         "tree64", "tree verify: B32 H16 d128, 64-node tree (depth<=8, fan-out<=4)",
         B=32, H=16, D=128, T=64, topology="tree", qkv="bf16", s0_std=0.05,
-        accept="root-path", seed=3),
+        accept="root-path", seed=3, V=32000),
     "hybrid27b-chain-gather": Workload(
         "hybrid27b-chain-gather",
         "27B-hybrid-shaped layer: B64 H32 d128, chain of 16 + state reads at 4 positions x 16 queries",
         B=64, H=32, D=128, T=16, topology="chain", qkv="bf16", s0_std=0.05,
-        accept="geometric", seed=4, P=4, R=16, Qn=16),
+        accept="geometric", seed=4, P=4, R=16, Qn=16, V=151936),
     "batch256-tree-commit": Workload(
         "batch256-tree-commit", "large-batch commit: B256 H32 d128, 32-node tree, accepted uniform over nodes",
         B=256, H=32, D=128, T=32, topology="tree", qkv="bf16", s0_std=0.05,
-        accept="uniform-node", seed=5),
+        accept="uniform-node", seed=5, V=151936),
 }
 
 
@@ -226,3 +244,48 @@ def make_gather_inputs(rng: np.random.Generator, wl: Workload) -> dict:
         slot[b] = b * R + rng.choice(R, size=P, replace=False)
     queries = l2_normalise_f32(rng.standard_normal((B, P, H, Qn, D), dtype=np.float32))
     return {"pool": pool, "slot": slot, "queries": _cast(queries, wl.qkv)}
+
+
+def make_block_read_inputs(wl: Workload, P: Optional[int] = None, Qn: Optional[int] = None,
+                           seed: Optional[int] = None) -> dict:
+    """Positions and queries for reads of states inside the verified block.
+
+    P distinct node positions per sequence (default: the workload's gather P,
+    at most T) and Qn queries per (sequence, position, head), unit-normalised
+    and cast like q.
+    """
+    rng = np.random.default_rng([wl.seed if seed is None else seed, _READ_STREAM])
+    B, H, D, T = wl.B, wl.H, wl.D, wl.T
+    P = min(wl.P or 4, T) if P is None else P
+    Qn = (wl.Qn or 16) if Qn is None else Qn
+    pos = np.empty((B, P), dtype=np.int32)
+    for b in range(B):
+        pos[b] = rng.choice(T, size=P, replace=P > T)
+    queries = l2_normalise_f32(rng.standard_normal((B, P, H, Qn, D), dtype=np.float32))
+    return {"pos": pos, "queries": _cast(queries, wl.qkv)}
+
+
+def make_select_inputs(wl: Workload, parent: np.ndarray, accepted: np.ndarray,
+                       V: Optional[int] = None, logits_dtype: Optional[str] = None,
+                       seed: Optional[int] = None) -> dict:
+    """Draft tokens and target logits for greedy accepted-node selection.
+
+    ``accepted`` (the workload's drawn acceptance) only shapes the logits: the
+    row that predicts each node on its root path gets the value 8 at that
+    node's token.  Returns tokens [B, T] int32 and logits [B, T+1, V] fp32
+    (bf16-exact when the dtype is bf16).
+    """
+    rng = np.random.default_rng([wl.seed if seed is None else seed, _SELECT_STREAM])
+    B, T = parent.shape
+    V = wl.V if V is None else V
+    if V <= 0:
+        raise ValueError("workload has no vocabulary")
+    tokens = rng.integers(0, V, size=(B, T), dtype=np.int32)
+    logits = rng.standard_normal((B, T + 1, V), dtype=np.float32)
+    for b in range(B):
+        n = int(accepted[b])
+        while n >= 0:
+            p = int(parent[b, n])
+            logits[b, p + 1, tokens[b, n]] = 8.0
+            n = p
+    return {"tokens": tokens, "logits": _cast(logits, logits_dtype or wl.qkv)}
