@@ -55,6 +55,7 @@ extern "C" {
 #define LDV_STATUS_BAD_PARENT 1   /* parent[b, n] outside [-1, n-1] */
 #define LDV_STATUS_BAD_ACCEPTED 2 /* accepted[b] outside [-1, T-1] */
 #define LDV_STATUS_BAD_SLOT 4     /* slot[b, p] outside [0, num_slots) */
+#define LDV_STATUS_BAD_POSITION 8 /* pos[b, p] outside [-1, T-1] */
 
 /* Element type of q / k / v / queries. */
 #define LDV_BF16 0
@@ -144,6 +145,34 @@ int ldv_commit_state(int B, int T, int H, int dk, int dv, int k_dtype,
 int ldv_gather_states(int B, int P, int H, int dk, int dv, int num_slots, int Qn, int q_dtype,
                       const float* pool, const int32_t* slot, const void* queries,
                       float* o, float* states_out, int* status, void* stream);
+
+/*
+ * Read states inside the verified block without forming them.  The drafter
+ * of the ReaDy page (arXiv 2610.20503, Fig. 2a) reads recurrent states at
+ * chosen positions; for a node j of the block just verified, the Bole page
+ * (arXiv 2608.01651, section IV, Eq. (9) / "Lemma 1") writes its state from
+ * the verify factors, so that
+ *     j = pos[b, p] in [-1, T-1]
+ *     o[b, p, h, i, :] = S_j q = P_j S0[b, h] q + sum_{m on root-to-j path} (P_j / P_m) (k_m . q) u_m
+ * with q = queries[b, p, h, i, :] and P = exp(logp); j = -1 reads S0 itself.
+ * Each head's S0 is read once for all P x Qn queries.
+ *
+ *   k         [B, T, H, dk] element type qk_dtype (the verified block's keys)
+ *   u, logp   [B, T, H, dv], [B, T, H] fp32, as written by the verify call
+ *   parent    [B, T] int32 or NULL for a chain
+ *   S0        [B, H, dv, dk] fp32, the committed state the block was verified from
+ *   pos       [B, P] int32 in [-1, T-1]; duplicates allowed
+ *   queries   [B, P, H, Qn, dk] element type qk_dtype
+ *   o         [B, P, H, Qn, dv] fp32 (written)
+ * A position outside [-1, T-1] -> LDV_STATUS_BAD_POSITION and its outputs are
+ * unwritten.  The parent row is needed only when a valid position of the
+ * sequence is a node; if it is then invalid -> LDV_STATUS_BAD_PARENT and
+ * nothing of that sequence is written.  Qn == 0 is a no-op.
+ */
+int ldv_read_block_states(int B, int T, int H, int dk, int dv, int P, int Qn, int qk_dtype,
+                          const void* k, const float* u, const float* logp, const int32_t* parent,
+                          const float* S0, const int32_t* pos, const void* queries, float* o,
+                          int* status, void* stream);
 
 /* Text for an LDV_OK / LDV_ERR_* return code (static storage). */
 const char* ldv_status_string(int code);

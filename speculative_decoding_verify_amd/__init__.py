@@ -5,7 +5,7 @@ package is its Python binding.  Importing the package loads the library and
 fails if it has not been built.
 """
 from .ldv import (LDV_BF16, LDV_F32, MAX_T, STATUS_BAD_ACCEPTED, STATUS_BAD_PARENT,  # noqa: F401
-                  STATUS_BAD_SLOT, LdvError, commit_state, gather_states, load, status_string,
-                  verify_chain, verify_tree, version)
+                  STATUS_BAD_POSITION, STATUS_BAD_SLOT, LdvError, commit_state, gather_states, load,
+                  read_block_states, status_string, verify_chain, verify_tree, version)
 
 load()

@@ -99,6 +99,26 @@ LDV_EXPORT int ldv_gather_states(int B, int P, int H, int dk, int dv, int num_sl
     return e == hipSuccess ? LDV_OK : LDV_ERR_LAUNCH;
 }
 
+LDV_EXPORT int ldv_read_block_states(int B, int T, int H, int dk, int dv, int P, int Qn, int qk_dtype,
+                                     const void* k, const float* u, const float* logp, const int32_t* parent,
+                                     const float* S0, const int32_t* pos, const void* queries, float* o,
+                                     int* status, void* stream) {
+    if (B < 0 || T < 0 || H < 0 || P < 0 || Qn < 0 || dk <= 0 || dv <= 0) return LDV_ERR_ARG;
+    if (qk_dtype != LDV_BF16 && qk_dtype != LDV_F32) return LDV_ERR_ARG;
+    if (dk != dv || !supported_d(dk) || T > LDV_MAX_T) return LDV_ERR_UNSUPPORTED;
+    if (B == 0 || T == 0 || H == 0 || P == 0 || Qn == 0) return LDV_OK;
+    if (!k || !u || !logp || !S0 || !pos || !queries || !o) return LDV_ERR_ARG;
+    if (!aligned(k, 16) || !aligned(u, 16) || !aligned(S0, 16) || !aligned(queries, 16) || !aligned(o, 16) ||
+        !aligned(logp, 4) || !aligned(parent, 4) || !aligned(pos, 4) || !aligned(status, 4))
+        return LDV_ERR_ARG;
+    if ((long long)P * Qn > 0x7fffffffLL ||
+        (long long)B * H * 2 * (((long long)P * Qn + 63) / 64) > 0x7fffffffLL)
+        return LDV_ERR_UNSUPPORTED;
+    ldv::ReadArgs args{B, T, H, dk, P, Qn, k, u, logp, parent, S0, pos, queries, o, status};
+    hipError_t e = ldv::launch_read(args, qk_dtype == LDV_F32, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? LDV_OK : LDV_ERR_LAUNCH;
+}
+
 LDV_EXPORT const char* ldv_status_string(int code) {
     switch (code) {
         case LDV_OK: return "ok";

@@ -43,10 +43,24 @@ struct GatherArgs {
     int* status;
 };
 
+struct ReadArgs {
+    int B, T, H, D, P, Qn;
+    const void* k;
+    const float* u;
+    const float* logp;
+    const int32_t* parent;  // NULL: chain
+    const float* S0;
+    const int32_t* pos;
+    const void* queries;
+    float* o;
+    int* status;  // may be NULL
+};
+
 // Each launcher assumes arguments already validated by the C ABI layer and
 // returns the HIP launch status.
 hipError_t launch_verify(const VerifyArgs& a, bool f32_inputs, hipStream_t stream);
 hipError_t launch_commit(const CommitArgs& a, bool f32_k, hipStream_t stream);
 hipError_t launch_gather(const GatherArgs& a, bool f32_queries, hipStream_t stream);
+hipError_t launch_read(const ReadArgs& a, bool f32_inputs, hipStream_t stream);
 
 }  // namespace ldv

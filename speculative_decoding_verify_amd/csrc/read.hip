@@ -1,0 +1,361 @@
+// Reads of states inside the verified block, without forming them (gfx950).
+//
+// The ReaDy page (arXiv 2610.20503, Fig. 2a) has the drafter read recurrent
+// states at chosen positions.  For a position inside the block that verify
+// just processed, the Bole page (arXiv 2608.01651, section IV, Eq. (9) and
+// its "Lemma 1") writes every node state through the factors verify leaves:
+//   S_j = P_j S0 + sum_{m on path(j)} (P_j / P_m) u_m k_m^T,
+// so a read is
+//   S_j q = P_j (S0 q) + sum_{m on path(j)} (P_j / P_m) (k_m . q) u_m,
+// and position -1 reads S0 itself.  All positions of a (sequence, head)
+// share S0, so it is read once for all P x Qn queries and no S_j is formed:
+// per head the traffic is S0 plus the queries and outputs, where a gather of
+// formed states reads one state per position.
+//
+// One workgroup per (sequence, head, value tile of BV rows, chunk of 64
+// queries), one wave per 16 value rows:
+//   1. issue the loads of the query chunk, K, the U tile, log P, the
+//      positions and the parent row, then the wave's S0 rows straight into
+//      MFMA operand registers (they stay in flight through steps 2-3);
+//   2. stage Q, K and the U tile in LDS; wave 0 turns the parent row into
+//      ancestor-or-self masks by pointer doubling;
+//   3. W[m, f] = [m on path(j_f)] exp(log P_j - log P_m) (k_m . q_f) on MFMA,
+//      one 16-query column block per wave;
+//   4. O^T = (S0 Q^T) diag(P_j) + U^T W on MFMA (S0, U and W carried as
+//      bf16 hi + lo terms), float4 stores.
+#include <limits.h>
+
+#include "ldv_device.hpp"
+#include "ldv_kernels.hpp"
+
+#include "../../include/ldv.h"
+
+namespace ldv {
+
+template <int D, int TM>
+struct RShape {
+    static constexpr int BV = D >= 64 ? 64 : D;  // value rows per block
+    static constexpr int NT = D / BV;            // value tiles per head
+    static constexpr int NW = BV / 16;           // waves per block
+    static constexpr int KS = (D + 31) / 32;     // MFMA k-steps over d_k
+    static constexpr int NQ = 64;                // queries per block (one per lane of wave 0)
+    static constexpr int NCB = NQ / 16;          // 16-query column blocks
+    static constexpr int QKLD = D + 8;           // bf16 row stride of Q / K in LDS
+    static constexpr int ULD = BV + 4;           // fp32 row stride of the U tile
+    static constexpr int WLD = NQ + 4;           // fp32 row stride of W
+    static constexpr int NKS = (TM + 31) / 32;   // MFMA k-steps over nodes
+    static constexpr int LOG2TM = TM <= 16 ? 4 : (TM <= 32 ? 5 : 6);
+};
+
+template <int D, int TM, bool F32IN>
+struct RLds {
+    using S = RShape<D, TM>;
+    static constexpr int NPL = F32IN ? 2 : 1;  // bf16 planes per operand (hi, then lo)
+    static constexpr size_t off_k = (size_t)NPL * S::NQ * S::QKLD * 2;
+    static constexpr size_t off_u = off_k + (size_t)NPL * TM * S::QKLD * 2;
+    static constexpr size_t off_w = off_u + (size_t)TM * S::ULD * 4;
+    static constexpr size_t off_anc = off_w + (size_t)TM * S::WLD * 4;
+    static constexpr size_t off_lp = off_anc + 8 * TM;
+    static constexpr size_t off_pos = off_lp + 4 * TM;
+    static constexpr size_t off_flag = off_pos + 4 * S::NQ;
+    static constexpr size_t total = off_flag + 16;
+};
+
+template <int D, int TM, bool F32IN>
+__global__ __launch_bounds__((RShape<D, TM>::NW * kWave)) void read_kernel(const ReadArgs p) {
+    using S = RShape<D, TM>;
+    using L = RLds<D, TM, F32IN>;
+    constexpr int BV = S::BV, NW = S::NW, KS = S::KS, NQ = S::NQ, NCB = S::NCB;
+    constexpr int QKLD = S::QKLD, ULD = S::ULD, WLD = S::WLD, NKS = S::NKS;
+    constexpr int NTHR = NW * kWave;
+    constexpr int EPC = F32IN ? 4 : 8;  // elements per 16-byte chunk
+    constexpr int CPR = D / EPC;        // chunks per q/k row
+    constexpr int QC = (NQ * CPR + NTHR - 1) / NTHR;
+    constexpr int KC = (TM * CPR + NTHR - 1) / NTHR;
+    constexpr int U4 = BV / 4;  // float4 chunks per U row of the tile
+    constexpr int UC = (TM * U4 + NTHR - 1) / NTHR;
+    static_assert(NQ == kWave, "one query column per lane of wave 0");
+
+    __shared__ __align__(16) unsigned char smem[L::total];
+    unsigned short* s_q = reinterpret_cast<unsigned short*>(smem);           // [NQ][QKLD] hi, then lo
+    unsigned short* s_k = reinterpret_cast<unsigned short*>(smem + L::off_k);  // [TM][QKLD] hi, then lo
+    float* s_u = reinterpret_cast<float*>(smem + L::off_u);                  // [TM][ULD]
+    float* s_w = reinterpret_cast<float*>(smem + L::off_w);                  // [TM][WLD]
+    uint64_t* s_anc = reinterpret_cast<uint64_t*>(smem + L::off_anc);       // [TM]
+    float* s_lp = reinterpret_cast<float*>(smem + L::off_lp);                // [TM]
+    int* s_pos = reinterpret_cast<int*>(smem + L::off_pos);                  // [NQ]
+    int* s_flag = reinterpret_cast<int*>(smem + L::off_flag);
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int c = lane & 15, g = lane >> 4;
+    const int T = p.T, H = p.H, P = p.P, Qn = p.Qn;
+    const int NQT = P * Qn;  // queries per (sequence, head), flattened f = p Qn + i
+    const int nch = (NQT + NQ - 1) / NQ;
+    const unsigned bid = xcd_remap(blockIdx.x, gridDim.x);
+    const int ch = (int)(bid % (unsigned)nch);
+    const unsigned r1 = bid / (unsigned)nch;
+    const int tile = (int)(r1 % S::NT);
+    const unsigned bh = r1 / S::NT;
+    const int h = (int)(bh % (unsigned)H), b = (int)(bh / (unsigned)H);
+    const int f0 = ch * NQ;
+    const int vrow0 = tile * BV + wave * 16;
+
+    // 1. loads, small ones first, branch-free (indices clamped into range;
+    // values past the ends are dropped when LDS is written)
+    const char* qbase = static_cast<const char*>(p.queries);
+    u32x4 qreg[QC];
+#pragma unroll
+    for (int i = 0; i < QC; ++i) {
+        const int chunk = tid + i * NTHR, col = (chunk % CPR) * EPC;
+        const int f = min(f0 + min(chunk / CPR, NQ - 1), NQT - 1);
+        const int pp = f / Qn, ii = f - pp * Qn;
+        const size_t off = (((((size_t)b * P + pp) * H + h) * Qn + ii) * D + col) * (F32IN ? 4 : 2);
+        qreg[i] = *reinterpret_cast<const u32x4*>(qbase + off);
+    }
+    u32x4 kreg[KC];
+#pragma unroll
+    for (int i = 0; i < KC; ++i) {
+        const int chunk = tid + i * NTHR, col = (chunk % CPR) * EPC;
+        const int m = min(chunk / CPR, T - 1);
+        const size_t off = ((((size_t)b * T + m) * H + h) * D + col) * (F32IN ? 4 : 2);
+        kreg[i] = *reinterpret_cast<const u32x4*>(static_cast<const char*>(p.k) + off);
+    }
+    float4 ureg[UC];
+#pragma unroll
+    for (int i = 0; i < UC; ++i) {
+        const int chunk = tid + i * NTHR;
+        const int m = min(chunk / U4, T - 1);
+        ureg[i] = *reinterpret_cast<const float4*>(p.u + (((size_t)b * T + m) * H + h) * D + tile * BV +
+                                                   4 * (chunk % U4));
+    }
+    const int nl = min(lane, T - 1);
+    const float lp_ld = p.logp[((size_t)b * T + nl) * H + h];
+    // a chain has no parent array: read the log-gate array instead (it has at
+    // least B * T entries) and discard the value
+    const global_ptr<const int32_t> parp =
+        (global_ptr<const int32_t>)(p.parent ? p.parent : reinterpret_cast<const int32_t*>(p.logp));
+    const int par_ld = parp[(size_t)b * T + nl];
+    const global_ptr<const int32_t> posp = (global_ptr<const int32_t>)p.pos;
+    const int pos_ld = posp[(size_t)b * P + min(f0 + lane, NQT - 1) / Qn];  // position of query column `lane`
+    const int need_ld = posp[(size_t)b * P + min(tid, P - 1)];                // for the parent-row check
+    const float* s0row = p.S0 + (((size_t)b * H + h) * D + vrow0 + c) * D;
+    float4 sreg[KS][2];
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+        const int k0 = 32 * s + 4 * g;
+        sreg[s][0] = (k0 < D) ? ld_stream(s0row + k0) : make_float4(0.f, 0.f, 0.f, 0.f);
+        sreg[s][1] = (k0 + 16 < D) ? ld_stream(s0row + k0 + 16) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    asm volatile("" ::: "memory");  // keep the loads above ahead of any use of them
+
+    // 2a. stage Q, K, U (rows past the ends zero)
+    const u32x4 z4 = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int i = 0; i < QC; ++i) {
+        const int chunk = tid + i * NTHR, row = chunk / CPR, col = (chunk % CPR) * EPC;
+        if (row < NQ) {
+            const u32x4 qv = (f0 + row < NQT) ? qreg[i] : z4;
+            if constexpr (!F32IN) {
+                *reinterpret_cast<u32x4*>(s_q + row * QKLD + col) = qv;
+            } else {
+                u16x4 hi, lo;
+                split4(__builtin_bit_cast(float4, qv), hi, lo);
+                *reinterpret_cast<u16x4*>(s_q + row * QKLD + col) = hi;
+                *reinterpret_cast<u16x4*>(s_q + (NQ + row) * QKLD + col) = lo;
+            }
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < KC; ++i) {
+        const int chunk = tid + i * NTHR, row = chunk / CPR, col = (chunk % CPR) * EPC;
+        if (row < TM) {
+            const u32x4 kv = row < T ? kreg[i] : z4;
+            if constexpr (!F32IN) {
+                *reinterpret_cast<u32x4*>(s_k + row * QKLD + col) = kv;
+            } else {
+                u16x4 hi, lo;
+                split4(__builtin_bit_cast(float4, kv), hi, lo);
+                *reinterpret_cast<u16x4*>(s_k + row * QKLD + col) = hi;
+                *reinterpret_cast<u16x4*>(s_k + (TM + row) * QKLD + col) = lo;
+            }
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < UC; ++i) {
+        const int chunk = tid + i * NTHR, m = chunk / U4;
+        if (m < TM)
+            *reinterpret_cast<float4*>(s_u + m * ULD + 4 * (chunk % U4)) =
+                m < T ? ureg[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+
+    // 2b. wave 0: per-query positions, log P, ancestor-or-self masks
+    if (wave == 0) {
+        s_pos[lane] = (f0 + lane < NQT) ? pos_ld : INT_MIN;
+        const int n = lane;
+        const bool valid = n < T;
+        const int par = p.parent ? par_ld : n - 1;
+        const bool bad = valid && (par < -1 || par >= n);
+        const bool anybad = __ballot(bad) != 0ull;
+        // pointer doubling: `set` covers the path segment from n up to (not
+        // including) jmp
+        uint64_t set = valid ? (1ull << n) : 0ull;
+        int jmp = (valid && !bad) ? par : -1;
+#pragma unroll
+        for (int it = 0; it < S::LOG2TM; ++it) {
+            const int src = jmp >= 0 ? jmp : n;
+            const uint64_t set_j = shfl_u64(set, src);
+            const int jmp_j = __shfl(jmp, src, kWave);
+            if (jmp >= 0) {
+                set |= set_j;
+                jmp = jmp_j;
+            }
+        }
+        if (n < TM) {
+            s_anc[n] = set;
+            s_lp[n] = valid ? lp_ld : 0.f;
+        }
+        if (lane == 0) s_flag[0] = anybad ? 1 : 0;
+    }
+    // the parent row matters only if some valid position of the sequence is a node
+    int need = tid < P && need_ld >= 0 && need_ld < T;
+    for (int pp = tid + NTHR; pp < P; pp += NTHR) {
+        const int j = p.pos[(size_t)b * P + pp];
+        need |= (j >= 0 && j < T);
+    }
+    need = __syncthreads_or(need);  // also the barrier after staging
+    if (s_flag[0] && need) {
+        if (tid == 0 && h == 0 && tile == 0 && ch == 0 && p.status) atomicOr(p.status, LDV_STATUS_BAD_PARENT);
+        return;  // invalid parent row: nothing of the sequence is written
+    }
+
+    // 3. W[m][f] = [m on path(j_f)] (P_j / P_m) k_m . q_f, column block cb
+#pragma unroll
+    for (int cb = wave; cb < NCB; cb += NW) {
+        const int fcol = cb * 16 + c;
+        const int j = s_pos[fcol];
+        const bool node = j >= 0 && j < T;
+        const uint64_t am = node ? s_anc[j] : 0ull;
+        const float lpj = node ? s_lp[j] : 0.f;
+#pragma unroll
+        for (int mb = 0; mb < TM / 16; ++mb) {
+            floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < KS; ++s) {
+                const bf16x8 bk = frag_row<D>(s_k + (mb * 16 + c) * QKLD, s, g);
+                const bf16x8 bq = frag_row<D>(s_q + fcol * QKLD, s, g);
+                acc = mfma16x16x32(bk, bq, acc);
+                if constexpr (F32IN) {
+                    acc = mfma16x16x32(bk, frag_row<D>(s_q + (NQ + fcol) * QKLD, s, g), acc);
+                    acc = mfma16x16x32(frag_row<D>(s_k + (TM + mb * 16 + c) * QKLD, s, g), bq, acc);
+                }
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int m = mb * 16 + 4 * g + r;
+                s_w[m * WLD + fcol] = ((am >> m) & 1ull) ? expf(lpj - s_lp[m]) * acc[r] : 0.f;
+            }
+        }
+    }
+    __syncthreads();
+
+    // 4. O^T = (S0 Q^T) diag(P_j) + U^T W for the wave's 16 value rows:
+    //    lane (c, g) of column block cb holds query f0 + 16 cb + c, values
+    //    vrow0 + 4 g .. +3
+    floatx4 acc[NCB];
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) acc[cb] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+        bf16x8 sh, sl;
+        split8(sreg[s][0], sreg[s][1], sh, sl);
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) {
+            const bf16x8 bq = frag_row<D>(s_q + (cb * 16 + c) * QKLD, s, g);
+            acc[cb] = mfma16x16x32(sh, bq, acc[cb]);
+            acc[cb] = mfma16x16x32(sl, bq, acc[cb]);
+            if constexpr (F32IN) acc[cb] = mfma16x16x32(sh, frag_row<D>(s_q + (NQ + cb * 16 + c) * QKLD, s, g), acc[cb]);
+        }
+    }
+    int jcol[NCB];
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) {
+        const int j = s_pos[cb * 16 + c];
+        jcol[cb] = j;
+        const float Pj = (j >= 0 && j < T) ? expf(s_lp[j]) : 1.f;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[cb][r] *= Pj;
+    }
+#pragma unroll
+    for (int s = 0; s < NKS; ++s) {
+        const int m0 = 32 * s + 4 * g;
+        float uu[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int m = m0 + (e & 3) + (e >> 2) * 16;
+            uu[e] = m < TM ? s_u[m * ULD + wave * 16 + c] : 0.f;
+        }
+        bf16x8 uh, ul;
+        split8(make_float4(uu[0], uu[1], uu[2], uu[3]), make_float4(uu[4], uu[5], uu[6], uu[7]), uh, ul);
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) {
+            float ww[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int m = m0 + (e & 3) + (e >> 2) * 16;
+                ww[e] = m < TM ? s_w[m * WLD + cb * 16 + c] : 0.f;
+            }
+            bf16x8 wh, wl;
+            split8(make_float4(ww[0], ww[1], ww[2], ww[3]), make_float4(ww[4], ww[5], ww[6], ww[7]), wh, wl);
+            acc[cb] = mma3(acc[cb], uh, ul, wh, wl);
+        }
+    }
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) {
+        const int f = f0 + cb * 16 + c, j = jcol[cb];
+        if (f < NQT && j >= -1 && j < T) {
+            const int pp = f / Qn, ii = f - pp * Qn;
+            const size_t off = ((((size_t)b * P + pp) * H + h) * Qn + ii) * D + vrow0 + 4 * g;
+            st_stream(p.o + off, make_float4(acc[cb][0], acc[cb][1], acc[cb][2], acc[cb][3]));
+        }
+    }
+    // positions outside [-1, T-1]: reported by the blocks of head 0, tile 0
+    if (h == 0 && tile == 0 && wave == 0 && p.status) {
+        const int j = s_pos[lane];
+        const bool badp = f0 + lane < NQT && (j < -1 || j >= T);
+        if (__ballot(badp) != 0ull && lane == 0) atomicOr(p.status, LDV_STATUS_BAD_POSITION);
+    }
+}
+
+template <int D, int TM, bool F32IN>
+static hipError_t launch_t(const ReadArgs& a, hipStream_t st) {
+    using S = RShape<D, TM>;
+    const long long nch = ((long long)a.P * a.Qn + S::NQ - 1) / S::NQ;
+    const long long nblk = (long long)a.B * a.H * S::NT * nch;
+    if (nblk <= 0) return hipSuccess;
+    hipLaunchKernelGGL((read_kernel<D, TM, F32IN>), dim3((unsigned)nblk), dim3(S::NW * kWave), 0, st, a);
+    return hipGetLastError();
+}
+
+template <int D, bool F32IN>
+static hipError_t launch_d(const ReadArgs& a, hipStream_t st) {
+    if (a.T <= 16) return launch_t<D, 16, F32IN>(a, st);
+    if (a.T <= 32) return launch_t<D, 32, F32IN>(a, st);
+    return launch_t<D, 64, F32IN>(a, st);
+}
+
+template <bool F32IN>
+static hipError_t launch_f(const ReadArgs& a, hipStream_t st) {
+    switch (a.D) {
+        case 16: return launch_d<16, F32IN>(a, st);
+        case 32: return launch_d<32, F32IN>(a, st);
+        case 64: return launch_d<64, F32IN>(a, st);
+        case 128: return launch_d<128, F32IN>(a, st);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_read(const ReadArgs& a, bool f32_inputs, hipStream_t stream) {
+    return f32_inputs ? launch_f<true>(a, stream) : launch_f<false>(a, stream);
+}
+
+}  // namespace ldv

@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(_HERE, "libldv.so")
 
 LDV_OK, LDV_ERR_ARG, LDV_ERR_UNSUPPORTED, LDV_ERR_LAUNCH = 0, -1, -2, -3
 LDV_BF16, LDV_F32 = 0, 1
-STATUS_BAD_PARENT, STATUS_BAD_ACCEPTED, STATUS_BAD_SLOT = 1, 2, 4
+STATUS_BAD_PARENT, STATUS_BAD_ACCEPTED, STATUS_BAD_SLOT, STATUS_BAD_POSITION = 1, 2, 4, 8
 MAX_T = 64
 
 _lib = None
@@ -46,7 +46,9 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.ldv_verify_chain.argtypes = [i, i, i, i, i, i, vp, vp, vp, fp, fp, fp, fp, fp, fp, ip, vp]
     lib.ldv_commit_state.argtypes = [i, i, i, i, i, i, vp, fp, fp, ip, ip, fp, fp, ip, vp]
     lib.ldv_gather_states.argtypes = [i, i, i, i, i, i, i, i, fp, ip, vp, fp, fp, ip, vp]
-    for f in ("ldv_verify_tree", "ldv_verify_chain", "ldv_commit_state", "ldv_gather_states", "ldv_version"):
+    lib.ldv_read_block_states.argtypes = [i, i, i, i, i, i, i, i, vp, fp, fp, ip, fp, ip, vp, fp, ip, vp]
+    for f in ("ldv_verify_tree", "ldv_verify_chain", "ldv_commit_state", "ldv_gather_states",
+              "ldv_read_block_states", "ldv_version"):
         getattr(lib, f).restype = ctypes.c_int
     lib.ldv_status_string.argtypes = [ctypes.c_int]
     lib.ldv_status_string.restype = ctypes.c_char_p
@@ -214,6 +216,42 @@ def gather_states(pool, slot, queries=None, o=None, states_out=None, want_states
         B, P, H, dk, dv, num_slots, Qn, code, _ptr(pool), _ptr(slot), _ptr(queries), _ptr(o),
         _ptr(states_out), _ptr(status), _stream(stream)))
     return o, states_out
+
+
+def read_block_states(k, u, logp, S0, pos, queries, parent=None, o=None, status=None, stream=None):
+    """Read states inside the verified block without forming them:
+    o[b, p, h, i] = S_j q with j = pos[b, p] in [-1, T-1] (S0 for -1).
+
+    k [B, T, H, dk] (bf16/fp32) and u [B, T, H, dv], logp [B, T, H] from the
+    verify call on the same S0 [B, H, dv, dk]; pos [B, P] int32; queries
+    [B, P, H, Qn, dk] with k's dtype; parent [B, T] int32 or None (chain).
+    Returns o [B, P, H, Qn, dv] fp32."""
+    _dev(k, "k")
+    B, T, H, dk = k.shape
+    code = _qkv_code(k)
+    _dev(u, "u", torch.float32)
+    if u.dim() != 4 or tuple(u.shape[:3]) != (B, T, H):
+        raise ValueError("u must have shape [B, T, H, dv]")
+    dv = u.shape[3]
+    _dev(logp, "logp", torch.float32, (B, T, H))
+    _dev(S0, "S0", torch.float32, (B, H, dv, dk))
+    _dev(pos, "pos", torch.int32)
+    if pos.dim() != 2 or pos.shape[0] != B:
+        raise ValueError("pos must have shape [B, P]")
+    P = pos.shape[1]
+    _dev(queries, "queries", k.dtype)
+    if queries.dim() != 5 or tuple(queries.shape[:3]) != (B, P, H) or queries.shape[4] != dk:
+        raise ValueError("queries must have shape [B, P, H, Qn, dk]")
+    Qn = queries.shape[3]
+    if parent is not None:
+        _dev(parent, "parent", torch.int32, (B, T))
+    o = _opt(o, "o", torch.float32, (B, P, H, Qn, dv), k.device)
+    if status is not None:
+        _dev(status, "status", torch.int32)
+    _check("ldv_read_block_states", load().ldv_read_block_states(
+        B, T, H, dk, dv, P, Qn, code, _ptr(k), _ptr(u), _ptr(logp), _ptr(parent), _ptr(S0), _ptr(pos),
+        _ptr(queries), _ptr(o), _ptr(status), _stream(stream)))
+    return o
 
 
 def version() -> int:

@@ -92,3 +92,19 @@ def test_status_strings(lib):
     lib.ldv_status_string.restype = ctypes.c_char_p
     assert lib.ldv_status_string(0) == b"ok"
     assert b"unsupported" in lib.ldv_status_string(-2)
+
+
+def test_read_block_argument_codes(lib):
+    r = lambda **kw: lib.ldv_read_block_states(
+        kw.get("B", 1), kw.get("T", 4), 1, kw.get("d", 128), kw.get("d", 128), kw.get("P", 2), kw.get("Qn", 3),
+        kw.get("dt", 0), kw.get("k", FAKE), FAKE, FAKE, None, kw.get("S0", FAKE), kw.get("pos", FAKE),
+        kw.get("q", FAKE), kw.get("o", FAKE), None, None)
+    assert r(dt=5) == -1
+    assert r(k=None) == -1
+    assert r(pos=None) == -1
+    assert r(q=None) == -1
+    assert r(o=MIS) == -1
+    assert r(P=-1) == -1
+    assert r(T=65) == -2
+    assert r(d=24) == -2
+    assert r(B=0) == 0 and r(P=0) == 0 and r(Qn=0, q=None) == 0
