@@ -174,6 +174,37 @@ int ldv_read_block_states(int B, int T, int H, int dk, int dv, int P, int Qn, in
                           const float* S0, const int32_t* pos, const void* queries, float* o,
                           int* status, void* stream);
 
+/*
+ * Greedy selection of the accepted node, on the device.  Verification fixes
+ * the accepted prefix (ReaDy page, Fig. 2a) and only the node selected after
+ * sampling keeps its state (Bole page, summary and section IV); with greedy
+ * decoding the selection is a walk from the committed state:
+ *     target[b, r] = argmax_v logits[b, r, v]     (r = 0 .. T)
+ *     cur = -1; while some node c with parent[c] == cur has
+ *               tokens[b, c] == target[b, cur + 1]: cur = the lowest such c
+ *     accepted[b] = cur;  accepted_len[b] = nodes walked (cur's depth);
+ *     bonus[b] = target[b, cur + 1] (the target's token after the accepted node)
+ * argmax: the larger value wins, equal values go to the lower index, NaN
+ * never wins (+0 equals -0) and an all-NaN row gives 0.
+ *
+ *   logits        [B, T+1, V] element type logits_dtype (LDV_BF16 / LDV_F32);
+ *                 row 0 is the target's prediction at the committed position,
+ *                 row n+1 its prediction after draft node n
+ *   tokens        [B, T] int32 draft token of each node (any value; one
+ *                 outside [0, V) never matches)
+ *   parent        [B, T] int32 or NULL for a chain
+ *   target        [B, T+1] int32 (written: every row's argmax)
+ *   accepted      [B] int32 in [-1, T-1] (written), ready for ldv_commit_state
+ *   accepted_len, bonus  [B] int32 or NULL
+ * The logits need element alignment only.  A sequence with an invalid parent
+ * row -> LDV_STATUS_BAD_PARENT; its target row is written, its accepted,
+ * accepted_len and bonus are not.  V must be >= 1; T <= 64.
+ */
+int ldv_select_accepted(int B, int T, int V, int logits_dtype, const void* logits,
+                        const int32_t* tokens, const int32_t* parent, int32_t* target,
+                        int32_t* accepted, int32_t* accepted_len, int32_t* bonus,
+                        int* status, void* stream);
+
 /* Text for an LDV_OK / LDV_ERR_* return code (static storage). */
 const char* ldv_status_string(int code);
 

@@ -6,6 +6,7 @@ fails if it has not been built.
 """
 from .ldv import (LDV_BF16, LDV_F32, MAX_T, STATUS_BAD_ACCEPTED, STATUS_BAD_PARENT,  # noqa: F401
                   STATUS_BAD_POSITION, STATUS_BAD_SLOT, LdvError, commit_state, gather_states, load,
-                  read_block_states, status_string, verify_chain, verify_tree, version)
+                  read_block_states, select_accepted, status_string, verify_chain, verify_tree,
+                  version)
 
 load()

@@ -10,7 +10,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libldv.so")
-SOURCES = ["verify.hip", "commit.hip", "gather.hip", "read.hip", "ldv_api.hip"]
+SOURCES = ["verify.hip", "commit.hip", "gather.hip", "read.hip", "select.hip", "ldv_api.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

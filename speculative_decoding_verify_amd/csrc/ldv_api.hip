@@ -119,6 +119,25 @@ LDV_EXPORT int ldv_read_block_states(int B, int T, int H, int dk, int dv, int P,
     return e == hipSuccess ? LDV_OK : LDV_ERR_LAUNCH;
 }
 
+LDV_EXPORT int ldv_select_accepted(int B, int T, int V, int logits_dtype, const void* logits,
+                                   const int32_t* tokens, const int32_t* parent, int32_t* target,
+                                   int32_t* accepted, int32_t* accepted_len, int32_t* bonus, int* status,
+                                   void* stream) {
+    if (B < 0 || T < 0 || V <= 0) return LDV_ERR_ARG;
+    if (logits_dtype != LDV_BF16 && logits_dtype != LDV_F32) return LDV_ERR_ARG;
+    if (T > LDV_MAX_T) return LDV_ERR_UNSUPPORTED;
+    if (B == 0 || T == 0) return LDV_OK;
+    if (!logits || !tokens || !target || !accepted) return LDV_ERR_ARG;
+    if (!aligned(logits, logits_dtype == LDV_F32 ? 4 : 2) || !aligned(tokens, 4) || !aligned(parent, 4) ||
+        !aligned(target, 4) || !aligned(accepted, 4) || !aligned(accepted_len, 4) || !aligned(bonus, 4) ||
+        !aligned(status, 4))
+        return LDV_ERR_ARG;
+    if ((long long)B * (T + 1) > 0x7fffffffLL) return LDV_ERR_UNSUPPORTED;
+    ldv::SelectArgs args{B, T, V, logits, tokens, parent, target, accepted, accepted_len, bonus, status};
+    hipError_t e = ldv::launch_select(args, logits_dtype == LDV_F32, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? LDV_OK : LDV_ERR_LAUNCH;
+}
+
 LDV_EXPORT const char* ldv_status_string(int code) {
     switch (code) {
         case LDV_OK: return "ok";

@@ -56,11 +56,24 @@ struct ReadArgs {
     int* status;  // may be NULL
 };
 
+struct SelectArgs {
+    int B, T, V;
+    const void* logits;      // [B, T+1, V]
+    const int32_t* tokens;   // [B, T]
+    const int32_t* parent;   // NULL: chain
+    int32_t* target;         // [B, T+1]
+    int32_t* accepted;       // [B]
+    int32_t* accepted_len;   // may be NULL
+    int32_t* bonus;          // may be NULL
+    int* status;             // may be NULL
+};
+
 // Each launcher assumes arguments already validated by the C ABI layer and
 // returns the HIP launch status.
 hipError_t launch_verify(const VerifyArgs& a, bool f32_inputs, hipStream_t stream);
 hipError_t launch_commit(const CommitArgs& a, bool f32_k, hipStream_t stream);
 hipError_t launch_gather(const GatherArgs& a, bool f32_queries, hipStream_t stream);
 hipError_t launch_read(const ReadArgs& a, bool f32_inputs, hipStream_t stream);
+hipError_t launch_select(const SelectArgs& a, bool f32_logits, hipStream_t stream);
 
 }  // namespace ldv

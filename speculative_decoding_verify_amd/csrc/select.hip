@@ -1,0 +1,166 @@
+// Greedy accepted-node selection on the device (gfx950).
+//
+// Verification fixes the accepted prefix (ReaDy page, arXiv 2610.20503,
+// Fig. 2a) and only the state of the node selected after sampling is kept
+// (Bole page, arXiv 2608.01651, summary and section IV).  Under greedy
+// decoding that node is found by walking down from the committed state: at
+// each step the target's most likely next token (the argmax of its logits at
+// the current position) is compared with the draft tokens of the current
+// node's children, and the walk moves to the lowest-index child that
+// matches.  The result feeds ldv_commit_state with no host round trip.
+//
+// Two launches on the caller's stream:
+//   1. argmax_kernel: one workgroup per logits row (B x (T+1) rows of V
+//      values), 16-byte loads with eight in flight per thread, a per-thread
+//      running (value, index) and a wave then workgroup reduction.  The rule,
+//      identical everywhere: the larger value wins, equal values go to the
+//      lower index, NaN never wins (+0 == -0), an all-NaN row gives 0.  The
+//      comparisons are exact in fp32 (bf16 widens exactly), so the argmax
+//      does not depend on the order of the reduction.  HBM-bound: the
+//      logits are read once.
+//   2. walk_kernel: one wave per sequence; lane n holds node n's parent and
+//      token and lane r the target of row r, so each step of the walk is a
+//      shuffle and a ballot (at most T steps).
+#include <limits.h>
+
+#include "ldv_device.hpp"
+#include "ldv_kernels.hpp"
+
+#include "../../include/ldv.h"
+
+namespace ldv {
+
+constexpr int kArgThreads = 256;
+constexpr int kArgUnroll = 8;  // 16-byte loads in flight per thread
+
+// (v, i) replaces (bv, bi) when v is larger, or equal with a lower index;
+// NaN compares false both ways and never replaces.
+__device__ __forceinline__ void take_max(float v, int i, float& bv, int& bi) {
+    if (v > bv || (v == bv && i < bi)) {
+        bv = v;
+        bi = i;
+    }
+}
+
+template <bool F32>
+__device__ __forceinline__ float elem(const unsigned char* row, int i) {
+    if constexpr (F32) return reinterpret_cast<const float*>(row)[i];
+    else return bf16_val(reinterpret_cast<const unsigned short*>(row)[i]);
+}
+
+template <bool F32>
+__global__ __launch_bounds__(kArgThreads) void argmax_kernel(const SelectArgs p) {
+    constexpr int ES = F32 ? 4 : 2;    // bytes per element
+    constexpr int EPC = 16 / ES;       // elements per 16-byte chunk
+    constexpr int STEP = kArgThreads * kArgUnroll;
+    __shared__ float s_v[kArgThreads / kWave];
+    __shared__ int s_i[kArgThreads / kWave];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int V = p.V;
+    const size_t row = blockIdx.x;
+    const unsigned char* base = static_cast<const unsigned char*>(p.logits) + row * (size_t)V * ES;
+    // elements up to the first 16-byte boundary of the row, 16-byte chunks,
+    // then the elements past the last whole chunk
+    const int mis = (int)((reinterpret_cast<uintptr_t>(base) & 15) / ES);
+    const int head = mis ? min(EPC - mis, V) : 0;
+    const int nbody = (V - head) / EPC;
+    const int tail0 = head + nbody * EPC;
+
+    float bv = -__builtin_inff();
+    int bi = INT_MAX;
+    if (tid < head) take_max(elem<F32>(base, tid), tid, bv, bi);
+    const global_ptr<const u32x4> body = (global_ptr<const u32x4>)(base + (size_t)head * ES);
+    for (int c0 = 0; c0 < nbody; c0 += STEP) {
+        u32x4 r[kArgUnroll];
+#pragma unroll
+        for (int u = 0; u < kArgUnroll; ++u) r[u] = body[min(c0 + tid + u * kArgThreads, nbody - 1)];
+#pragma unroll
+        for (int u = 0; u < kArgUnroll; ++u) {
+            const int cidx = c0 + tid + u * kArgThreads;
+            if (cidx < nbody) {
+                const int i0 = head + cidx * EPC;
+                if constexpr (F32) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) take_max(__uint_as_float(r[u][e]), i0 + e, bv, bi);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        take_max(__uint_as_float(r[u][e] << 16), i0 + 2 * e, bv, bi);
+                        take_max(__uint_as_float(r[u][e] & 0xffff0000u), i0 + 2 * e + 1, bv, bi);
+                    }
+                }
+            }
+        }
+    }
+    for (int i = tail0 + tid; i < V; i += kArgThreads) take_max(elem<F32>(base, i), i, bv, bi);
+
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        const float ov = __shfl_xor(bv, off, kWave);
+        const int oi = __shfl_xor(bi, off, kWave);
+        take_max(ov, oi, bv, bi);
+    }
+    if (lane == 0) {
+        s_v[wave] = bv;
+        s_i[wave] = bi;
+    }
+    __syncthreads();
+    if (tid == 0) {
+#pragma unroll
+        for (int w = 1; w < kArgThreads / kWave; ++w) take_max(s_v[w], s_i[w], bv, bi);
+        p.target[row] = bi == INT_MAX ? 0 : bi;  // a row of NaN: 0
+    }
+}
+
+__global__ __launch_bounds__(256) void walk_kernel(const SelectArgs p) {
+    const int lane = threadIdx.x & 63;
+    const int b = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (b >= p.B) return;  // whole waves
+    const int T = p.T;
+    const int n = lane;
+    const bool valid = n < T;
+    const int nl = min(n, T - 1);
+    const int par = p.parent ? p.parent[(size_t)b * T + nl] : n - 1;
+    const int tok = p.tokens[(size_t)b * T + nl];
+    const int32_t* trow = p.target + (size_t)b * (T + 1);
+    const int tgt = trow[min(n, T)];  // target of row n (rows 0 .. 63)
+    const int tgt_last = trow[T];     // row T (the only row past 63 when T = 64)
+    if (__ballot(valid && (par < -1 || par >= n)) != 0ull) {
+        if (lane == 0 && p.status) atomicOr(p.status, LDV_STATUS_BAD_PARENT);
+        return;  // outputs of the sequence left unwritten
+    }
+    int cur = -1, len = 0;
+    for (int it = 0; it < T; ++it) {  // a path has at most T nodes
+        const int r = cur + 1;
+        const int sh = __shfl(tgt, r & 63, kWave);
+        const int want = r < 64 ? sh : tgt_last;
+        const uint64_t m = __ballot(valid && par == cur && tok == want);
+        if (m == 0ull) break;
+        cur = __builtin_ctzll(m);
+        ++len;
+    }
+    const int r = cur + 1;
+    const int sh = __shfl(tgt, r & 63, kWave);
+    const int bonus = r < 64 ? sh : tgt_last;
+    if (lane == 0) {
+        p.accepted[b] = cur;
+        if (p.accepted_len) p.accepted_len[b] = len;
+        if (p.bonus) p.bonus[b] = bonus;
+    }
+}
+
+hipError_t launch_select(const SelectArgs& a, bool f32_logits, hipStream_t stream) {
+    const long long rows = (long long)a.B * (a.T + 1);
+    if (rows <= 0) return hipSuccess;
+    if (f32_logits)
+        hipLaunchKernelGGL(argmax_kernel<true>, dim3((unsigned)rows), dim3(kArgThreads), 0, stream, a);
+    else
+        hipLaunchKernelGGL(argmax_kernel<false>, dim3((unsigned)rows), dim3(kArgThreads), 0, stream, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(walk_kernel, dim3((unsigned)((a.B + 3) / 4)), dim3(256), 0, stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace ldv

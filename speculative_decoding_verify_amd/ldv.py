@@ -47,8 +47,9 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.ldv_commit_state.argtypes = [i, i, i, i, i, i, vp, fp, fp, ip, ip, fp, fp, ip, vp]
     lib.ldv_gather_states.argtypes = [i, i, i, i, i, i, i, i, fp, ip, vp, fp, fp, ip, vp]
     lib.ldv_read_block_states.argtypes = [i, i, i, i, i, i, i, i, vp, fp, fp, ip, fp, ip, vp, fp, ip, vp]
+    lib.ldv_select_accepted.argtypes = [i, i, i, i, vp, ip, ip, ip, ip, ip, ip, ip, vp]
     for f in ("ldv_verify_tree", "ldv_verify_chain", "ldv_commit_state", "ldv_gather_states",
-              "ldv_read_block_states", "ldv_version"):
+              "ldv_read_block_states", "ldv_select_accepted", "ldv_version"):
         getattr(lib, f).restype = ctypes.c_int
     lib.ldv_status_string.argtypes = [ctypes.c_int]
     lib.ldv_status_string.restype = ctypes.c_char_p
@@ -252,6 +253,36 @@ def read_block_states(k, u, logp, S0, pos, queries, parent=None, o=None, status=
         B, T, H, dk, dv, P, Qn, code, _ptr(k), _ptr(u), _ptr(logp), _ptr(parent), _ptr(S0), _ptr(pos),
         _ptr(queries), _ptr(o), _ptr(status), _stream(stream)))
     return o
+
+
+def select_accepted(logits, tokens, parent=None, target=None, accepted=None, accepted_len=None,
+                    bonus=None, status=None, stream=None):
+    """Greedy accepted-node selection on the device.
+
+    logits [B, T+1, V] bf16/fp32 (row 0: the committed position, row n+1:
+    after node n); tokens [B, T] int32; parent [B, T] int32 or None (chain).
+    Returns (target [B, T+1], accepted [B], accepted_len [B], bonus [B]),
+    all int32."""
+    _dev(logits, "logits")
+    if logits.dim() != 3:
+        raise ValueError("logits must have shape [B, T+1, V]")
+    B, T1, V = logits.shape
+    T = T1 - 1
+    code = _qkv_code(logits)
+    _dev(tokens, "tokens", torch.int32, (B, T))
+    if parent is not None:
+        _dev(parent, "parent", torch.int32, (B, T))
+    dev = logits.device
+    target = _opt(target, "target", torch.int32, (B, T1), dev)
+    accepted = _opt(accepted, "accepted", torch.int32, (B,), dev)
+    accepted_len = _opt(accepted_len, "accepted_len", torch.int32, (B,), dev)
+    bonus = _opt(bonus, "bonus", torch.int32, (B,), dev)
+    if status is not None:
+        _dev(status, "status", torch.int32)
+    _check("ldv_select_accepted", load().ldv_select_accepted(
+        B, T, V, code, _ptr(logits), _ptr(tokens), _ptr(parent), _ptr(target), _ptr(accepted),
+        _ptr(accepted_len), _ptr(bonus), _ptr(status), _stream(stream)))
+    return target, accepted, accepted_len, bonus
 
 
 def version() -> int:

@@ -108,3 +108,16 @@ def test_read_block_argument_codes(lib):
     assert r(T=65) == -2
     assert r(d=24) == -2
     assert r(B=0) == 0 and r(P=0) == 0 and r(Qn=0, q=None) == 0
+
+
+def test_select_argument_codes(lib):
+    s = lambda **kw: lib.ldv_select_accepted(
+        kw.get("B", 2), kw.get("T", 4), kw.get("V", 100), kw.get("dt", 0), kw.get("lg", FAKE),
+        kw.get("tok", FAKE), None, kw.get("tg", FAKE), kw.get("acc", FAKE), None, None, None, None)
+    assert s(V=0) == -1
+    assert s(dt=9) == -1
+    assert s(lg=None) == -1 and s(tok=None) == -1 and s(tg=None) == -1 and s(acc=None) == -1
+    assert s(lg=ctypes.c_void_p(0x10001)) == -1       # not element aligned
+    assert s(dt=1, lg=ctypes.c_void_p(0x10002)) == -1
+    assert s(T=65) == -2
+    assert s(B=0) == 0 and s(T=0) == 0

@@ -1,0 +1,142 @@
+"""HIP greedy accepted-node selection against the oracle: every output is an
+index, so every comparison is exact."""
+import json
+import os
+
+import numpy as np
+import pytest
+
+from gpu_util import dev
+from workloads import (WORKLOADS, bf16_round, make_chain, make_inputs, make_select_inputs, make_tree)
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+@pytest.fixture(scope="module")
+def ldv():
+    import speculative_decoding_verify_amd as m
+    return m
+
+
+def run(ldv, logits, tokens, parent, dtype):
+    st = torch.zeros(1, dtype=torch.int32, device="cuda")
+    lg = dev(logits).to(torch.bfloat16 if dtype == "bf16" else torch.float32)
+    out = ldv.select_accepted(lg, dev(tokens), None if parent is None else dev(parent), status=st)
+    torch.cuda.synchronize()
+    return [t.cpu().numpy() for t in out], int(st.item())
+
+
+def compare(orc, ldv, logits, tokens, parent, dtype, name):
+    (tg, acc, alen, bonus), st = run(ldv, logits, tokens, parent, dtype)
+    rt, racc, ralen, rbonus, rs = orc.select(logits, tokens, parent)
+    assert st == rs == 0
+    assert np.array_equal(tg, rt), name + ": target"
+    assert np.array_equal(acc, racc), name + ": accepted"
+    assert np.array_equal(alen, ralen), name + ": accepted_len"
+    assert np.array_equal(bonus, rbonus), name + ": bonus"
+    print("%-32s accepted len mean %.2f" % (name, float(np.mean(alen))), flush=True)
+
+
+def test_select_golden(ldv, orc):
+    with open(os.path.join(GOLDEN, "select_forest6_handworked.json")) as f:
+        g = json.load(f)
+    logits = np.array([[float(x) for x in row] for row in g["logits"]], dtype=np.float32)[None]
+    tokens = np.array([g["tokens"]], dtype=np.int32)
+    par = np.array([g["parent"]], dtype=np.int32)
+    for dt in ("f32", "bf16"):   # every value of the example is exact in bf16
+        (tg, acc, alen, bonus), st = run(ldv, logits, tokens, par, dt)
+        assert st == 0
+        assert tg[0].tolist() == g["target"]
+        assert (int(acc[0]), int(alen[0]), int(bonus[0])) == (g["accepted"], g["accepted_len"], g["bonus"])
+
+
+GRID = [  # B, T, V, dtype, topology, value kind
+    (5, 12, 4, "f32", "tree", "ties"),
+    (6, 12, 5, "bf16", "tree", "ties"),
+    (7, 64, 1000, "bf16", "tree", "normal"),
+    (3, 64, 37, "bf16", "chain", "ties"),        # odd V: rows start off a 16-byte boundary
+    (3, 9, 1, "f32", "chain", "normal"),         # V = 1
+    (4, 30, 50003, "f32", "tree", "normal"),
+    (2, 16, 151936, "bf16", "chain", "normal"),
+    (5, 20, 777, "f32", "tree", "specials"),      # NaN, +-inf, signed zeros
+]
+
+
+@pytest.mark.parametrize("B,T,V,dtype,topology,kind", GRID, ids=lambda v: str(v))
+def test_select_grid(ldv, orc, B, T, V, dtype, topology, kind):
+    rng = np.random.default_rng(7000 + B * T + V)
+    par = make_chain(B, T) if topology == "chain" else make_tree(rng, B, T, 6, 3)
+    tokens = rng.integers(0, V, size=(B, T)).astype(np.int32)
+    if kind == "ties":
+        logits = rng.integers(-2, 3, size=(B, T + 1, V)).astype(np.float32)
+    else:
+        logits = rng.standard_normal((B, T + 1, V)).astype(np.float32)
+    if kind == "specials":
+        m = rng.random(logits.shape)
+        logits[m < 0.05] = np.nan
+        logits[(m >= 0.05) & (m < 0.07)] = -np.inf
+        logits[(m >= 0.07) & (m < 0.08)] = np.inf
+        logits[(m >= 0.08) & (m < 0.1)] = -0.0
+        logits[0, 1] = np.nan               # a row of NaN
+        logits[1, 0] = -np.inf              # a row of -inf
+    # agree with a random root path so that walks go deep
+    for b in range(B):
+        n = int(rng.integers(0, T))
+        path = []
+        while n >= 0:
+            path.append(n)
+            n = int(par[b, n])
+        for n in path:
+            if kind != "ties" or rng.random() < 0.7:
+                logits[b, int(par[b, n]) + 1, tokens[b, n]] = 9.0
+    if dtype == "bf16":  # (special values only appear with fp32 logits)
+        logits = bf16_round(logits)
+    compare(orc, ldv, logits, tokens, par if topology == "tree" else None, dtype,
+            "select B%d T%d V%d %s %s %s" % (B, T, V, dtype, topology, kind))
+    if topology == "chain":  # an explicit chain parent row gives the same result
+        compare(orc, ldv, logits, tokens, par, dtype, "select explicit chain")
+
+
+@pytest.mark.parametrize("key", ["hybrid27b-chain-gather", "tree64", "gdn1.3b-chain"])
+def test_select_workload_full_size(ldv, orc, key):
+    wl = WORKLOADS[key]
+    x = make_inputs(wl, with_gather=False)
+    s = make_select_inputs(wl, x["parent"], x["accepted"])
+    compare(orc, ldv, s["logits"], s["tokens"], x["parent"] if wl.topology == "tree" else None, wl.qkv,
+            "select " + key)
+
+
+def test_select_bad_parent(ldv, orc):
+    rng = np.random.default_rng(7100)
+    logits = rng.standard_normal((3, 6, 50)).astype(np.float32)
+    tokens = np.argmax(logits[:, :5], axis=-1).astype(np.int32)
+    par = make_chain(3, 5)
+    par[1, 3] = 3
+    (tg, acc, alen, bonus), st = run(ldv, logits, tokens, par, "f32")
+    assert st == ldv.STATUS_BAD_PARENT
+    assert np.array_equal(tg, np.argmax(logits, axis=-1))
+    rt, racc, _, _, rs = orc.select(logits, tokens, par)
+    assert rs == 1 and acc[0] == racc[0] == 4 and acc[2] == racc[2] == 4
+
+
+def test_select_then_commit(ldv, orc):
+    """Selection feeds commit on the device: the committed state is the
+    oracle's walk state at the oracle's selected node."""
+    wl = WORKLOADS["tree64"].replace(B=6, H=4, V=3000, seed=31)
+    x = make_inputs(wl, with_gather=False)
+    s = make_select_inputs(wl, x["parent"], x["accepted"])
+    q, k, v = (dev(x[n]).to(torch.bfloat16) for n in ("q", "k", "v"))
+    a, beta, S0, par = dev(x["a"]), dev(x["beta"]), dev(x["S0"]), dev(x["parent"])
+    _, u, logp = ldv.verify_tree(q, k, v, a, beta, S0, par)
+    _, acc, _, _ = ldv.select_accepted(dev(s["logits"]).to(torch.bfloat16), dev(s["tokens"]), par)
+    S = ldv.commit_state(k, u, logp, acc, S0, parent=par)
+    torch.cuda.synchronize()
+    _, racc, _, _, _ = orc.select(s["logits"], s["tokens"], x["parent"])
+    assert np.array_equal(acc.cpu().numpy(), racc)
+    ref, st = orc.commit(x["k"], x["v"], x["a"], x["beta"], x["S0"], racc, x["parent"])
+    assert st == 0
+    from gpu_util import check
+    check("select -> commit", S, ref)
