@@ -4,14 +4,23 @@ One step = ldv_verify_chain / ldv_verify_tree over every draft node of the
 batch, ldv_commit_state of the accepted node (in place), and, for workloads
 with drafter reads, ldv_gather_states (o = S q for every query) - one pass of
 the whole path over one batch of seeded synthetic inputs already resident in
-HBM.  Each kernel is bracketed by HIP events (created without the
-system-scope fence) on the stream it runs on, inside the timed region, so
-the per-kernel durations come from the same run.
+HBM.  Buffer sets are rotated (at least 4, at least 1 GB in all) so that the
+256 MB Infinity Cache cannot hold a step's working set.
+
+Timing uses HIP events created without the system-scope fence, recorded on
+the stream the library launches on.  The timed region is K steps captured in
+one HIP graph and replayed once (--eager: launched from Python instead; the
+Python launch cost then dominates the small workloads).  Per-kernel
+durations come from K back-to-back launches of that kernel alone in one
+graph, the median of 5 replays; they include the two steps around verify
+(ldv_read_block_states at 4 in-block positions x 16 queries per sequence,
+and ldv_select_accepted on target logits [B, T+1, V]; --no-next skips them).
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu]
 
 Prints one JSON line.  --gpus N with N > 1 is refused: this path runs on one
-GPU (every (sequence, head) is independent; see the design doc for how it shards).
+GPU (every (sequence, head) is independent, so batch or head sharding needs
+no exchange inside the path).
 """
 from __future__ import annotations
 
@@ -26,13 +35,13 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-from workloads import WORKLOADS, make_inputs, tree_depths  # noqa: E402
+from workloads import (WORKLOADS, make_block_read_inputs, make_inputs, make_select_inputs,  # noqa: E402
+                       tree_depths)
 
 METRIC = "verified draft nodes/sec (B*H*N) on MFMA; commit+gather HBM GB/s vs peak"
 DEFAULT_WORKLOAD = "hybrid27b-chain-gather"
 HBM_PEAK_GBS = 8000.0      # MI355X HBM3E, AMD published
 BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, AMD published
-NSETS = 3                  # rotated verify/commit buffer sets (defeats the 256 MB MALL)
 
 
 def algorithmic(wl, x):
@@ -53,6 +62,16 @@ def algorithmic(wl, x):
     if wl.P > 0:
         gather_bytes = B * wl.P * H * (D * D * 4 + wl.Qn * D * esz + wl.Qn * D * 4) + B * wl.P * 4
     return dict(verify=verify_bytes, verify_flops=verify_flops, commit=commit_bytes, gather=gather_bytes)
+
+
+def algorithmic_next(wl, P, Qn):
+    """Algorithmic bytes per launch of the in-block read and the selection."""
+    B, H, D, T = wl.B, wl.H, wl.D, wl.T
+    esz = 2 if wl.qkv == "bf16" else 4
+    tree = B * T * 4 if wl.topology == "tree" else 0
+    read = B * H * (D * D * 4 + T * (D * esz + D * 4 + 4) + P * Qn * (D * esz + D * 4)) + B * P * 4 + tree
+    sel = B * (T + 1) * wl.V * esz + B * T * 4 + tree + B * (T + 1) * 4 + 3 * B * 4
+    return read, sel
 
 
 def cpu_baseline(wl, x, seconds_min=10.0, seconds_cap=30.0):
@@ -144,6 +163,98 @@ def traffic_from_profiles(kernel_name, src_files):
     return ent.get("bytes_per_launch")
 
 
+def set_bytes(wl):
+    """Bytes of one rotated verify/commit buffer set (inputs and outputs)."""
+    esz = 2 if wl.qkv == "bf16" else 4
+    return wl.B * wl.H * wl.D * wl.D * 4 + wl.B * wl.T * wl.H * (3 * wl.D * esz + 2 * wl.D * 4 + 12)
+
+
+class Runner:
+    """Buffers and launch functions of the path on one workload; launch i
+    uses buffer set i mod nsets."""
+
+    def __init__(self, ldv, torch, wl, x, nsets, next_rows):
+        self.ldv, self.torch, self.wl = ldv, torch, wl
+        self.chain = wl.topology == "chain"
+        dt = torch.bfloat16 if wl.qkv == "bf16" else torch.float32
+        cuda = lambda a, t=None: (torch.from_numpy(np.ascontiguousarray(a)).cuda() if t is None
+                                  else torch.from_numpy(np.ascontiguousarray(a)).cuda().to(t))
+        base = dict(q=cuda(x["q"], dt), k=cuda(x["k"], dt), v=cuda(x["v"], dt), a=cuda(x["a"]),
+                    beta=cuda(x["beta"]), S0=cuda(x["S0"]), parent=cuda(x["parent"]), acc=cuda(x["accepted"]))
+        self.sets = []
+        for i in range(nsets):
+            st = {n: t.clone() for n, t in base.items()}
+            st["o"] = torch.empty((wl.B, wl.T, wl.H, wl.D), device="cuda")
+            st["u"] = torch.empty((wl.B, wl.T, wl.H, wl.D), device="cuda")
+            st["logp"] = torch.empty((wl.B, wl.T, wl.H), device="cuda")
+            self.sets.append(st)
+        del base
+        self.status = torch.zeros(1, dtype=torch.int32, device="cuda")
+        if wl.P > 0:
+            self.pool = cuda(x["pool"])
+            self.slot = cuda(x["slot"])
+            self.queries = cuda(x["queries"], dt)
+            self.go = torch.empty((wl.B, wl.P, wl.H, wl.Qn, wl.D), device="cuda")
+        self.next = None
+        if next_rows:
+            r = make_block_read_inputs(wl)
+            self.P2, self.Qn2 = r["pos"].shape[1], r["queries"].shape[3]
+            self.pos, self.rq = cuda(r["pos"]), cuda(r["queries"], dt)
+            self.ro = torch.empty((wl.B, self.P2, wl.H, self.Qn2, wl.D), device="cuda")
+            self.logits = []
+            if wl.V > 0:
+                sel = make_select_inputs(wl, x["parent"], x["accepted"])
+                lb = sel["logits"].size * (2 if wl.qkv == "bf16" else 4)
+                nlog = int(min(nsets, max(4, -(-1_000_000_000 // lb))))
+                self.logits = [cuda(sel["logits"], dt) for _ in range(nlog)]
+                self.tokens = cuda(sel["tokens"])
+                del sel
+                self.sel_out = [torch.empty((wl.B, wl.T + 1), dtype=torch.int32, device="cuda")] + \
+                               [torch.empty((wl.B,), dtype=torch.int32, device="cuda") for _ in range(3)]
+
+    def verify(self, i):
+        s = self.sets[i % len(self.sets)]
+        if self.chain:
+            self.ldv.verify_chain(s["q"], s["k"], s["v"], s["a"], s["beta"], s["S0"], o=s["o"], u=s["u"],
+                                  logp=s["logp"], status=self.status)
+        else:
+            self.ldv.verify_tree(s["q"], s["k"], s["v"], s["a"], s["beta"], s["S0"], s["parent"], o=s["o"],
+                                 u=s["u"], logp=s["logp"], status=self.status)
+
+    def commit(self, i):
+        s = self.sets[i % len(self.sets)]
+        self.ldv.commit_state(s["k"], s["u"], s["logp"], s["acc"], s["S0"], S_out=s["S0"],
+                              parent=None if self.chain else s["parent"], status=self.status)
+
+    def gather(self, i):
+        self.ldv.gather_states(self.pool, self.slot, self.queries, o=self.go, status=self.status)
+
+    def read(self, i):
+        s = self.sets[i % len(self.sets)]
+        self.ldv.read_block_states(s["k"], s["u"], s["logp"], s["S0"], self.pos, self.rq,
+                                   parent=None if self.chain else s["parent"], o=self.ro, status=self.status)
+
+    def select(self, i):
+        s = self.sets[i % len(self.sets)]
+        t, a, l, b = self.sel_out
+        self.ldv.select_accepted(self.logits[i % len(self.logits)], self.tokens,
+                                 None if self.chain else s["parent"], target=t, accepted=a, accepted_len=l,
+                                 bonus=b, status=self.status)
+
+    def step_fns(self):
+        return [self.verify, self.commit] + ([self.gather] if self.wl.P > 0 else [])
+
+
+def capture(torch, fns, K):
+    """One HIP graph holding K launches of each function in fns, in order."""
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(K):
+            for fn in fns:
+                fn(i)
+    return g
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -151,14 +262,18 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-next", action="store_true", help="skip timing the in-block read and the selection")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum CPU-oracle time")
+    ap.add_argument("--repeats", type=int, default=5, help="timed replays of each per-kernel graph")
+    ap.add_argument("--eager", action="store_true",
+                    help="launch from Python each step instead of replaying HIP graphs (for profilers)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES bytes (5 times), to scale "
                          "rocprofv3 FETCH_SIZE / WRITE_SIZE counters, and print its bandwidth")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path "
-              "(each (sequence, head) is independent; sharding is described in DESIGN.md).",
+              "(each (sequence, head) is independent, so the batch or the heads shard with no exchange).",
               file=sys.stderr)
         sys.exit(2)
 
@@ -181,89 +296,84 @@ def main():
     import speculative_decoding_verify_amd as ldv
 
     wl = WORKLOADS[args.workload]
-    chain = wl.topology == "chain"
-    print("[bench] generating %s inputs" % wl.key, file=sys.stderr, flush=True)
-    x = make_inputs(wl)
-    dt = torch.bfloat16 if wl.qkv == "bf16" else torch.float32
-    cuda = lambda a, t=None: (torch.from_numpy(np.ascontiguousarray(a)).cuda() if t is None
-                              else torch.from_numpy(np.ascontiguousarray(a)).cuda().to(t))
-    base = dict(q=cuda(x["q"], dt), k=cuda(x["k"], dt), v=cuda(x["v"], dt), a=cuda(x["a"]),
-                beta=cuda(x["beta"]), S0=cuda(x["S0"]), parent=cuda(x["parent"]), acc=cuda(x["accepted"]))
-    sets = []
-    for i in range(NSETS):
-        s = {n: t.clone() for n, t in base.items()}
-        s["o"] = torch.empty((wl.B, wl.T, wl.H, wl.D), device="cuda")
-        s["u"] = torch.empty((wl.B, wl.T, wl.H, wl.D), device="cuda")
-        s["logp"] = torch.empty((wl.B, wl.T, wl.H), device="cuda")
-        sets.append(s)
-    del base
-    if wl.P > 0:
-        pool = cuda(x["pool"])
-        slot = cuda(x["slot"])
-        queries = cuda(x["queries"], dt)
-        go = torch.empty((wl.B, wl.P, wl.H, wl.Qn, wl.D), device="cuda")
-    status = torch.zeros(1, dtype=torch.int32, device="cuda")
-    stream = torch.cuda.current_stream()
-    sh = stream.cuda_stream  # the stream the library launches on
-    hev = HipEvents()
-
-    def step(i, ev=None):
-        s = sets[i % NSETS]
-        if ev is not None:
-            hev.record(ev[0], sh)
-        if chain:
-            ldv.verify_chain(s["q"], s["k"], s["v"], s["a"], s["beta"], s["S0"], o=s["o"], u=s["u"],
-                             logp=s["logp"], status=status)
-        else:
-            ldv.verify_tree(s["q"], s["k"], s["v"], s["a"], s["beta"], s["S0"], s["parent"], o=s["o"],
-                            u=s["u"], logp=s["logp"], status=status)
-        if ev is not None:
-            hev.record(ev[1], sh)
-        ldv.commit_state(s["k"], s["u"], s["logp"], s["acc"], s["S0"], S_out=s["S0"],
-                         parent=None if chain else s["parent"], status=status)
-        if ev is not None:
-            hev.record(ev[2], sh)
-        if wl.P > 0:
-            ldv.gather_states(pool, slot, queries, o=go, status=status)
-        if ev is not None:
-            hev.record(ev[3], sh)
-
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    assert int(status.item()) == 0, "device status %d" % int(status.item())
-
     K = args.steps
-    evs = [[hev.create() for _ in range(4)] for _ in range(K)]
+    nsets = int(min(64, max(4, -(-1_000_000_000 // set_bytes(wl)))))
+    print("[bench] generating %s inputs (%d rotated buffer sets)" % (wl.key, nsets), file=sys.stderr, flush=True)
+    x = make_inputs(wl)
+    run = Runner(ldv, torch, wl, x, nsets, not args.no_next)
+    hev = HipEvents()
+    sh = torch.cuda.current_stream().cuda_stream  # the stream the library launches on (outside capture)
+
+    def timed(fn_replay):
+        e0, e1 = hev.create(), hev.create()
+        hev.record(e0, sh)
+        fn_replay()
+        hev.record(e1, sh)
+        torch.cuda.synchronize()
+        t = hev.elapsed_s(e0, e1)
+        hev.destroy(e0)
+        hev.destroy(e1)
+        return t
+
+    fns = run.step_fns()
+    for i in range(args.warmup):
+        for fn in fns:
+            fn(i)
+    torch.cuda.synchronize()
+    assert int(run.status.item()) == 0, "device status %d" % int(run.status.item())
+
+    # the timed region: K steps (one HIP graph, or K eager steps)
+    if args.eager:
+        replay = lambda: [fn(i) for i in range(K) for fn in fns]
+    else:
+        g_step = capture(torch, fns, K)
+        g_step.replay()  # untimed: first replay uploads the graph
+        replay = g_step.replay
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(K):
-        step(i, evs[i])
-    torch.cuda.synchronize()
+    t_total = timed(replay)
     wall = time.perf_counter() - t0
-    t_ver = np.array([hev.elapsed_s(evs[i][0], evs[i][1]) for i in range(K)])
-    t_com = np.array([hev.elapsed_s(evs[i][1], evs[i][2]) for i in range(K)])
-    t_gat = np.array([hev.elapsed_s(evs[i][2], evs[i][3]) for i in range(K)])
-    t_total = hev.elapsed_s(evs[0][0], evs[K - 1][3])
-    for e in (e for row in evs for e in row):
-        hev.destroy(e)
     ms_per_step = t_total / K * 1e3
     nodes = wl.B * wl.H * wl.T
     value = nodes * K / t_total
 
+    # per-kernel durations: K back-to-back launches of one kernel in one
+    # graph (rotating buffer sets), median of `repeats` timed replays
+    def per_kernel(fn):
+        if args.eager:
+            rep = lambda: [fn(i) for i in range(K)]
+        else:
+            g = capture(torch, [fn], K)
+            g.replay()
+            rep = g.replay
+        torch.cuda.synchronize()
+        ts = [timed(rep) / K for _ in range(args.repeats)]
+        return float(np.median(ts)), float(np.min(ts)), float(np.max(ts))
+
     alg = algorithmic(wl, x)
     kern = {}
-    for name, t, by in (("verify", t_ver, alg["verify"]), ("commit", t_com, alg["commit"]),
-                        ("gather", t_gat, alg["gather"])):
-        if name == "gather" and wl.P == 0:
-            continue
-        m = float(np.mean(t))
-        kern[name] = {"us_mean": m * 1e6, "us_median": float(np.median(t)) * 1e6,
-                      "alg_bytes": int(by), "GB_s": by / m / 1e9, "hbm_frac": by / m / 1e9 / HBM_PEAK_GBS}
-    kern["verify"]["nodes_per_s"] = nodes / kern["verify"]["us_mean"] * 1e6
+    names = [("verify", run.verify, alg["verify"]), ("commit", run.commit, alg["commit"])]
+    if wl.P > 0:
+        names.append(("gather", run.gather, alg["gather"]))
+    if not args.no_next:
+        read_bytes, sel_bytes = algorithmic_next(wl, run.P2, run.Qn2)
+        names.append(("read_block", run.read, read_bytes))
+        if wl.V > 0:
+            names.append(("select", run.select, sel_bytes))
+    for name, fn, by in names:
+        med, lo, hi = per_kernel(fn)
+        kern[name] = {"us": med * 1e6, "us_min": lo * 1e6, "us_max": hi * 1e6, "launches": K,
+                      "alg_bytes": int(by), "GB_s": by / med / 1e9, "hbm_frac": by / med / 1e9 / HBM_PEAK_GBS}
+    assert int(run.status.item()) == 0, "device status %d" % int(run.status.item())
+    kern["verify"]["nodes_per_s"] = nodes / kern["verify"]["us"] * 1e6
     kern["verify"]["alg_flops"] = alg["verify_flops"]
-    kern["verify"]["mfma_frac"] = alg["verify_flops"] / (kern["verify"]["us_mean"] * 1e-6) / (BF16_PEAK_TFLOPS * 1e12)
-    dom = max(kern, key=lambda n: kern[n]["us_mean"])
+    kern["verify"]["mfma_frac"] = alg["verify_flops"] / (kern["verify"]["us"] * 1e-6) / (BF16_PEAK_TFLOPS * 1e12)
+    if "read_block" in kern:
+        kern["read_block"].update({"P": run.P2, "Qn": run.Qn2})
+    if "select" in kern:
+        kern["select"].update({"V": wl.V, "logits": wl.qkv})
+    step_names = [n for n in ("verify", "commit", "gather") if n in kern]
+    dom = max(step_names, key=lambda n: kern[n]["us"])
     srcs = {"verify": "speculative_decoding_verify_amd/csrc/verify.hip",
             "commit": "speculative_decoding_verify_amd/csrc/commit.hip",
             "gather": "speculative_decoding_verify_amd/csrc/gather.hip"}
@@ -283,7 +393,8 @@ def main():
         "config": {"workload": wl.key, "B": wl.B, "H": wl.H, "d_k": wl.D, "d_v": wl.D, "T": wl.T,
                    "topology": wl.topology, "qkv": wl.qkv, "state": "f32",
                    "gather": ({"P": wl.P, "Qn": wl.Qn, "pool_slots": wl.B * wl.R} if wl.P else None),
-                   "step": "verify+commit" + ("+gather" if wl.P else ""), "rotated_sets": NSETS},
+                   "step": "+".join(step_names), "rotated_sets": nsets,
+                   "timing": "eager launches" if args.eager else "HIP graph replay"},
         "kernels": kern,
         "roofline": roof,
         "cpu_baseline": cpu,

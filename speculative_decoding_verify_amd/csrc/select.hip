@@ -30,7 +30,7 @@
 
 namespace ldv {
 
-constexpr int kArgThreads = 256;
+constexpr int kArgThreads = 512;
 constexpr int kArgUnroll = 8;  // 16-byte loads in flight per thread
 
 // (v, i) replaces (bv, bi) when v is larger, or equal with a lower index;

@@ -39,7 +39,7 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     p = path or LIB_PATH
     if not os.path.exists(p):
         raise ImportError("libldv.so not found at %s: build it with "
-                          "`python -c 'import __graft_entry__ as g; g.build()'`" % p)
+                          "`python speculative_decoding_verify_amd/build.py`" % p)
     lib = ctypes.CDLL(p)
     i, vp, fp, ip = ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p
     lib.ldv_verify_tree.argtypes = [i, i, i, i, i, i, vp, vp, vp, fp, fp, fp, ip, fp, fp, fp, ip, vp]
