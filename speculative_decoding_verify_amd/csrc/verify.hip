@@ -25,12 +25,12 @@
 //      loads stay in flight through steps 2-4;
 //   2. stage Q, K (bf16) in LDS; wave 0 turns the parent row into ancestor
 //      masks and log P by pointer doubling;
-//   3. 16 x 16 blocks of Q K^T and K K^T on MFMA, masked and decay-scaled
-//      into C and G; the diagonal blocks of X are solved by forward
-//      substitution in registers, reading G from the MFMA accumulators with
-//      readlane;
+//   3. 16 x 16 blocks of K K^T on MFMA, masked and decay-scaled into G;
+//      the diagonal blocks of X are solved by forward substitution in
+//      registers, reading G from the MFMA accumulators with readlane;
 //   4. the off-diagonal blocks of X, X_ij = -X_ii sum_k G_ik X_kj (one stage
-//      per block diagonal), then M = C X, on MFMA;
+//      per block diagonal), then M = C X on MFMA, with the blocks of C made
+//      on the fly from K Q^T (so C never takes LDS);
 //   5. S0 Q^T and S0 K^T on MFMA (S0 split into bf16 hi + lo terms) give
 //      B0^T and R^T for the wave's rows;
 //   6. U^T = R^T X^T and O^T = B0^T + R^T M^T on MFMA; each lane then holds
@@ -57,6 +57,10 @@ struct VShape {
     static constexpr int QKLD = D + 8;        // bf16 row stride of Q/K in LDS
     static constexpr int FLD = TM + 4;        // fp32 row stride of the T x T factors and of R^T
     static constexpr int NBM = TM / 16;       // 16-node blocks at most
+    // waves per SIMD the registers must allow: two blocks per CU at 64 nodes
+    // (eight waves each), four at 32 nodes (four waves each; five would
+    // spill)
+    static constexpr int WPE = 4;
 };
 
 template <int D, int TM, bool F32IN>
@@ -68,8 +72,7 @@ struct VLds {
     static constexpr size_t regionA = ((qk > rt ? qk : rt) + 15) / 16 * 16;
     static constexpr size_t fac = (size_t)TM * S::FLD * 4;
     static constexpr size_t off_g = regionA;    // G, later M
-    static constexpr size_t off_c = off_g + fac;
-    static constexpr size_t off_x = off_c + fac;
+    static constexpr size_t off_x = off_g + fac;
     static constexpr size_t off_anc = off_x + fac;   // uint64 [TM]
     static constexpr size_t off_f = off_anc + 8 * TM;  // float logp, P, beta [TM] each
     static constexpr size_t off_i = off_f + 12 * TM;   // int: bad flag
@@ -77,7 +80,8 @@ struct VLds {
 };
 
 template <int D, int TM, bool F32IN>
-__global__ __launch_bounds__((VShape<D, TM>::NW * kWave)) void verify_kernel(const VerifyArgs p) {
+__global__ __launch_bounds__((VShape<D, TM>::NW * kWave))
+__attribute__((amdgpu_waves_per_eu(VShape<D, TM>::WPE))) void verify_kernel(const VerifyArgs p) {
     using S = VShape<D, TM>;
     using L = VLds<D, TM, F32IN>;
     constexpr int BV = S::BV, NW = S::NW, KS = S::KS, QKLD = S::QKLD, FLD = S::FLD, NBM = S::NBM;
@@ -93,7 +97,6 @@ __global__ __launch_bounds__((VShape<D, TM>::NW * kWave)) void verify_kernel(con
     unsigned short* s_klo = s_qlo + TM * QKLD;
     float* s_rt = reinterpret_cast<float*>(smem);  // R^T [BV][FLD], aliases Q/K once they are dead
     float* s_g = reinterpret_cast<float*>(smem + L::off_g);  // G [TM][FLD], then M
-    float* s_c = reinterpret_cast<float*>(smem + L::off_c);  // C [TM][FLD]
     float* s_x = reinterpret_cast<float*>(smem + L::off_x);  // X [TM][FLD]
     uint64_t* s_anc = reinterpret_cast<uint64_t*>(smem + L::off_anc);
     float* s_logp = reinterpret_cast<float*>(smem + L::off_f);
@@ -191,8 +194,8 @@ __global__ __launch_bounds__((VShape<D, TM>::NW * kWave)) void verify_kernel(con
         uint64_t set = valid ? (1ull << n) : 0ull;
         int jmp = (valid && !bad) ? par : -1;
         float ls = la;
-#pragma unroll
         for (int it = 0; it < 6; ++it) {
+            if (__ballot(jmp >= 0) == 0ull) break;  // every path complete
             const int src = jmp >= 0 ? jmp : n;
             const uint64_t set_j = shfl_u64(set, src);
             const float ls_j = __shfl(ls, src, kWave);
@@ -218,10 +221,10 @@ __global__ __launch_bounds__((VShape<D, TM>::NW * kWave)) void verify_kernel(con
     __syncthreads();
     if (s_int[0]) return;  // invalid parent row: nothing is written
 
-    // 3. C and G blocks (mb, nb), nb <= mb, from Q K^T and K K^T; zero above
-    //    the block diagonal.  Items 0 .. NB-1 are the diagonal blocks: block
-    //    (i, i) goes to wave i % NW, which also solves the diagonal block of
-    //    X from its G registers.
+    // 3. G blocks (mb, nb), nb <= mb, from K K^T; zero above the block
+    //    diagonal.  Items 0 .. NB-1 are the diagonal blocks: block (i, i)
+    //    goes to wave i % NW, which also solves the diagonal block of X from
+    //    its G registers.
     for (int it = wave; it < NB * NB; it += NW) {
         int mb, nb;
         if (it < NB) {
@@ -232,32 +235,25 @@ __global__ __launch_bounds__((VShape<D, TM>::NW * kWave)) void verify_kernel(con
             nb = r % (NB - 1);
             if (nb >= mb) ++nb;
         }
-        if (nb > mb) {  // above the diagonal: zero G (later M), C and X
+        if (nb > mb) {  // above the diagonal: zero G (later M) and X
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int n = mb * 16 + 4 * g + r, m = nb * 16 + c;
                 s_g[n * FLD + m] = 0.f;
-                s_c[n * FLD + m] = 0.f;
                 s_x[n * FLD + m] = 0.f;
             }
             continue;
         }
-        floatx4 acc_c = {0.f, 0.f, 0.f, 0.f}, acc_g = acc_c;
-        const unsigned short* qrow = s_q + (mb * 16 + c) * QKLD;
+        floatx4 acc_g = {0.f, 0.f, 0.f, 0.f};
         const unsigned short* krow_a = s_k + (mb * 16 + c) * QKLD;
         const unsigned short* krow_b = s_k + (nb * 16 + c) * QKLD;
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
             const bf16x8 bk = frag_row<D>(krow_b, s, g);
-            const bf16x8 aq = frag_row<D>(qrow, s, g);
             const bf16x8 ak = frag_row<D>(krow_a, s, g);
-            acc_c = mfma16x16x32(aq, bk, acc_c);
             acc_g = mfma16x16x32(ak, bk, acc_g);
             if constexpr (F32IN) {
-                const bf16x8 bkl = frag_row<D>(s_klo + (nb * 16 + c) * QKLD, s, g);
-                acc_c = mfma16x16x32(aq, bkl, acc_c);
-                acc_c = mfma16x16x32(frag_row<D>(s_qlo + (mb * 16 + c) * QKLD, s, g), bk, acc_c);
-                acc_g = mfma16x16x32(ak, bkl, acc_g);
+                acc_g = mfma16x16x32(ak, frag_row<D>(s_klo + (nb * 16 + c) * QKLD, s, g), acc_g);
                 acc_g = mfma16x16x32(frag_row<D>(s_klo + (mb * 16 + c) * QKLD, s, g), bk, acc_g);
             }
         }
@@ -273,7 +269,6 @@ __global__ __launch_bounds__((VShape<D, TM>::NW * kWave)) void verify_kernel(con
             const bool strict = on_path && m != n;
             const float dec = on_path ? expf(s_logp[n] - lpm) : 0.f;
             gv[r] = strict ? s_beta[n] * dec * acc_g[r] : 0.f;
-            s_c[n * FLD + m] = dec * acc_c[r];
             s_g[n * FLD + m] = gv[r];
         }
         if (mb == nb) {
@@ -339,21 +334,48 @@ __global__ __launch_bounds__((VShape<D, TM>::NW * kWave)) void verify_kernel(con
 
     // 4b. M = C X on the blocks (i, j), j <= i, into the G area
     //     (M_ij = sum_{k=j}^{i} C_ik X_kj; every X block is final, so G is
-    //     no longer read)
+    //     no longer read).  The A operand, row n = 16 i + c of C at the
+    //     k-slots m = 32 s + 4 g + r and m + 16, comes from the K Q^T blocks
+    //     of node blocks 2 s and 2 s + 1 against block i: in the MFMA C
+    //     layout those hold exactly k_m . q_n for this lane's (n, m).
     for (int it = wave; it < NB * (NB + 1) / 2; it += NW) {
         int i = 0;
         while ((i + 1) * (i + 2) / 2 <= it) ++i;
         const int j = it - i * (i + 1) / 2;
         const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
+        const int n = 16 * i + c;
+        const uint64_t path_n = s_anc[n] | (1ull << n);
+        const float lpn = s_logp[n];
+        const unsigned short* qrow = s_q + n * QKLD;
         floatx4 macc = {0.f, 0.f, 0.f, 0.f};
-        const float* crow = s_c + (16 * i + c) * FLD;
         const float* xcol = s_x + 16 * j + c;
         for (int s = j / 2; 32 * s < 16 * (i + 1); ++s) {
             const int k0 = 32 * s + 4 * g;
             const bool v0 = k0 >= 16 * j && k0 < 16 * (i + 1);
             const bool v1 = k0 + 16 >= 16 * j && k0 + 16 < 16 * (i + 1);
-            const float4 a0 = v0 ? *reinterpret_cast<const float4*>(crow + k0) : z;
-            const float4 a1 = v1 ? *reinterpret_cast<const float4*>(crow + k0 + 16) : z;
+            floatx4 t0 = {0.f, 0.f, 0.f, 0.f}, t1 = t0;  // k_m . q_n, m in blocks 2 s and 2 s + 1
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const bf16x8 bq = frag_row<D>(qrow, ks, g);
+                const bf16x8 ak0 = frag_row<D>(s_k + (32 * s + c) * QKLD, ks, g);
+                const bf16x8 ak1 = frag_row<D>(s_k + (32 * s + 16 + c) * QKLD, ks, g);
+                t0 = mfma16x16x32(ak0, bq, t0);
+                t1 = mfma16x16x32(ak1, bq, t1);
+                if constexpr (F32IN) {
+                    const bf16x8 bql = frag_row<D>(s_qlo + n * QKLD, ks, g);
+                    t0 = mfma16x16x32(ak0, bql, t0);
+                    t0 = mfma16x16x32(frag_row<D>(s_klo + (32 * s + c) * QKLD, ks, g), bq, t0);
+                    t1 = mfma16x16x32(ak1, bql, t1);
+                    t1 = mfma16x16x32(frag_row<D>(s_klo + (32 * s + 16 + c) * QKLD, ks, g), bq, t1);
+                }
+            }
+            float ca[8];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int m0 = k0 + r, m1 = k0 + 16 + r;
+                ca[r] = (v0 && ((path_n >> m0) & 1ull)) ? expf(lpn - s_logp[m0]) * t0[r] : 0.f;
+                ca[4 + r] = (v1 && ((path_n >> m1) & 1ull)) ? expf(lpn - s_logp[m1]) * t1[r] : 0.f;
+            }
             const float4 b0 = v0 ? make_float4(xcol[(k0 + 0) * FLD], xcol[(k0 + 1) * FLD], xcol[(k0 + 2) * FLD],
                                                xcol[(k0 + 3) * FLD])
                                  : z;
@@ -361,7 +383,7 @@ __global__ __launch_bounds__((VShape<D, TM>::NW * kWave)) void verify_kernel(con
                                                xcol[(k0 + 18) * FLD], xcol[(k0 + 19) * FLD])
                                  : z;
             bf16x8 ah, al, bh, bl;
-            split8(a0, a1, ah, al);
+            split8(make_float4(ca[0], ca[1], ca[2], ca[3]), make_float4(ca[4], ca[5], ca[6], ca[7]), ah, al);
             split8(b0, b1, bh, bl);
             macc = mma3(macc, ah, al, bh, bl);
         }
