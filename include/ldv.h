@@ -62,6 +62,8 @@ extern "C" {
 #define LDV_F32 1
 
 #define LDV_MAX_T 64
+/* Longest chain ldv_verify_chain_long and ldv_commit_state (chain) accept. */
+#define LDV_MAX_LONG_T (1 << 20)
 
 /*
  * Verify a draft tree: for every node n of every (sequence b, head h),
@@ -104,6 +106,30 @@ int ldv_verify_chain(int B, int T, int H, int dk, int dv, int qkv_dtype,
                      int* status, void* stream);
 
 /*
+ * Verify a chain of any length up to LDV_MAX_LONG_T (a long draft block).
+ * The chain is cut into chunks of LDV_MAX_T consecutive nodes; chunk c is
+ * verified with the closed form from the state at the end of chunk c - 1,
+ * which is formed in S_work by the commit of that chunk's last node (the
+ * chunk form: the Bole page's Eq. (2) per chunk, Eq. (9) to pass the state
+ * on).  Results are those of ldv_verify_chain on the whole chain: o, the node
+ * corrections u_n = beta_n (v_n - a_n S_{n-1} k_n) and log P_n counted from
+ * S0, so ldv_commit_state (no parent array) commits any node from S0.
+ *
+ *   q, k, v, a, beta, S0, o: as for ldv_verify_chain; u_out and logp_out are
+ *             required
+ *   S_work    [B, H, dv, dk] fp32 scratch owned by the caller, not
+ *             overlapping S0; needed when T > LDV_MAX_T (may be NULL
+ *             otherwise); its contents on return are unspecified
+ * The chunks are enqueued in order on `stream`.  T <= LDV_MAX_T is the same
+ * as ldv_verify_chain.
+ */
+int ldv_verify_chain_long(int B, int T, int H, int dk, int dv, int qkv_dtype,
+                          const void* q, const void* k, const void* v,
+                          const float* a, const float* beta, const float* S0,
+                          float* o, float* u_out, float* logp_out, float* S_work,
+                          int* status, void* stream);
+
+/*
  * Commit: form only the state of the accepted node (Bole page, summary and
  * section IV, Eq. (9) / "Lemma 1"):
  *     n = accepted[b];  n = -1: S_out[b, h] = S0[b, h]
@@ -113,7 +139,8 @@ int ldv_verify_chain(int B, int T, int H, int dk, int dv, int qkv_dtype,
  *
  *   k         [B, T, H, dk] element type k_dtype
  *   u         [B, T, H, dv] fp32, logp [B, T, H] fp32 (from verify)
- *   parent    [B, T] int32 or NULL for a chain
+ *   parent    [B, T] int32 or NULL for a chain; T <= LDV_MAX_T with a
+ *             parent array, T <= LDV_MAX_LONG_T for a chain
  *   accepted  [B] int32 in [-1, T-1]
  *   S0        [B, H, dv, dk] fp32; S_out [B, H, dv, dk] fp32.  S_out == S0
  *             (in place) is allowed and then heads with accepted = -1 are not

@@ -9,6 +9,11 @@
 // a rank-L update of S0 with L the path length (at most 8 for the draft
 // trees, T for a chain).
 //
+// A chain (no parent array) may be longer than 64 nodes: its path is
+// n, n-1, ..., 0 and is generated instead of walked.  The same kernel forms
+// the state at the end of each 64-node chunk of a long chain (the chunk
+// view: the base state is the previous chunk's end, log P relative to it).
+//
 // The work is a streaming read of S0 and write of S_out (64 KiB each per head
 // at d = 128), so it is bound by HBM.  One block of 256 threads per
 // (sequence, head, row block of up to 32 KiB); each thread owns float4 chunks
@@ -54,8 +59,10 @@ __global__ __launch_bounds__(256) void commit_kernel(const CommitArgs p) {
     const int rb = (int)(bid % S::NRB);
     const int bh = (int)(bid / S::NRB);
     const int h = bh % H, b = bh / H;
+    const size_t nb0 = (size_t)b * p.Ts + p.t0;  // node 0 of this sequence's (chunk of the) draft
+    const bool chain = p.parent == nullptr;
 
-    const int nacc = p.accepted[b];
+    const int nacc = p.acc_const >= -1 ? p.acc_const : p.accepted[b];
     if (nacc < -1 || nacc >= T) {
         if (tid == 0 && p.status && h == 0 && rb == 0) atomicOr(p.status, LDV_STATUS_BAD_ACCEPTED);
         return;
@@ -87,8 +94,10 @@ __global__ __launch_bounds__(256) void commit_kernel(const CommitArgs p) {
         return;
     }
 
+    // log P at the node before a chunk (0: the path starts at the committed state)
+    const float lbase = p.t0 > 0 ? p.logp[(nb0 - 1) * H + h] : 0.f;
     // validate the parent row (as verify does) and walk from the accepted node
-    if (wave == 0) {
+    if (wave == 0 && !chain) {
         const int par = p.parent ? par_ld : lane - 1;
         const bool bad = lane < T && (par < -1 || par >= lane);
         const uint64_t badm = __ballot(bad);
@@ -98,35 +107,38 @@ __global__ __launch_bounds__(256) void commit_kernel(const CommitArgs p) {
             if (badm != 0ull && p.status && h == 0 && rb == 0) atomicOr(p.status, LDV_STATUS_BAD_PARENT);
         }
     }
+    if (chain && tid == 0) s_bad = 0;
     __syncthreads();
     if (s_bad) return;
-    if (tid == 0) {  // parents strictly decrease, so the walk ends within T steps
+    if (!chain && tid == 0) {  // parents strictly decrease, so the walk ends within T steps
         int len = 0;
         for (int m = nacc; m >= 0; m = s_par[m]) s_path[len++] = m;
         s_len = len;
     }
     __syncthreads();
-    const int len = s_len;
+    const int len = chain ? nacc + 1 : s_len;
+    // i-th node of the path from the accepted node towards the root
+    auto path_node = [&](int i) { return chain ? nacc - i : s_path[i]; };
     const int col4 = tid % C4;  // this thread's chunks share one column group (C4 divides NTHR)
 
     for (int c0 = 0; c0 < len; c0 += PCH) {
         const int cl = min(PCH, len - c0);
         // issue every load of this pass before using any of them
-        const float lp_n = p.logp[((size_t)b * T + nacc) * H + h];
+        const float lp_n = p.logp[(nb0 + nacc) * H + h];
         float4 kf[KI];
         u16x4 kb[KI];
         float uval[UI], lval[UI];
 #pragma unroll
         for (int j = 0; j < KI; ++j) {
             const int idx = tid + NTHR * j, i = min(idx / C4, cl - 1), c4 = idx % C4;
-            const size_t krow = (((size_t)b * T + s_path[c0 + i]) * H + h) * D;
+            const size_t krow = ((nb0 + path_node(c0 + i)) * H + h) * D;
             if constexpr (F32K) kf[j] = *reinterpret_cast<const float4*>(static_cast<const float*>(p.k) + krow + 4 * c4);
             else kb[j] = load_u16x4(static_cast<const unsigned short*>(p.k) + krow + 4 * c4);
         }
 #pragma unroll
         for (int j = 0; j < UI; ++j) {
             const int idx = tid + NTHR * j, i = min(idx / RB, cl - 1), r = idx % RB;
-            const size_t node = ((size_t)b * T + s_path[c0 + i]) * H + h;
+            const size_t node = (nb0 + path_node(c0 + i)) * H + h;
             uval[j] = p.u[node * D + (size_t)rb * RB + r];
             lval[j] = p.logp[node];
         }
@@ -144,7 +156,7 @@ __global__ __launch_bounds__(256) void commit_kernel(const CommitArgs p) {
             if (idx < cl * RB) s_uw[idx] = expf(lp_n - lval[j]) * uval[j];
         }
         if (c0 == 0) {
-            const float Pn = expf(lp_n);
+            const float Pn = expf(lp_n - lbase);
 #pragma unroll
             for (int i = 0; i < F4; ++i) sv[i] = make_float4(Pn * sv[i].x, Pn * sv[i].y, Pn * sv[i].z, Pn * sv[i].w);
         }

@@ -36,7 +36,7 @@ int check_verify(int B, int T, int H, int dk, int dv, int dt, const void* q, con
 int verify_common(int B, int T, int H, int d, int dt, const void* q, const void* k, const void* v, const float* a,
                   const float* beta, const float* S0, const int32_t* parent, float* o, float* u_out,
                   float* logp_out, int* status, void* stream) {
-    ldv::VerifyArgs args{B, T, H, d, q, k, v, a, beta, S0, parent, o, u_out, logp_out, status};
+    ldv::VerifyArgs args{B, T, H, d, T, 0, q, k, v, a, beta, S0, parent, o, u_out, logp_out, status};
     hipError_t e = ldv::launch_verify(args, dt == LDV_F32, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? LDV_OK : LDV_ERR_LAUNCH;
 }
@@ -62,12 +62,50 @@ LDV_EXPORT int ldv_verify_chain(int B, int T, int H, int dk, int dv, int qkv_dty
                          stream);
 }
 
+LDV_EXPORT int ldv_verify_chain_long(int B, int T, int H, int dk, int dv, int qkv_dtype, const void* q,
+                                     const void* k, const void* v, const float* a, const float* beta,
+                                     const float* S0, float* o, float* u_out, float* logp_out, float* S_work,
+                                     int* status, void* stream) {
+    if (B < 0 || T < 0 || H < 0 || dk <= 0 || dv <= 0) return LDV_ERR_ARG;
+    if (qkv_dtype != LDV_BF16 && qkv_dtype != LDV_F32) return LDV_ERR_ARG;
+    if (dk != dv || !supported_d(dk) || T > LDV_MAX_LONG_T) return LDV_ERR_UNSUPPORTED;
+    if (B == 0 || T == 0 || H == 0) return LDV_OK;
+    if (!q || !k || !v || !a || !beta || !S0 || !o || !u_out || !logp_out) return LDV_ERR_ARG;
+    if (T > LDV_MAX_T && !S_work) return LDV_ERR_ARG;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(S0, 16) || !aligned(o, 16) ||
+        !aligned(u_out, 16) || !aligned(S_work, 16) || !aligned(a, 4) || !aligned(beta, 4) ||
+        !aligned(logp_out, 4) || !aligned(status, 4))
+        return LDV_ERR_ARG;
+    if ((long long)B * H * 4 > 0x7fffffffLL || (long long)B * T > 0x7fffffffLL) return LDV_ERR_UNSUPPORTED;
+    if (S_work) {  // S_work must not overlap S0 (the first chunk reads S0 while later ones write S_work)
+        const char *w0 = reinterpret_cast<const char*>(S_work), *s0 = reinterpret_cast<const char*>(S0);
+        const size_t bytes = (size_t)B * H * dk * dv * 4;
+        if (w0 < s0 + bytes && s0 < w0 + bytes) return LDV_ERR_ARG;
+    }
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    const bool f32 = qkv_dtype == LDV_F32;
+    for (int t0 = 0; t0 < T; t0 += LDV_MAX_T) {
+        const int len = T - t0 < LDV_MAX_T ? T - t0 : LDV_MAX_T;
+        const float* base = t0 == 0 ? S0 : S_work;
+        ldv::VerifyArgs va{B, len, H, dk, T, t0, q, k, v, a, beta, base, nullptr, o, u_out, logp_out, status};
+        if (ldv::launch_verify(va, f32, st) != hipSuccess) return LDV_ERR_LAUNCH;
+        if (t0 + len < T) {  // the state at the chunk's last node is the next chunk's base
+            ldv::CommitArgs ca{B, len, H, dk, T, t0, len - 1, k, u_out, logp_out, nullptr, nullptr, base, S_work,
+                               status};
+            if (ldv::launch_commit(ca, f32, st) != hipSuccess) return LDV_ERR_LAUNCH;
+        }
+    }
+    return LDV_OK;
+}
+
 LDV_EXPORT int ldv_commit_state(int B, int T, int H, int dk, int dv, int k_dtype, const void* k, const float* u,
                                 const float* logp, const int32_t* parent, const int32_t* accepted,
                                 const float* S0, float* S_out, int* status, void* stream) {
     if (B < 0 || T < 0 || H < 0 || dk <= 0 || dv <= 0) return LDV_ERR_ARG;
     if (k_dtype != LDV_BF16 && k_dtype != LDV_F32) return LDV_ERR_ARG;
-    if (dk != dv || !supported_d(dk) || T > LDV_MAX_T) return LDV_ERR_UNSUPPORTED;
+    // a chain (no parent array) may be of any length, a tree at most 64 nodes
+    if (dk != dv || !supported_d(dk) || (parent && T > LDV_MAX_T) || T > LDV_MAX_LONG_T)
+        return LDV_ERR_UNSUPPORTED;
     if (B == 0 || H == 0) return LDV_OK;
     if (!accepted || !S0 || !S_out) return LDV_ERR_ARG;
     if (T > 0 && (!k || !u || !logp)) return LDV_ERR_ARG;
@@ -75,7 +113,8 @@ LDV_EXPORT int ldv_commit_state(int B, int T, int H, int dk, int dv, int k_dtype
         !aligned(parent, 4) || !aligned(accepted, 4) || !aligned(status, 4))
         return LDV_ERR_ARG;
     if ((long long)B * H * 4 > 0x7fffffffLL) return LDV_ERR_UNSUPPORTED;
-    ldv::CommitArgs args{B, T, H, dk, k, u, logp, parent, accepted, S0, S_out, status};
+    if ((long long)B * T > 0x7fffffffLL) return LDV_ERR_UNSUPPORTED;
+    ldv::CommitArgs args{B, T, H, dk, T, 0, -2, k, u, logp, parent, accepted, S0, S_out, status};
     hipError_t e = ldv::launch_commit(args, k_dtype == LDV_F32, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? LDV_OK : LDV_ERR_LAUNCH;
 }

@@ -6,8 +6,15 @@
 
 namespace ldv {
 
+// Node arrays ([B, T, H, ...] and [B, T, H]) are addressed as node
+// b * Ts + t0 + n for n < T: a call on a whole draft has Ts = T and t0 = 0;
+// a chunk of a longer chain views nodes [t0, t0 + T) of arrays with Ts nodes
+// per sequence.  For t0 > 0, log P is counted from the committed state: the
+// value at node t0 - 1 (already written) is the chunk's base.
+
 struct VerifyArgs {
     int B, T, H, D;
+    int Ts, t0;
     const void* q;
     const void* k;
     const void* v;
@@ -23,6 +30,8 @@ struct VerifyArgs {
 
 struct CommitArgs {
     int B, T, H, D;
+    int Ts, t0;
+    int acc_const;  // >= -1: the accepted node of every sequence; -2: read accepted[]
     const void* k;
     const float* u;
     const float* logp;

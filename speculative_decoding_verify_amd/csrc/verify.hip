@@ -111,6 +111,7 @@ __attribute__((amdgpu_waves_per_eu(VShape<D, TM>::WPE))) void verify_kernel(cons
     const int tile = (int)(bid % S::NT);
     const int bh = (int)(bid / S::NT);
     const int h = bh % H, b = bh / H;
+    const size_t nb0 = (size_t)b * p.Ts + p.t0;  // node 0 of this sequence's (chunk of the) draft
     const int NB = (T + 15) >> 4;  // 16-node blocks in use
     const int T16 = NB * 16;
     const int vrow0 = tile * BV + wave * 16;  // first value row (of S0, o, u) of this wave
@@ -125,7 +126,7 @@ __attribute__((amdgpu_waves_per_eu(VShape<D, TM>::WPE))) void verify_kernel(cons
 #pragma unroll
     for (int i = 0; i < QKC; ++i) {
         const int ch = tid + i * NTHR, row = min(ch / CPR, T - 1), col = (ch % CPR) * EPC;
-        const size_t off = ((((size_t)b * T + row) * H + h) * D + col) * (F32IN ? 4 : 2);
+        const size_t off = (((nb0 + row) * H + h) * D + col) * (F32IN ? 4 : 2);
         qreg[i] = *reinterpret_cast<const u32x4*>(static_cast<const char*>(p.q) + off);
         kreg[i] = *reinterpret_cast<const u32x4*>(static_cast<const char*>(p.k) + off);
     }
@@ -135,7 +136,7 @@ __attribute__((amdgpu_waves_per_eu(VShape<D, TM>::WPE))) void verify_kernel(cons
 #pragma unroll
     for (int nb = 0; nb < NBM; ++nb) {
         const int n = min(nb * 16 + c, T - 1);
-        const size_t off = (((size_t)b * T + n) * H + h) * D + vrow0 + 4 * g;
+        const size_t off = ((nb0 + n) * H + h) * D + vrow0 + 4 * g;
         if constexpr (F32IN) vf[nb] = *reinterpret_cast<const float4*>(static_cast<const float*>(p.v) + off);
         else vb[nb] = load_u16x4(static_cast<const unsigned short*>(p.v) + off);
     }
@@ -145,9 +146,12 @@ __attribute__((amdgpu_waves_per_eu(VShape<D, TM>::WPE))) void verify_kernel(cons
     const global_ptr<const int32_t> parp =
         (global_ptr<const int32_t>)(p.parent ? p.parent : reinterpret_cast<const int32_t*>(p.a));
     const int par_ld = parp[(size_t)b * T + nl];
-    const size_t gi = ((size_t)b * T + nl) * H + h;
+    const size_t gi = (nb0 + nl) * H + h;
     const float ga = p.a[gi];
     const float gb = p.beta[gi];
+    // log P at the node before a chunk (read from any valid entry otherwise)
+    const float* lbp = p.logp_out ? p.logp_out : p.a;
+    const float lbase_ld = lbp[((p.t0 > 0 ? nb0 - 1 : nb0)) * H + h];
     // this lane's S0 row (A operand row c of the wave's 16-row block)
     const float* s0row = p.S0 + (((size_t)b * H + h) * D + vrow0 + c) * D;
     float4 sreg[KS][2];
@@ -216,7 +220,8 @@ __attribute__((amdgpu_waves_per_eu(VShape<D, TM>::WPE))) void verify_kernel(cons
             s_int[0] = badm != 0ull;
             if (badm != 0ull && p.status && h == 0 && tile == 0) atomicOr(p.status, LDV_STATUS_BAD_PARENT);
         }
-        if (badm == 0ull && valid && tile == 0 && p.logp_out) p.logp_out[((size_t)b * T + n) * H + h] = ls;
+        if (badm == 0ull && valid && tile == 0 && p.logp_out)
+            p.logp_out[(nb0 + n) * H + h] = ls + (p.t0 > 0 ? lbase_ld : 0.f);
     }
     __syncthreads();
     if (s_int[0]) return;  // invalid parent row: nothing is written
@@ -488,7 +493,7 @@ __attribute__((amdgpu_waves_per_eu(VShape<D, TM>::WPE))) void verify_kernel(cons
     for (int nb = 0; nb < NBM; ++nb) {
         const int n = nb * 16 + c;
         if (nb < NB && n < T) {
-            const size_t off = (((size_t)b * T + n) * H + h) * D + vrow0 + 4 * g;
+            const size_t off = ((nb0 + n) * H + h) * D + vrow0 + 4 * g;
             st_stream(p.o + off, make_float4(acco[nb][0], acco[nb][1], acco[nb][2], acco[nb][3]));
             if (p.u_out) st_stream(p.u_out + off, make_float4(accu[nb][0], accu[nb][1], accu[nb][2], accu[nb][3]));
         }
@@ -562,6 +567,7 @@ __global__ __launch_bounds__((W16Shape<D>::NW * kWave)) void verify_t16_kernel(c
     const int tile = (int)(bid % S::NT);
     const int bh = (int)(bid / S::NT);
     const int h = bh % H, b = bh / H;
+    const size_t nb0 = (size_t)b * p.Ts + p.t0;  // node 0 of this sequence's (chunk of the) draft
     const int vrow0 = tile * BV + wave * 16;
 
     // 1. loads, small ones first, branch-free (rows clamped into range)
@@ -569,7 +575,7 @@ __global__ __launch_bounds__((W16Shape<D>::NW * kWave)) void verify_t16_kernel(c
 #pragma unroll
     for (int i = 0; i < QKC; ++i) {
         const int ch = tid + i * NTHR, row = min(ch / CPR, T - 1), col = (ch % CPR) * EPC;
-        const size_t off = ((((size_t)b * T + row) * H + h) * D + col) * (F32IN ? 4 : 2);
+        const size_t off = (((nb0 + row) * H + h) * D + col) * (F32IN ? 4 : 2);
         qreg[i] = *reinterpret_cast<const u32x4*>(static_cast<const char*>(p.q) + off);
         kreg[i] = *reinterpret_cast<const u32x4*>(static_cast<const char*>(p.k) + off);
     }
@@ -577,7 +583,7 @@ __global__ __launch_bounds__((W16Shape<D>::NW * kWave)) void verify_t16_kernel(c
     float vv[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-        const size_t off = (((size_t)b * T + min(4 * g + r, T - 1)) * H + h) * D + vrow0 + c;
+        const size_t off = ((nb0 + min(4 * g + r, T - 1)) * H + h) * D + vrow0 + c;
         if constexpr (F32IN) vv[r] = static_cast<const float*>(p.v)[off];
         else vv[r] = bf16_val(static_cast<const unsigned short*>(p.v)[off]);
     }
@@ -585,9 +591,11 @@ __global__ __launch_bounds__((W16Shape<D>::NW * kWave)) void verify_t16_kernel(c
     const global_ptr<const int32_t> parp =
         (global_ptr<const int32_t>)(p.parent ? p.parent : reinterpret_cast<const int32_t*>(p.a));
     const int par_ld = parp[(size_t)b * T + nq];
-    const size_t gi = ((size_t)b * T + nq) * H + h;
+    const size_t gi = (nb0 + nq) * H + h;
     const float ga = p.a[gi];
     const float gb = p.beta[gi];
+    const float* lbp = p.logp_out ? p.logp_out : p.a;  // log P before a chunk
+    const float lbase_ld = lbp[((p.t0 > 0 ? nb0 - 1 : nb0)) * H + h];
     const float* s0row = p.S0 + (((size_t)b * H + h) * D + vrow0 + c) * D;
     float4 sreg[KS][2];
 #pragma unroll
@@ -648,7 +656,8 @@ __global__ __launch_bounds__((W16Shape<D>::NW * kWave)) void verify_t16_kernel(c
     }
     const unsigned anc = set & ~(1u << c);
     const float lp = ls, Pc = valid ? expf(ls) : 0.f, bec = valid ? gb : 0.f;
-    if (tile == 0 && wave == 0 && g == 0 && valid && p.logp_out) p.logp_out[((size_t)b * T + c) * H + h] = lp;
+    if (tile == 0 && wave == 0 && g == 0 && valid && p.logp_out)
+        p.logp_out[(nb0 + c) * H + h] = lp + (p.t0 > 0 ? lbase_ld : 0.f);
     // node data for the rows n = 4 g + r of the C layout
     unsigned anc_r[4];
     float lp_r[4], P_r[4], be_r[4];
@@ -748,7 +757,7 @@ __global__ __launch_bounds__((W16Shape<D>::NW * kWave)) void verify_t16_kernel(c
     const floatx4 Ut = mm16(R, Xt);
     const floatx4 RMt = mm16(R, Mt);
     if (c < T) {
-        const size_t off = (((size_t)b * T + c) * H + h) * D + vrow0 + 4 * g;
+        const size_t off = ((nb0 + c) * H + h) * D + vrow0 + 4 * g;
         st_stream(p.o + off, make_float4(B0t[0] + RMt[0], B0t[1] + RMt[1], B0t[2] + RMt[2], B0t[3] + RMt[3]));
         if (p.u_out) st_stream(p.u_out + off, make_float4(Ut[0], Ut[1], Ut[2], Ut[3]));
     }

@@ -21,6 +21,7 @@ LDV_OK, LDV_ERR_ARG, LDV_ERR_UNSUPPORTED, LDV_ERR_LAUNCH = 0, -1, -2, -3
 LDV_BF16, LDV_F32 = 0, 1
 STATUS_BAD_PARENT, STATUS_BAD_ACCEPTED, STATUS_BAD_SLOT, STATUS_BAD_POSITION = 1, 2, 4, 8
 MAX_T = 64
+MAX_LONG_T = 1 << 20
 
 _lib = None
 
@@ -44,11 +45,12 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     i, vp, fp, ip = ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p
     lib.ldv_verify_tree.argtypes = [i, i, i, i, i, i, vp, vp, vp, fp, fp, fp, ip, fp, fp, fp, ip, vp]
     lib.ldv_verify_chain.argtypes = [i, i, i, i, i, i, vp, vp, vp, fp, fp, fp, fp, fp, fp, ip, vp]
+    lib.ldv_verify_chain_long.argtypes = [i, i, i, i, i, i, vp, vp, vp, fp, fp, fp, fp, fp, fp, fp, ip, vp]
     lib.ldv_commit_state.argtypes = [i, i, i, i, i, i, vp, fp, fp, ip, ip, fp, fp, ip, vp]
     lib.ldv_gather_states.argtypes = [i, i, i, i, i, i, i, i, fp, ip, vp, fp, fp, ip, vp]
     lib.ldv_read_block_states.argtypes = [i, i, i, i, i, i, i, i, vp, fp, fp, ip, fp, ip, vp, fp, ip, vp]
     lib.ldv_select_accepted.argtypes = [i, i, i, i, vp, ip, ip, ip, ip, ip, ip, ip, vp]
-    for f in ("ldv_verify_tree", "ldv_verify_chain", "ldv_commit_state", "ldv_gather_states",
+    for f in ("ldv_verify_tree", "ldv_verify_chain", "ldv_verify_chain_long", "ldv_commit_state", "ldv_gather_states",
               "ldv_read_block_states", "ldv_select_accepted", "ldv_version"):
         getattr(lib, f).restype = ctypes.c_int
     lib.ldv_status_string.argtypes = [ctypes.c_int]
@@ -151,6 +153,40 @@ def verify_tree(q, k, v, a, beta, S0, parent, o=None, u=None, logp=None, factors
                 status=None, stream=None):
     """Verify a draft tree per sequence; parent [B, T] int32, parent[n] in [-1, n-1]."""
     return _verify("ldv_verify_tree", q, k, v, a, beta, S0, parent, o, u, logp, factors, status, stream)
+
+
+def verify_chain_long(q, k, v, a, beta, S0, o=None, u=None, logp=None, S_work=None, status=None,
+                      stream=None):
+    """Verify a chain of any length (up to MAX_LONG_T) in chunks of MAX_T
+    nodes, each from the state at the end of the previous chunk.  Same
+    arguments and results as verify_chain (u and logp are always produced);
+    S_work [B, H, dv, dk] fp32 is scratch, allocated here when not given and
+    T > MAX_T.  Returns (o, u, logp)."""
+    _dev(q, "q")
+    B, T, H, dk = q.shape
+    code = _qkv_code(q)
+    _dev(k, "k", q.dtype, (B, T, H, dk))
+    _dev(v, "v", q.dtype)
+    if v.dim() != 4 or tuple(v.shape[:3]) != (B, T, H):
+        raise ValueError("v must have shape [B, T, H, dv]")
+    dv = v.shape[3]
+    _dev(a, "a", torch.float32, (B, T, H))
+    _dev(beta, "beta", torch.float32, (B, T, H))
+    _dev(S0, "S0", torch.float32, (B, H, dv, dk))
+    dev = q.device
+    o = _opt(o, "o", torch.float32, (B, T, H, dv), dev)
+    u = _opt(u, "u", torch.float32, (B, T, H, dv), dev)
+    logp = _opt(logp, "logp", torch.float32, (B, T, H), dev)
+    if S_work is None and T > MAX_T:
+        S_work = torch.empty((B, H, dv, dk), dtype=torch.float32, device=dev)
+    elif S_work is not None:
+        _dev(S_work, "S_work", torch.float32, (B, H, dv, dk))
+    if status is not None:
+        _dev(status, "status", torch.int32)
+    _check("ldv_verify_chain_long", load().ldv_verify_chain_long(
+        B, T, H, dk, dv, code, _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(beta), _ptr(S0), _ptr(o), _ptr(u),
+        _ptr(logp), _ptr(S_work), _ptr(status), _stream(stream)))
+    return o, u, logp
 
 
 def commit_state(k, u, logp, accepted, S0, S_out=None, parent=None, status=None, stream=None):

@@ -72,7 +72,7 @@ def test_commit_argument_codes(lib):
     assert c(acc=None) == -1
     assert c(out=None) == -1
     assert c(S0=MIS) == -1
-    assert c(T=65) == -2
+    assert c(T=(1 << 20) + 1) == -2   # a chain may be long, but not beyond the limit
     assert c(B=0) == 0
 
 
@@ -121,3 +121,20 @@ def test_select_argument_codes(lib):
     assert s(dt=1, lg=ctypes.c_void_p(0x10002)) == -1
     assert s(T=65) == -2
     assert s(B=0) == 0 and s(T=0) == 0
+
+
+def test_verify_chain_long_argument_codes(lib):
+    c = lambda **kw: lib.ldv_verify_chain_long(
+        kw.get("B", 1), kw.get("T", 100), 1, kw.get("d", 128), kw.get("d", 128), kw.get("dt", 0), FAKE, FAKE, FAKE,
+        FAKE, FAKE, kw.get("S0", FAKE), FAKE, kw.get("u", FAKE), kw.get("lp", FAKE), kw.get("w", ctypes.c_void_p(0x900000)),
+        None, None)
+    assert c(u=None) == -1 and c(lp=None) == -1
+    assert c(w=None) == -1                    # T > 64 needs the work state
+    assert c(w=FAKE) == -1                    # overlaps S0
+    assert c(w=MIS) == -1
+    assert c(T=(1 << 20) + 1) == -2
+    assert c(d=48) == -2
+    assert c(B=0) == 0 and c(T=0) == 0
+    # commit: a chain may be long, a tree may not
+    k = lambda T, par: lib.ldv_commit_state(1, T, 1, 128, 128, 0, FAKE, FAKE, FAKE, par, FAKE, FAKE, FAKE, None, None)
+    assert k(65, FAKE) == -2

@@ -1,0 +1,88 @@
+"""Chains longer than 64 nodes: chunked verify (each chunk from the state at
+the end of the previous one) and commit of any node from S0, against the
+oracle's sequential decode and path walk."""
+import numpy as np
+import pytest
+
+import pins
+from gpu_util import check, dev, host, log_p, qkv_torch_dtype
+from workloads import WORKLOADS, bf16_round, make_chain, make_inputs
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def ldv():
+    import speculative_decoding_verify_amd as m
+    return m
+
+
+def case(seed, B, T, H, D, qkv):
+    c = pins.random_case(seed, B, T, H, D, D, "chain", s0_std=0.05)
+    if qkv == "bf16":
+        for key in ("q", "k", "v"):
+            c[key] = bf16_round(c[key])
+    return c
+
+
+def run(ldv, c, qkv):
+    dt = qkv_torch_dtype(qkv)
+    t = {key: dev(c[key], dt) for key in ("q", "k", "v")}
+    a, beta, S0 = dev(c["a"]), dev(c["beta"]), dev(c["S0"])
+    st = torch.zeros(1, dtype=torch.int32, device="cuda")
+    o, u, logp = ldv.verify_chain_long(t["q"], t["k"], t["v"], a, beta, S0, status=st)
+    return t, a, beta, S0, o, u, logp, st
+
+
+GRID = [  # B, T, H, D, qkv
+    (2, 65, 2, 128, "bf16"),
+    (2, 100, 3, 128, "bf16"),
+    (3, 129, 2, 64, "f32"),
+    (2, 200, 2, 32, "bf16"),
+    (1, 150, 2, 16, "f32"),
+    (2, 80, 2, 128, "f32"),
+]
+
+
+@pytest.mark.parametrize("B,T,H,D,qkv", GRID, ids=lambda v: str(v))
+def test_long_chain_verify_and_commit(ldv, orc, B, T, H, D, qkv):
+    c = case(8000 + T + D, B, T, H, D, qkv)
+    t, a, beta, S0, o, u, logp, st = run(ldv, c, qkv)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+    ref = orc.chain_decode(c["q"], c["k"], c["v"], c["a"], c["beta"], c["S0"])
+    check("long chain o B%d T%d H%d D%d %s" % (B, T, H, D, qkv), o, ref)
+    # log P from S0 along the whole chain (each log a clamped at -87)
+    lp = log_p(c["a"], make_chain(B, T))
+    assert np.max(np.abs(host(logp) - lp)) <= 1e-4 * max(1.0, np.max(np.abs(lp)))
+    # commit nodes in every chunk, from S0, with the factors of the whole chain
+    for n in sorted({0, 63, 64, T // 2, T - 1}):
+        acc = np.full(B, n, dtype=np.int32)
+        acc[0] = -1 if n == 0 else acc[0]
+        S = ldv.commit_state(t["k"], u, logp, dev(acc), S0)
+        torch.cuda.synchronize()
+        want, s = orc.commit(c["k"], c["v"], c["a"], c["beta"], c["S0"], acc)
+        assert s == 0
+        check("long chain commit n=%d" % n, S, want)
+
+
+def test_long_chain_short_is_verify_chain(ldv):
+    """Up to 64 nodes the long form is the ordinary chain verify, bit for bit."""
+    c = case(8100, 2, 40, 2, 128, "bf16")
+    _, _, _, _, o, u, logp, _ = run(ldv, c, "bf16")
+    t = {key: dev(c[key], torch.bfloat16) for key in ("q", "k", "v")}
+    o2, u2, lp2 = ldv.verify_chain(t["q"], t["k"], t["v"], dev(c["a"]), dev(c["beta"]), dev(c["S0"]))
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2) and torch.equal(u, u2) and torch.equal(logp, lp2)
+
+
+def test_long_chain_gdn_shape(ldv, orc):
+    """GDN-1.3B-shaped layer (B16 H16 d128) with a 256-token draft block."""
+    wl = WORKLOADS["gdn1.3b-chain"].replace(T=256, seed=41)
+    x = make_inputs(wl, with_gather=False)
+    t = {key: dev(x[key], torch.bfloat16) for key in ("q", "k", "v")}
+    o, u, logp = ldv.verify_chain_long(t["q"], t["k"], t["v"], dev(x["a"]), dev(x["beta"]), dev(x["S0"]))
+    torch.cuda.synchronize()
+    ref = orc.chain_decode(x["q"], x["k"], x["v"], x["a"], x["beta"], x["S0"])
+    check("long chain GDN shape T256", o, ref)
