@@ -92,6 +92,30 @@ __device__ __forceinline__ floatx4 mma3(floatx4 acc, bf16x8 ah, bf16x8 al, bf16x
     return mfma16x16x32(al, bh, acc);
 }
 
+// An fp32 value packed as its two bf16 terms in one 32-bit word: the hi term
+// in the low half, the lo term in the high half.  A matrix that several
+// waves read as MFMA operands is packed once, so that each read only
+// separates the halves.
+__device__ __forceinline__ uint32_t pack_hilo(float x) {
+    const unsigned short h = bf16_bits(x);
+    const unsigned short l = bf16_bits(x - bf16_val(h));
+    return (uint32_t)h | ((uint32_t)l << 16);
+}
+
+// Eight packed values of one row as the hi and lo A/B fragments of k-step s
+// (runs k0 = 32 s + 4 g and k0 + 16; a run at or past `klim` reads as zero).
+__device__ __forceinline__ void frag_packed(const uint32_t* row, int s, int g, int klim, bf16x8& hi, bf16x8& lo) {
+    const int k0 = 32 * s + 4 * g;
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    const u32x4 p0 = (k0 < klim) ? *reinterpret_cast<const u32x4*>(row + k0) : z;
+    const u32x4 p1 = (k0 + 16 < klim) ? *reinterpret_cast<const u32x4*>(row + k0 + 16) : z;
+    const u16x8 a = __builtin_bit_cast(u16x8, p0), b = __builtin_bit_cast(u16x8, p1);
+    const u16x8 h = {a[0], a[2], a[4], a[6], b[0], b[2], b[4], b[6]};
+    const u16x8 l = {a[1], a[3], a[5], a[7], b[1], b[3], b[5], b[7]};
+    hi = __builtin_bit_cast(bf16x8, h);
+    lo = __builtin_bit_cast(bf16x8, l);
+}
+
 // Eight fp32 values of one matrix row as an A/B fragment of k-step s: the
 // runs k0 = 32 s + 4 g and k0 + 16; a run at or past `klim` reads as zero.
 __device__ __forceinline__ void frag_f32(const float* row, int s, int g, int klim, float4& a, float4& b) {

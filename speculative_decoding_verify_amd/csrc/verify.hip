@@ -61,6 +61,10 @@ struct VShape {
     // (eight waves each), four at 32 nodes (four waves each; five would
     // spill)
     static constexpr int WPE = 4;
+    // pack X, M and R^T as bf16 hi | lo once before step 6 when eight waves
+    // read them (fewer waves: splitting at each read is cheaper than the
+    // extra pass and barrier)
+    static constexpr bool PACK = NW >= 8;
 };
 
 template <int D, int TM, bool F32IN>
@@ -450,41 +454,77 @@ __attribute__((amdgpu_waves_per_eu(VShape<D, TM>::WPE))) void verify_kernel(cons
         }
     }
     __syncthreads();  // Q/K dead in every wave; X and M complete
-#pragma unroll
-    for (int nb = 0; nb < NBM; ++nb) {
-        if (nb < NB) {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) s_rt[(wave * 16 + 4 * g + r) * FLD + nb * 16 + c] = rtv[nb][r];
-        }
-    }
-    // the wave reads back only the R^T rows it wrote (LDS keeps one wave's
-    // operations in order)
 
-    // 6. U^T = R^T X^T and O^T = B0^T + R^T M^T (K = nodes, 32 per step)
+    // 6. U^T = R^T X^T and O^T = B0^T + R^T M^T (K = nodes, 32 per step).
+    //    R^T goes to the Q/K area; each wave reads back only the rows it
+    //    wrote (LDS keeps one wave's operations in order).
     const int ksteps = (T16 + 31) / 32;
-    const float* rrow = s_rt + (wave * 16 + c) * FLD;
     floatx4 accu[NBM], acco[NBM];
 #pragma unroll
     for (int nb = 0; nb < NBM; ++nb) {
         accu[nb] = floatx4{0.f, 0.f, 0.f, 0.f};
         acco[nb] = b0t[nb];
     }
-    for (int s = 0; s < ksteps; ++s) {
-        float4 a0, a1;
-        frag_f32(rrow, s, g, T16, a0, a1);
-        bf16x8 rh, rl;
-        split8(a0, a1, rh, rl);
+    if constexpr (S::PACK) {
+        // R^T, X and M as packed hi | lo words, X and M converted in place
+        uint32_t* s_rtp = reinterpret_cast<uint32_t*>(s_rt);
+        uint32_t* s_xp = reinterpret_cast<uint32_t*>(s_x);
+        uint32_t* s_mp = reinterpret_cast<uint32_t*>(s_g);
 #pragma unroll
         for (int nb = 0; nb < NBM; ++nb) {
             if (nb < NB) {
-                float4 x0, x1, m0, m1;
-                frag_f32(s_x + (nb * 16 + c) * FLD, s, g, T16, x0, x1);
-                frag_f32(s_g + (nb * 16 + c) * FLD, s, g, T16, m0, m1);
-                bf16x8 xh, xl, mh, ml;
-                split8(x0, x1, xh, xl);
-                split8(m0, m1, mh, ml);
-                accu[nb] = mma3(accu[nb], rh, rl, xh, xl);
-                acco[nb] = mma3(acco[nb], rh, rl, mh, ml);
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    s_rtp[(wave * 16 + 4 * g + r) * FLD + nb * 16 + c] = pack_hilo(rtv[nb][r]);
+            }
+        }
+        for (int e = tid; e < T16 * T16; e += NTHR) {
+            const int row = e / T16, col = e - row * T16;
+            s_xp[row * FLD + col] = pack_hilo(s_x[row * FLD + col]);
+            s_mp[row * FLD + col] = pack_hilo(s_g[row * FLD + col]);
+        }
+        __syncthreads();
+        const uint32_t* rrow = s_rtp + (wave * 16 + c) * FLD;
+        for (int s = 0; s < ksteps; ++s) {
+            bf16x8 rh, rl;
+            frag_packed(rrow, s, g, T16, rh, rl);
+#pragma unroll
+            for (int nb = 0; nb < NBM; ++nb) {
+                if (nb < NB) {
+                    bf16x8 xh, xl, mh, ml;
+                    frag_packed(s_xp + (nb * 16 + c) * FLD, s, g, T16, xh, xl);
+                    frag_packed(s_mp + (nb * 16 + c) * FLD, s, g, T16, mh, ml);
+                    accu[nb] = mma3(accu[nb], rh, rl, xh, xl);
+                    acco[nb] = mma3(acco[nb], rh, rl, mh, ml);
+                }
+            }
+        }
+    } else {
+#pragma unroll
+        for (int nb = 0; nb < NBM; ++nb) {
+            if (nb < NB) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) s_rt[(wave * 16 + 4 * g + r) * FLD + nb * 16 + c] = rtv[nb][r];
+            }
+        }
+        const float* rrow = s_rt + (wave * 16 + c) * FLD;
+        for (int s = 0; s < ksteps; ++s) {
+            float4 a0, a1;
+            frag_f32(rrow, s, g, T16, a0, a1);
+            bf16x8 rh, rl;
+            split8(a0, a1, rh, rl);
+#pragma unroll
+            for (int nb = 0; nb < NBM; ++nb) {
+                if (nb < NB) {
+                    float4 x0, x1, m0, m1;
+                    frag_f32(s_x + (nb * 16 + c) * FLD, s, g, T16, x0, x1);
+                    frag_f32(s_g + (nb * 16 + c) * FLD, s, g, T16, m0, m1);
+                    bf16x8 xh, xl, mh, ml;
+                    split8(x0, x1, xh, xl);
+                    split8(m0, m1, mh, ml);
+                    accu[nb] = mma3(accu[nb], rh, rl, xh, xl);
+                    acco[nb] = mma3(acco[nb], rh, rl, mh, ml);
+                }
             }
         }
     }
