@@ -48,19 +48,22 @@ namespace ldv {
 
 template <int D, int TM>
 struct VShape {
-    // a 64-node block keeps the whole head (BV = 128, eight waves) when it
-    // can: its factor work is the largest, so it is done once per head
-    static constexpr int BV = (TM == 64 && D >= 128) ? 128 : (D >= 64 ? 64 : D);
+    // At d = 128 a block keeps the whole head (BV = 128), so the factor work
+    // is done once per head: eight waves of 16 value rows at 64 nodes, four
+    // waves of two 16-row blocks (MBW = 2) at 32 nodes, where each operand
+    // fragment read from LDS then serves two MFMA row blocks.
+    static constexpr int BV = (D >= 128) ? 128 : (D >= 64 ? 64 : D);
+    static constexpr int MBW = (TM == 32 && D >= 128) ? 2 : 1;  // 16-row blocks per wave
     static constexpr int NT = D / BV;         // value tiles per head
-    static constexpr int NW = BV / 16;        // waves per block
+    static constexpr int NW = BV / (16 * MBW);  // waves per block
     static constexpr int KS = (D + 31) / 32;  // MFMA k-steps over d_k
     static constexpr int QKLD = D + 8;        // bf16 row stride of Q/K in LDS
     static constexpr int FLD = TM + 4;        // fp32 row stride of the T x T factors and of R^T
     static constexpr int NBM = TM / 16;       // 16-node blocks at most
     // waves per SIMD the registers must allow: two blocks per CU at 64 nodes
-    // (eight waves each), four at 32 nodes (four waves each; five would
-    // spill)
-    static constexpr int WPE = 4;
+    // (eight waves each), three at 32 nodes with two row blocks per wave,
+    // four otherwise
+    static constexpr int WPE = MBW == 2 ? 3 : 4;
     // pack X, M and R^T as bf16 hi | lo once before step 6 when eight waves
     // read them (fewer waves: splitting at each read is cheaper than the
     // extra pass and barrier)
@@ -88,7 +91,7 @@ __global__ __launch_bounds__((VShape<D, TM>::NW * kWave))
 __attribute__((amdgpu_waves_per_eu(VShape<D, TM>::WPE))) void verify_kernel(const VerifyArgs p) {
     using S = VShape<D, TM>;
     using L = VLds<D, TM, F32IN>;
-    constexpr int BV = S::BV, NW = S::NW, KS = S::KS, QKLD = S::QKLD, FLD = S::FLD, NBM = S::NBM;
+    constexpr int BV = S::BV, NW = S::NW, KS = S::KS, QKLD = S::QKLD, FLD = S::FLD, NBM = S::NBM, MBW = S::MBW;
     constexpr int NTHR = NW * kWave;
     constexpr int EPC = F32IN ? 4 : 8;                 // elements per 16-byte chunk
     constexpr int CPR = D / EPC;                       // chunks per q/k row
@@ -118,7 +121,8 @@ __attribute__((amdgpu_waves_per_eu(VShape<D, TM>::WPE))) void verify_kernel(cons
     const size_t nb0 = (size_t)b * p.Ts + p.t0;  // node 0 of this sequence's (chunk of the) draft
     const int NB = (T + 15) >> 4;  // 16-node blocks in use
     const int T16 = NB * 16;
-    const int vrow0 = tile * BV + wave * 16;  // first value row (of S0, o, u) of this wave
+    const int wrow0 = wave * 16 * MBW;        // first value row of this wave within the tile
+    const int vrow0 = tile * BV + wrow0;      // first value row (of S0, o, u) of this wave
 
     // 1. global loads.  Every small per-node input first, so that, loads
     // completing in issue order, steps 2-4 can run while the S0 rows are in
@@ -134,15 +138,19 @@ __attribute__((amdgpu_waves_per_eu(VShape<D, TM>::WPE))) void verify_kernel(cons
         qreg[i] = *reinterpret_cast<const u32x4*>(static_cast<const char*>(p.q) + off);
         kreg[i] = *reinterpret_cast<const u32x4*>(static_cast<const char*>(p.k) + off);
     }
-    // v[n][vrow0 + 4g .. +3] for the node n = 16 nb + c this lane holds in step 5
-    u16x4 vb[NBM];
-    float4 vf[NBM];
+    // v[n][vrow0 + 16 mi + 4g .. +3] for the node n = 16 nb + c this lane
+    // holds in step 5
+    u16x4 vb[MBW][NBM];
+    float4 vf[MBW][NBM];
 #pragma unroll
-    for (int nb = 0; nb < NBM; ++nb) {
-        const int n = min(nb * 16 + c, T - 1);
-        const size_t off = ((nb0 + n) * H + h) * D + vrow0 + 4 * g;
-        if constexpr (F32IN) vf[nb] = *reinterpret_cast<const float4*>(static_cast<const float*>(p.v) + off);
-        else vb[nb] = load_u16x4(static_cast<const unsigned short*>(p.v) + off);
+    for (int mi = 0; mi < MBW; ++mi) {
+#pragma unroll
+        for (int nb = 0; nb < NBM; ++nb) {
+            const int n = min(nb * 16 + c, T - 1);
+            const size_t off = ((nb0 + n) * H + h) * D + vrow0 + 16 * mi + 4 * g;
+            if constexpr (F32IN) vf[mi][nb] = *reinterpret_cast<const float4*>(static_cast<const float*>(p.v) + off);
+            else vb[mi][nb] = load_u16x4(static_cast<const unsigned short*>(p.v) + off);
+        }
     }
     const int nl = min(lane, T - 1);
     // a chain has no parent array: read the gate array instead (it has at
@@ -156,14 +164,29 @@ __attribute__((amdgpu_waves_per_eu(VShape<D, TM>::WPE))) void verify_kernel(cons
     // log P at the node before a chunk (read from any valid entry otherwise)
     const float* lbp = p.logp_out ? p.logp_out : p.a;
     const float lbase_ld = lbp[((p.t0 > 0 ? nb0 - 1 : nb0)) * H + h];
-    // this lane's S0 row (A operand row c of the wave's 16-row block)
-    const float* s0row = p.S0 + (((size_t)b * H + h) * D + vrow0 + c) * D;
-    float4 sreg[KS][2];
+    // this lane's S0 rows (A operand row c of each of the wave's 16-row blocks)
+    // (one row block is written without the row-block loop: with it the
+    // compiler's allocation of the 64-node kernel spills)
+    float4 sreg[MBW][KS][2];
+    if constexpr (MBW == 1) {
+        const float* s0row = p.S0 + (((size_t)b * H + h) * D + vrow0 + c) * D;
 #pragma unroll
-    for (int s = 0; s < KS; ++s) {
-        const int k0 = 32 * s + 4 * g;
-        sreg[s][0] = (k0 < D) ? ld_stream(s0row + k0) : make_float4(0.f, 0.f, 0.f, 0.f);
-        sreg[s][1] = (k0 + 16 < D) ? ld_stream(s0row + k0 + 16) : make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int s = 0; s < KS; ++s) {
+            const int k0 = 32 * s + 4 * g;
+            sreg[0][s][0] = (k0 < D) ? ld_stream(s0row + k0) : make_float4(0.f, 0.f, 0.f, 0.f);
+            sreg[0][s][1] = (k0 + 16 < D) ? ld_stream(s0row + k0 + 16) : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+    } else {
+#pragma unroll
+        for (int mi = 0; mi < MBW; ++mi) {
+            const float* s0row = p.S0 + (((size_t)b * H + h) * D + vrow0 + 16 * mi + c) * D;
+#pragma unroll
+            for (int s = 0; s < KS; ++s) {
+                const int k0 = 32 * s + 4 * g;
+                sreg[mi][s][0] = (k0 < D) ? ld_stream(s0row + k0) : make_float4(0.f, 0.f, 0.f, 0.f);
+                sreg[mi][s][1] = (k0 + 16 < D) ? ld_stream(s0row + k0 + 16) : make_float4(0.f, 0.f, 0.f, 0.f);
+            }
+        }
     }
     asm volatile("" ::: "memory");  // keep the loads above ahead of any use of them
     const int par = p.parent ? par_ld : lane - 1;
@@ -400,57 +423,72 @@ __attribute__((amdgpu_waves_per_eu(VShape<D, TM>::WPE))) void verify_kernel(cons
         for (int r = 0; r < 4; ++r) s_g[(16 * i + 4 * g + r) * FLD + 16 * j + c] = macc[r];
     }
 
-    // 5. S0 Q^T and S0 K^T for the wave's 16 value rows (A = S0 rows, split
-    //    hi + lo; B = Q / K rows).  Lane (c, g) ends with value rows 4 g + r
-    //    and node n = 16 nb + c of each node block.
-    floatx4 accq[NBM], acck[NBM];
+    // 5. S0 Q^T and S0 K^T for the wave's value rows (A = S0 rows, split
+    //    hi + lo; B = Q / K rows).  Lane (c, g) ends with value rows
+    //    16 mi + 4 g + r and node n = 16 nb + c of each node block.
+    floatx4 accq[MBW][NBM], acck[MBW][NBM];
 #pragma unroll
-    for (int nb = 0; nb < NBM; ++nb) {
-        accq[nb] = floatx4{0.f, 0.f, 0.f, 0.f};
-        acck[nb] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int mi = 0; mi < MBW; ++mi) {
+#pragma unroll
+        for (int nb = 0; nb < NBM; ++nb) {
+            accq[mi][nb] = floatx4{0.f, 0.f, 0.f, 0.f};
+            acck[mi][nb] = floatx4{0.f, 0.f, 0.f, 0.f};
+        }
     }
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
-        bf16x8 sh, sl;
-        split8(sreg[s][0], sreg[s][1], sh, sl);
+        bf16x8 sh[MBW], sl[MBW];
+#pragma unroll
+        for (int mi = 0; mi < MBW; ++mi) split8(sreg[mi][s][0], sreg[mi][s][1], sh[mi], sl[mi]);
 #pragma unroll
         for (int nb = 0; nb < NBM; ++nb) {
             if (nb < NB) {
                 const bf16x8 bq = frag_row<D>(s_q + (nb * 16 + c) * QKLD, s, g);
                 const bf16x8 bk = frag_row<D>(s_k + (nb * 16 + c) * QKLD, s, g);
-                accq[nb] = mfma16x16x32(sh, bq, accq[nb]);
-                accq[nb] = mfma16x16x32(sl, bq, accq[nb]);
-                acck[nb] = mfma16x16x32(sh, bk, acck[nb]);
-                acck[nb] = mfma16x16x32(sl, bk, acck[nb]);
+#pragma unroll
+                for (int mi = 0; mi < MBW; ++mi) {
+                    accq[mi][nb] = mfma16x16x32(sh[mi], bq, accq[mi][nb]);
+                    accq[mi][nb] = mfma16x16x32(sl[mi], bq, accq[mi][nb]);
+                    acck[mi][nb] = mfma16x16x32(sh[mi], bk, acck[mi][nb]);
+                    acck[mi][nb] = mfma16x16x32(sl[mi], bk, acck[mi][nb]);
+                }
                 if constexpr (F32IN) {
-                    accq[nb] = mfma16x16x32(sh, frag_row<D>(s_qlo + (nb * 16 + c) * QKLD, s, g), accq[nb]);
-                    acck[nb] = mfma16x16x32(sh, frag_row<D>(s_klo + (nb * 16 + c) * QKLD, s, g), acck[nb]);
+                    const bf16x8 bql = frag_row<D>(s_qlo + (nb * 16 + c) * QKLD, s, g);
+                    const bf16x8 bkl = frag_row<D>(s_klo + (nb * 16 + c) * QKLD, s, g);
+#pragma unroll
+                    for (int mi = 0; mi < MBW; ++mi) {
+                        accq[mi][nb] = mfma16x16x32(sh[mi], bql, accq[mi][nb]);
+                        acck[mi][nb] = mfma16x16x32(sh[mi], bkl, acck[mi][nb]);
+                    }
                 }
             }
         }
     }
     // B0^T[i][n] = P_n (S0 q_n)[i];  R^T[i][n] = beta_n (v_n[i] - P_n (S0 k_n)[i])
-    floatx4 b0t[NBM];
-    float rtv[NBM][4];
+    floatx4 b0t[MBW][NBM];
+    float rtv[MBW][NBM][4];
 #pragma unroll
     for (int nb = 0; nb < NBM; ++nb) {
         const int n = nb * 16 + c;
         const bool nv = nb < NB && n < T;
         const float P = nv ? s_P[n] : 0.f, be = nv ? s_beta[n] : 0.f;
-        float vv[4];
-        if constexpr (F32IN) {
-            vv[0] = vf[nb].x;
-            vv[1] = vf[nb].y;
-            vv[2] = vf[nb].z;
-            vv[3] = vf[nb].w;
-        } else {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) vv[r] = bf16_val(vb[nb][r]);
-        }
+        for (int mi = 0; mi < MBW; ++mi) {
+            float vv[4];
+            if constexpr (F32IN) {
+                vv[0] = vf[mi][nb].x;
+                vv[1] = vf[mi][nb].y;
+                vv[2] = vf[mi][nb].z;
+                vv[3] = vf[mi][nb].w;
+            } else {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            b0t[nb][r] = P * accq[nb][r];
-            rtv[nb][r] = nv ? be * (vv[r] - P * acck[nb][r]) : 0.f;
+                for (int r = 0; r < 4; ++r) vv[r] = bf16_val(vb[mi][nb][r]);
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                b0t[mi][nb][r] = P * accq[mi][nb][r];
+                rtv[mi][nb][r] = nv ? be * (vv[r] - P * acck[mi][nb][r]) : 0.f;
+            }
         }
     }
     __syncthreads();  // Q/K dead in every wave; X and M complete
@@ -459,11 +497,14 @@ __attribute__((amdgpu_waves_per_eu(VShape<D, TM>::WPE))) void verify_kernel(cons
     //    R^T goes to the Q/K area; each wave reads back only the rows it
     //    wrote (LDS keeps one wave's operations in order).
     const int ksteps = (T16 + 31) / 32;
-    floatx4 accu[NBM], acco[NBM];
+    floatx4 accu[MBW][NBM], acco[MBW][NBM];
 #pragma unroll
-    for (int nb = 0; nb < NBM; ++nb) {
-        accu[nb] = floatx4{0.f, 0.f, 0.f, 0.f};
-        acco[nb] = b0t[nb];
+    for (int mi = 0; mi < MBW; ++mi) {
+#pragma unroll
+        for (int nb = 0; nb < NBM; ++nb) {
+            accu[mi][nb] = floatx4{0.f, 0.f, 0.f, 0.f};
+            acco[mi][nb] = b0t[mi][nb];
+        }
     }
     if constexpr (S::PACK) {
         // R^T, X and M as packed hi | lo words, X and M converted in place
@@ -471,11 +512,14 @@ __attribute__((amdgpu_waves_per_eu(VShape<D, TM>::WPE))) void verify_kernel(cons
         uint32_t* s_xp = reinterpret_cast<uint32_t*>(s_x);
         uint32_t* s_mp = reinterpret_cast<uint32_t*>(s_g);
 #pragma unroll
-        for (int nb = 0; nb < NBM; ++nb) {
-            if (nb < NB) {
+        for (int mi = 0; mi < MBW; ++mi) {
 #pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    s_rtp[(wave * 16 + 4 * g + r) * FLD + nb * 16 + c] = pack_hilo(rtv[nb][r]);
+            for (int nb = 0; nb < NBM; ++nb) {
+                if (nb < NB) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        s_rtp[(wrow0 + 16 * mi + 4 * g + r) * FLD + nb * 16 + c] = pack_hilo(rtv[mi][nb][r]);
+                }
             }
         }
         for (int e = tid; e < T16 * T16; e += NTHR) {
@@ -484,35 +528,44 @@ __attribute__((amdgpu_waves_per_eu(VShape<D, TM>::WPE))) void verify_kernel(cons
             s_mp[row * FLD + col] = pack_hilo(s_g[row * FLD + col]);
         }
         __syncthreads();
-        const uint32_t* rrow = s_rtp + (wave * 16 + c) * FLD;
         for (int s = 0; s < ksteps; ++s) {
-            bf16x8 rh, rl;
-            frag_packed(rrow, s, g, T16, rh, rl);
+            bf16x8 rh[MBW], rl[MBW];
+#pragma unroll
+            for (int mi = 0; mi < MBW; ++mi) frag_packed(s_rtp + (wrow0 + 16 * mi + c) * FLD, s, g, T16, rh[mi], rl[mi]);
 #pragma unroll
             for (int nb = 0; nb < NBM; ++nb) {
                 if (nb < NB) {
                     bf16x8 xh, xl, mh, ml;
                     frag_packed(s_xp + (nb * 16 + c) * FLD, s, g, T16, xh, xl);
                     frag_packed(s_mp + (nb * 16 + c) * FLD, s, g, T16, mh, ml);
-                    accu[nb] = mma3(accu[nb], rh, rl, xh, xl);
-                    acco[nb] = mma3(acco[nb], rh, rl, mh, ml);
+#pragma unroll
+                    for (int mi = 0; mi < MBW; ++mi) {
+                        accu[mi][nb] = mma3(accu[mi][nb], rh[mi], rl[mi], xh, xl);
+                        acco[mi][nb] = mma3(acco[mi][nb], rh[mi], rl[mi], mh, ml);
+                    }
                 }
             }
         }
     } else {
 #pragma unroll
-        for (int nb = 0; nb < NBM; ++nb) {
-            if (nb < NB) {
+        for (int mi = 0; mi < MBW; ++mi) {
 #pragma unroll
-                for (int r = 0; r < 4; ++r) s_rt[(wave * 16 + 4 * g + r) * FLD + nb * 16 + c] = rtv[nb][r];
+            for (int nb = 0; nb < NBM; ++nb) {
+                if (nb < NB) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        s_rt[(wrow0 + 16 * mi + 4 * g + r) * FLD + nb * 16 + c] = rtv[mi][nb][r];
+                }
             }
         }
-        const float* rrow = s_rt + (wave * 16 + c) * FLD;
         for (int s = 0; s < ksteps; ++s) {
-            float4 a0, a1;
-            frag_f32(rrow, s, g, T16, a0, a1);
-            bf16x8 rh, rl;
-            split8(a0, a1, rh, rl);
+            bf16x8 rh[MBW], rl[MBW];
+#pragma unroll
+            for (int mi = 0; mi < MBW; ++mi) {
+                float4 a0, a1;
+                frag_f32(s_rt + (wrow0 + 16 * mi + c) * FLD, s, g, T16, a0, a1);
+                split8(a0, a1, rh[mi], rl[mi]);
+            }
 #pragma unroll
             for (int nb = 0; nb < NBM; ++nb) {
                 if (nb < NB) {
@@ -522,20 +575,27 @@ __attribute__((amdgpu_waves_per_eu(VShape<D, TM>::WPE))) void verify_kernel(cons
                     bf16x8 xh, xl, mh, ml;
                     split8(x0, x1, xh, xl);
                     split8(m0, m1, mh, ml);
-                    accu[nb] = mma3(accu[nb], rh, rl, xh, xl);
-                    acco[nb] = mma3(acco[nb], rh, rl, mh, ml);
+#pragma unroll
+                    for (int mi = 0; mi < MBW; ++mi) {
+                        accu[mi][nb] = mma3(accu[mi][nb], rh[mi], rl[mi], xh, xl);
+                        acco[mi][nb] = mma3(acco[mi][nb], rh[mi], rl[mi], mh, ml);
+                    }
                 }
             }
         }
     }
-    // lane (c, g): node n = 16 nb + c, value rows vrow0 + 4 g .. +3
+    // lane (c, g): node n = 16 nb + c, value rows vrow0 + 16 mi + 4 g .. +3
 #pragma unroll
-    for (int nb = 0; nb < NBM; ++nb) {
-        const int n = nb * 16 + c;
-        if (nb < NB && n < T) {
-            const size_t off = ((nb0 + n) * H + h) * D + vrow0 + 4 * g;
-            st_stream(p.o + off, make_float4(acco[nb][0], acco[nb][1], acco[nb][2], acco[nb][3]));
-            if (p.u_out) st_stream(p.u_out + off, make_float4(accu[nb][0], accu[nb][1], accu[nb][2], accu[nb][3]));
+    for (int mi = 0; mi < MBW; ++mi) {
+#pragma unroll
+        for (int nb = 0; nb < NBM; ++nb) {
+            const int n = nb * 16 + c;
+            if (nb < NB && n < T) {
+                const size_t off = ((nb0 + n) * H + h) * D + vrow0 + 16 * mi + 4 * g;
+                st_stream(p.o + off, make_float4(acco[mi][nb][0], acco[mi][nb][1], acco[mi][nb][2], acco[mi][nb][3]));
+                if (p.u_out)
+                    st_stream(p.u_out + off, make_float4(accu[mi][nb][0], accu[mi][nb][1], accu[mi][nb][2], accu[mi][nb][3]));
+            }
         }
     }
 }
