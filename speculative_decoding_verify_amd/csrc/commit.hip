@@ -16,9 +16,10 @@
 //
 // The work is a streaming read of S0 and write of S_out (64 KiB each per head
 // at d = 128), so it is bound by HBM.  One block of 256 threads per
-// (sequence, head, row block of up to 32 KiB); each thread owns float4 chunks
-// of consecutive columns so that every wave reads and writes contiguous 1 KiB
-// runs.  The block loads the parent row, then its S0 rows; walks the parent
+// (sequence, head, row block of up to 16 KiB; small blocks keep more of them
+// in flight per CU, measured 2-3 % faster than 32 KiB); each thread owns
+// float4 chunks of consecutive columns so that every wave reads and writes
+// contiguous 1 KiB runs.  The block loads the parent row, then its S0 rows; walks the parent
 // row in LDS from the accepted node to the root while the state is in
 // flight; issues the loads of u, k and log P on the path; stages w_m u_m (its
 // rows) and k_m (all columns) for up to 16 path nodes at a time in LDS; and
@@ -34,7 +35,7 @@ template <int D>
 struct CShape {
     static constexpr int NTHR = 256;
     static constexpr int C4 = D / 4;                                  // float4 per state row (divides NTHR)
-    static constexpr int E4 = (D * D / 4 < 2048) ? D * D / 4 : 2048;  // float4 per block (<= 32 KiB)
+    static constexpr int E4 = (D * D / 4 < 1024) ? D * D / 4 : 1024;  // float4 per block (<= 16 KiB)
     static constexpr int RB = E4 / C4;                                // rows per block
     static constexpr int NRB = D / RB;                                // row blocks per head
     static constexpr int F4 = (E4 + NTHR - 1) / NTHR;                 // float4 per thread
