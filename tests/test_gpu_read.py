@@ -112,19 +112,27 @@ def test_read_bad_position_and_parent(ldv):
     assert torch.all(o[1] == 7.0) and not torch.any(o[2] == 7.0) and not torch.any(o[0, 0] == 7.0)
 
 
-def test_read_workload_full_size(ldv, orc):
-    """27B-hybrid shape: B64 H32 d128, chain of 16, 4 in-block positions x 16
-    queries per sequence; every output checked against the oracle's walk."""
-    wl = WORKLOADS["hybrid27b-chain-gather"]
+@pytest.mark.parametrize("key", list(WORKLOADS))
+def test_read_workload_full_size(ldv, orc, key):
+    """Every workload shape at full size (4 in-block positions x 16 queries
+    per sequence, 27B-hybrid: its own P and Qn); every output checked
+    against the oracle's walk."""
+    wl = WORKLOADS[key]
     x = make_inputs(wl, with_gather=False)
     r = make_block_read_inputs(wl)
-    q, k, v = (dev(x[key], torch.bfloat16) for key in ("q", "k", "v"))
+    dt = torch.bfloat16 if wl.qkv == "bf16" else torch.float32
+    q, k, v = (dev(x[n], dt) for n in ("q", "k", "v"))
     a, beta, S0 = dev(x["a"]), dev(x["beta"]), dev(x["S0"])
-    _, u, logp = ldv.verify_chain(q, k, v, a, beta, S0)
+    par = dev(x["parent"]) if wl.topology == "tree" else None
+    if par is None:
+        _, u, logp = ldv.verify_chain(q, k, v, a, beta, S0)
+    else:
+        _, u, logp = ldv.verify_tree(q, k, v, a, beta, S0, par)
     st = torch.zeros(1, dtype=torch.int32, device="cuda")
-    o = ldv.read_block_states(k, u, logp, S0, dev(r["pos"]), dev(r["queries"], torch.bfloat16), status=st)
+    o = ldv.read_block_states(k, u, logp, S0, dev(r["pos"]), dev(r["queries"], dt), parent=par, status=st)
     torch.cuda.synchronize()
     assert int(st.item()) == 0
-    ref, s = orc.read_states(x["k"], x["v"], x["a"], x["beta"], x["S0"], r["pos"], r["queries"], None)
+    ref, s = orc.read_states(x["k"], x["v"], x["a"], x["beta"], x["S0"], r["pos"], r["queries"],
+                             x["parent"] if wl.topology == "tree" else None)
     assert s == 0
-    check("read hybrid27b full size", o, ref)
+    check("read %s full size" % key, o, ref)

@@ -100,7 +100,7 @@ def test_select_grid(ldv, orc, B, T, V, dtype, topology, kind):
         compare(orc, ldv, logits, tokens, par, dtype, "select explicit chain")
 
 
-@pytest.mark.parametrize("key", ["hybrid27b-chain-gather", "tree64", "gdn1.3b-chain"])
+@pytest.mark.parametrize("key", ["hybrid27b-chain-gather", "tree64", "gdn1.3b-chain", "batch256-tree-commit"])
 def test_select_workload_full_size(ldv, orc, key):
     wl = WORKLOADS[key]
     x = make_inputs(wl, with_gather=False)
