@@ -245,6 +245,35 @@ class Runner:
         return [self.verify, self.commit] + ([self.gather] if self.wl.P > 0 else [])
 
 
+def measure_peaks(torch):
+    """Achievable peaks on this GPU: a 2 GiB device-to-device copy (HBM read
+    plus write) and an 8192^3 bf16 GEMM (hipBLASLt through torch.matmul), each
+    the best of 5 timed runs after a warm-up."""
+    n = (2 << 30) // 4
+    src = torch.ones(n, device="cuda")
+    dst = torch.empty(n, device="cuda")
+    a = torch.randn(8192, 8192, device="cuda", dtype=torch.bfloat16)
+    b = torch.randn(8192, 8192, device="cuda", dtype=torch.bfloat16)
+    out = {}
+    for name, fn, work in (("copy_GB_s", lambda: dst.copy_(src), 2 * n * 4 / 1e9),
+                           ("bf16_gemm_TFLOP_s", lambda: torch.matmul(a, b), 2 * 8192 ** 3 / 1e12)):
+        fn()
+        torch.cuda.synchronize()
+        best = None
+        for _ in range(5):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            t = e0.elapsed_time(e1) * 1e-3
+            best = t if best is None else min(best, t)
+        out[name] = work / best
+    del src, dst, a, b
+    torch.cuda.empty_cache()
+    return out
+
+
 def capture(torch, fns, K):
     """One HIP graph holding K launches of each function in fns, in order."""
     g = torch.cuda.CUDAGraph()
@@ -265,6 +294,7 @@ def main():
     ap.add_argument("--no-next", action="store_true", help="skip timing the in-block read and the selection")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum CPU-oracle time")
     ap.add_argument("--repeats", type=int, default=5, help="timed replays of each per-kernel graph")
+    ap.add_argument("--no-peaks", action="store_true", help="skip measuring the copy and GEMM peaks")
     ap.add_argument("--eager", action="store_true",
                     help="launch from Python each step instead of replaying HIP graphs (for profilers)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
@@ -351,6 +381,7 @@ def main():
         return float(np.median(ts)), float(np.min(ts)), float(np.max(ts))
 
     alg = algorithmic(wl, x)
+    peaks = None if args.no_peaks else measure_peaks(torch)
     kern = {}
     names = [("verify", run.verify, alg["verify"]), ("commit", run.commit, alg["commit"])]
     if wl.P > 0:
@@ -368,6 +399,16 @@ def main():
     kern["verify"]["nodes_per_s"] = nodes / kern["verify"]["us"] * 1e6
     kern["verify"]["alg_flops"] = alg["verify_flops"]
     kern["verify"]["mfma_frac"] = alg["verify_flops"] / (kern["verify"]["us"] * 1e-6) / (BF16_PEAK_TFLOPS * 1e12)
+    # o = S q products of the state reads (2 d^2 flops per query)
+    for name, nq in (("gather", wl.B * wl.P * wl.H * wl.Qn),
+                     ("read_block", wl.B * (run.P2 if not args.no_next else 0) * wl.H * (run.Qn2 if not args.no_next else 0))):
+        if name in kern and nq:
+            fl = 2.0 * wl.D * wl.D * nq
+            kern[name]["alg_flops"] = fl
+            kern[name]["mfma_frac"] = fl / (kern[name]["us"] * 1e-6) / (BF16_PEAK_TFLOPS * 1e12)
+    if peaks:
+        for v in kern.values():
+            v["hbm_frac_of_measured_copy"] = v["GB_s"] / peaks["copy_GB_s"]
     if "read_block" in kern:
         kern["read_block"].update({"P": run.P2, "Qn": run.Qn2})
     if "select" in kern:
@@ -380,6 +421,9 @@ def main():
     roof = {"kernel": dom, "bound": "hbm", "achieved": kern[dom]["GB_s"], "peak": HBM_PEAK_GBS,
             "unit": "GB/s", "frac": kern[dom]["hbm_frac"],
             "traffic": traffic_from_profiles(dom, [srcs[dom], "speculative_decoding_verify_amd/csrc/ldv_device.hpp"])}
+    if peaks:
+        roof["measured_peaks"] = peaks
+        roof["frac_of_measured_copy"] = kern[dom]["GB_s"] / peaks["copy_GB_s"]
 
     cpu = None
     if not args.no_cpu:
