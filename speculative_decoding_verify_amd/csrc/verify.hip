@@ -17,9 +17,12 @@
 // depend only on Q, K, the gates and the topology; with them U = X R and
 // O = B0 + M R.
 //
-// One workgroup per (sequence, head, value tile of BV columns): G and C do
-// not depend on the value channel (Eq. (7) context), so value tiles are
-// independent.  Each wave owns 16 value rows of the tile.  Per block:
+// Drafts of up to 16 nodes go to verify_t16_kernel (below).  Longer ones
+// use one workgroup per (sequence, head, value tile of BV columns): G and C
+// do not depend on the value channel (Eq. (7) context), so value tiles are
+// independent; at d = 128 a tile is the whole head, so the T x T factor work
+// is done once per head.  Each wave owns one 16-row block of the tile (two
+// at 32 nodes).  Per block:
 //   1. issue the loads of q, k, v, the gates and the parent row, then of the
 //      block's S0 rows (fp32) straight into MFMA operand registers; the S0
 //      loads stay in flight through steps 2-4;
@@ -33,8 +36,10 @@
 //      on the fly from K Q^T (so C never takes LDS);
 //   5. S0 Q^T and S0 K^T on MFMA (S0 split into bf16 hi + lo terms) give
 //      B0^T and R^T for the wave's rows;
-//   6. U^T = R^T X^T and O^T = B0^T + R^T M^T on MFMA; each lane then holds
-//      four consecutive values of one node and stores them as a float4.
+//   6. U^T = R^T X^T and O^T = B0^T + R^T M^T on MFMA (with eight waves
+//      reading X and M, they are first packed once as bf16 hi | lo words);
+//      each lane then holds four consecutive values of one node and stores
+//      them as a float4.
 // Products with fp32 operands on both sides (X, M, R) carry both as hi + lo
 // bf16 terms (three MFMAs per step).  P_n / P_m is exp(log P_n - log P_m),
 // evaluated only for ancestor pairs (exponent <= 0 for gates in [0, 1]);
