@@ -539,7 +539,10 @@ __attribute__((amdgpu_waves_per_eu(VShape<D, TM>::WPE))) void verify_kernel(cons
             for (int mi = 0; mi < MBW; ++mi) frag_packed(s_rtp + (wrow0 + 16 * mi + c) * FLD, s, g, T16, rh[mi], rl[mi]);
 #pragma unroll
             for (int nb = 0; nb < NBM; ++nb) {
-                if (nb < NB) {
+                // rows of node block nb of X and M vanish past the block
+                // (both are lower triangular): skip k-steps starting there
+                // (with at most 32 nodes there is one k-step, never skipped)
+                if (nb < NB && (TM <= 32 || 32 * s < 16 * (nb + 1))) {
                     bf16x8 xh, xl, mh, ml;
                     frag_packed(s_xp + (nb * 16 + c) * FLD, s, g, T16, xh, xl);
                     frag_packed(s_mp + (nb * 16 + c) * FLD, s, g, T16, mh, ml);
@@ -573,7 +576,7 @@ __attribute__((amdgpu_waves_per_eu(VShape<D, TM>::WPE))) void verify_kernel(cons
             }
 #pragma unroll
             for (int nb = 0; nb < NBM; ++nb) {
-                if (nb < NB) {
+                if (nb < NB && (TM <= 32 || 32 * s < 16 * (nb + 1))) {  // as above
                     float4 x0, x1, m0, m1;
                     frag_f32(s_x + (nb * 16 + c) * FLD, s, g, T16, x0, x1);
                     frag_f32(s_g + (nb * 16 + c) * FLD, s, g, T16, m0, m1);
