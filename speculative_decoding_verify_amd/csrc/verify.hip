@@ -13,37 +13,43 @@
 // recurrence):
 //   C[n, m] = (P_n / P_m) q_n . k_m        (m = n included)
 //   G[n, m] = beta_n (P_n / P_m) k_n . k_m (m a strict ancestor)
-// G is strictly lower in topological order.  X = (I + G)^{-1} and M = C X
-// depend only on Q, K, the gates and the topology; with them U = X R and
-// O = B0 + M R.
+// G is strictly lower in topological order, so over 16-node blocks
+//   U_i = X_ii (R_i - sum_{k < i} G_ik U_k),   X_ii = (I + G_ii)^{-1}
+// (block forward substitution: only the diagonal blocks of (I + G)^{-1} are
+// ever formed), and O_j = B0_j + sum_{i <= j} C_ji U_i.
+//
+// All 16 x 16 products use one identity.  With a matrix P held in the MFMA
+// C layout (lane (c, g), register r holds P[4 g + r][c]), the same registers
+// are the B operand of a 16-deep product as they stand and the A operand of
+// one with P transposed, so mm(P, Q) = P^T Q needs no data movement; fp32
+// operands go in as bf16 hi + lo terms (two MFMAs, lo * lo dropped).
 //
 // Drafts of up to 16 nodes go to verify_t16_kernel (below).  Longer ones
 // use one workgroup per (sequence, head, value tile of BV columns): G and C
 // do not depend on the value channel (Eq. (7) context), so value tiles are
 // independent; at d = 128 a tile is the whole head, so the T x T factor work
-// is done once per head.  Each wave owns one 16-row block of the tile (two
-// at 32 nodes).  Per block:
+// is done once per head.  Each wave owns one 16-row value block of the tile
+// (two at 32 nodes).  Per workgroup:
 //   1. issue the loads of q, k, v, the gates and the parent row, then of the
-//      block's S0 rows (fp32) straight into MFMA operand registers; the S0
-//      loads stay in flight through steps 2-4;
+//      wave's S0 rows (fp32) straight into MFMA operand registers; the S0
+//      loads stay in flight through steps 2-3;
 //   2. stage Q, K (bf16) in LDS; wave 0 turns the parent row into ancestor
 //      masks and log P by pointer doubling;
-//   3. 16 x 16 blocks of K K^T on MFMA, masked and decay-scaled into G;
-//      the diagonal blocks of X are solved by forward substitution in
-//      registers, reading G from the MFMA accumulators with readlane;
-//   4. the off-diagonal blocks of X, X_ij = -X_ii sum_k G_ik X_kj (one stage
-//      per block diagonal), then M = C X on MFMA, with the blocks of C made
-//      on the fly from K Q^T (so C never takes LDS);
-//   5. S0 Q^T and S0 K^T on MFMA (S0 split into bf16 hi + lo terms) give
-//      B0^T and R^T for the wave's rows;
-//   6. U^T = R^T X^T and O^T = B0^T + R^T M^T on MFMA (with eight waves
-//      reading X and M, they are first packed once as bf16 hi | lo words);
-//      each lane then holds four consecutive values of one node and stores
-//      them as a float4.
-// Products with fp32 operands on both sides (X, M, R) carry both as hi + lo
-// bf16 terms (three MFMAs per step).  P_n / P_m is exp(log P_n - log P_m),
-// evaluated only for ancestor pairs (exponent <= 0 for gates in [0, 1]);
-// log a is clamped at -87 so that a zero gate gives a finite log.
+//   3. the factor tiles, spread over the waves: each is a 16 x 16 product of
+//      K or Q rows on MFMA, masked and decay-scaled in the accumulators and
+//      kept in LDS in the C layout as hi + lo terms:
+//        X_ii^T  (forward substitution in registers from G_ii),
+//        -G_ik^T (k < i),  C_ji^T (i <= j);
+//   4. S0 Q^T (value-major) and K S0^T (node-major) on MFMA give B0^T and R
+//      for the wave's value rows;
+//   5. per node block i: Y = R_i - sum_k G_ik U_k, then U_i = X_ii Y (kept
+//      for the later blocks) and U_i^T = Y^T X_ii^T (stored), and
+//      O_j^T += U_i^T C_ji^T for j >= i; O_i^T is then complete and stored,
+//      each lane writing four consecutive values of one node (float4).
+// Two workgroup barriers in all (after step 2 and after step 3).
+// P_n / P_m is exp(log P_n - log P_m), evaluated only for ancestor pairs
+// (exponent <= 0 for gates in [0, 1]); log a is clamped at -87 so that a
+// zero gate gives a finite log.
 #include "ldv_device.hpp"
 #include "ldv_kernels.hpp"
 
@@ -51,28 +57,59 @@
 
 namespace ldv {
 
+// acc + P^T Q for 16 x 16 fp32 matrices in the C layout, given as hi + lo
+// bf16 terms: the 32 k-slots of the first MFMA pair P_hi and P_lo with
+// Q_hi, the second adds P_hi^T Q_lo (lo * lo dropped).
+__device__ __forceinline__ floatx4 mm16_acc(floatx4 acc, u16x4 ph, u16x4 pl, u16x4 qh, u16x4 ql) {
+    acc = mfma16x16x32(join(ph, pl), join(qh, qh), acc);
+    return mfma16x16x32(join(ph, zero4()), join(ql, zero4()), acc);
+}
+
+// Makes v be computed at this point of the program.  An MFMA whose result
+// feeds only a store under a per-lane condition may otherwise be sunk into
+// that condition's exec-masked block together with its operand set-up,
+// which the masked lanes then skip although the MFMA reads their registers.
+__device__ __forceinline__ void keep_here(floatx4& v) { asm volatile("" : "+v"(v)); }
+
+__device__ __forceinline__ void split_x4(const floatx4 v, u16x4& hi, u16x4& lo) {
+    split4(make_float4(v[0], v[1], v[2], v[3]), hi, lo);
+}
+
+// A 16 x 16 factor tile in LDS: the hi terms of the 64 lanes' C-layout
+// registers, then the lo terms (8 bytes per lane each, conflict-free).
+__device__ __forceinline__ void tile_store(u16x4* tiles, int t, int lane, const floatx4 v) {
+    u16x4 hi, lo;
+    split_x4(v, hi, lo);
+    tiles[(2 * t) * kWave + lane] = hi;
+    tiles[(2 * t + 1) * kWave + lane] = lo;
+}
+
+__device__ __forceinline__ void tile_load(const u16x4* tiles, int t, int lane, u16x4& hi, u16x4& lo) {
+    hi = tiles[(2 * t) * kWave + lane];
+    lo = tiles[(2 * t + 1) * kWave + lane];
+}
+
 template <int D, int TM>
 struct VShape {
     // At d = 128 a block keeps the whole head (BV = 128), so the factor work
     // is done once per head: eight waves of 16 value rows at 64 nodes, four
-    // waves of two 16-row blocks (MBW = 2) at 32 nodes, where each operand
-    // fragment read from LDS then serves two MFMA row blocks.
+    // waves of two 16-row blocks (MBW = 2) at 32 nodes, where each factor
+    // tile read from LDS then serves two row blocks.
     static constexpr int BV = (D >= 128) ? 128 : (D >= 64 ? 64 : D);
     static constexpr int MBW = (TM == 32 && D >= 128) ? 2 : 1;  // 16-row blocks per wave
     static constexpr int NT = D / BV;         // value tiles per head
     static constexpr int NW = BV / (16 * MBW);  // waves per block
     static constexpr int KS = (D + 31) / 32;  // MFMA k-steps over d_k
     static constexpr int QKLD = D + 8;        // bf16 row stride of Q/K in LDS
-    static constexpr int FLD = TM + 4;        // fp32 row stride of the T x T factors and of R^T
     static constexpr int NBM = TM / 16;       // 16-node blocks at most
+    // factor tiles: X_ii^T (NBM), -G_ik^T (k < i), C_ji^T (i <= j)
+    static constexpr int NTILE = NBM * (NBM + 1);
+    static constexpr int TG0 = NBM;                        // first -G tile
+    static constexpr int TC0 = NBM + NBM * (NBM - 1) / 2;  // first C tile
     // waves per SIMD the registers must allow: two blocks per CU at 64 nodes
     // (eight waves each), three at 32 nodes with two row blocks per wave,
     // four otherwise
     static constexpr int WPE = MBW == 2 ? 3 : 4;
-    // pack X, M and R^T as bf16 hi | lo once before step 6 when eight waves
-    // read them (fewer waves: splitting at each read is cheaper than the
-    // extra pass and barrier)
-    static constexpr bool PACK = NW >= 8;
 };
 
 template <int D, int TM, bool F32IN>
@@ -80,12 +117,8 @@ struct VLds {
     using S = VShape<D, TM>;
     static constexpr int NPLANE = F32IN ? 4 : 2;  // q, k (hi and lo planes for fp32 input)
     static constexpr size_t qk = (size_t)NPLANE * TM * S::QKLD * 2;
-    static constexpr size_t rt = (size_t)S::BV * S::FLD * 4;  // R^T, after Q/K are dead
-    static constexpr size_t regionA = ((qk > rt ? qk : rt) + 15) / 16 * 16;
-    static constexpr size_t fac = (size_t)TM * S::FLD * 4;
-    static constexpr size_t off_g = regionA;    // G, later M
-    static constexpr size_t off_x = off_g + fac;
-    static constexpr size_t off_anc = off_x + fac;   // uint64 [TM]
+    static constexpr size_t off_t = (qk + 15) / 16 * 16;                          // factor tiles
+    static constexpr size_t off_anc = off_t + (size_t)S::NTILE * 2 * kWave * 8;  // uint64 [TM]
     static constexpr size_t off_f = off_anc + 8 * TM;  // float logp, P, beta [TM] each
     static constexpr size_t off_i = off_f + 12 * TM;   // int: bad flag
     static constexpr size_t total = off_i + 16;
@@ -96,20 +129,17 @@ __global__ __launch_bounds__((VShape<D, TM>::NW * kWave))
 __attribute__((amdgpu_waves_per_eu(VShape<D, TM>::WPE))) void verify_kernel(const VerifyArgs p) {
     using S = VShape<D, TM>;
     using L = VLds<D, TM, F32IN>;
-    constexpr int BV = S::BV, NW = S::NW, KS = S::KS, QKLD = S::QKLD, FLD = S::FLD, NBM = S::NBM, MBW = S::MBW;
+    constexpr int BV = S::BV, NW = S::NW, KS = S::KS, QKLD = S::QKLD, NBM = S::NBM, MBW = S::MBW;
     constexpr int NTHR = NW * kWave;
     constexpr int EPC = F32IN ? 4 : 8;                 // elements per 16-byte chunk
     constexpr int CPR = D / EPC;                       // chunks per q/k row
     constexpr int QKC = (TM * CPR + NTHR - 1) / NTHR;  // q (and k) chunks per thread
+    constexpr int LO = 2 * TM * QKLD;                  // offset of the lo planes (fp32 input)
 
     __shared__ __align__(16) unsigned char smem[L::total];
     unsigned short* s_q = reinterpret_cast<unsigned short*>(smem);
     unsigned short* s_k = s_q + TM * QKLD;
-    unsigned short* s_qlo = s_k + TM * QKLD;  // fp32 input only
-    unsigned short* s_klo = s_qlo + TM * QKLD;
-    float* s_rt = reinterpret_cast<float*>(smem);  // R^T [BV][FLD], aliases Q/K once they are dead
-    float* s_g = reinterpret_cast<float*>(smem + L::off_g);  // G [TM][FLD], then M
-    float* s_x = reinterpret_cast<float*>(smem + L::off_x);  // X [TM][FLD]
+    u16x4* s_tl = reinterpret_cast<u16x4*>(smem + L::off_t);
     uint64_t* s_anc = reinterpret_cast<uint64_t*>(smem + L::off_anc);
     float* s_logp = reinterpret_cast<float*>(smem + L::off_f);
     float* s_P = s_logp + TM;
@@ -126,11 +156,10 @@ __attribute__((amdgpu_waves_per_eu(VShape<D, TM>::WPE))) void verify_kernel(cons
     const size_t nb0 = (size_t)b * p.Ts + p.t0;  // node 0 of this sequence's (chunk of the) draft
     const int NB = (T + 15) >> 4;  // 16-node blocks in use
     const int T16 = NB * 16;
-    const int wrow0 = wave * 16 * MBW;        // first value row of this wave within the tile
-    const int vrow0 = tile * BV + wrow0;      // first value row (of S0, o, u) of this wave
+    const int vrow0 = tile * BV + wave * 16 * MBW;  // first value row (of S0, o, u) of this wave
 
     // 1. global loads.  Every small per-node input first, so that, loads
-    // completing in issue order, steps 2-4 can run while the S0 rows are in
+    // completing in issue order, steps 2-3 can run while the S0 rows are in
     // flight.  The loads are branch-free (indices clamped into range, values
     // of rows past T dropped later by selects): a load under a branch, or a
     // register overwritten while its load is pending, would make the
@@ -143,18 +172,21 @@ __attribute__((amdgpu_waves_per_eu(VShape<D, TM>::WPE))) void verify_kernel(cons
         qreg[i] = *reinterpret_cast<const u32x4*>(static_cast<const char*>(p.q) + off);
         kreg[i] = *reinterpret_cast<const u32x4*>(static_cast<const char*>(p.k) + off);
     }
-    // v[n][vrow0 + 16 mi + 4g .. +3] for the node n = 16 nb + c this lane
-    // holds in step 5
-    u16x4 vb[MBW][NBM];
-    float4 vf[MBW][NBM];
+    // v[n][vrow0 + 16 mi + c] for the nodes n = 16 nb + 4 g + r this lane
+    // holds in R (node-major C layout)
+    float vf[MBW][NBM][4];
+    unsigned short vb[MBW][NBM][4];
 #pragma unroll
     for (int mi = 0; mi < MBW; ++mi) {
 #pragma unroll
         for (int nb = 0; nb < NBM; ++nb) {
-            const int n = min(nb * 16 + c, T - 1);
-            const size_t off = ((nb0 + n) * H + h) * D + vrow0 + 16 * mi + 4 * g;
-            if constexpr (F32IN) vf[mi][nb] = *reinterpret_cast<const float4*>(static_cast<const float*>(p.v) + off);
-            else vb[mi][nb] = load_u16x4(static_cast<const unsigned short*>(p.v) + off);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int n = min(nb * 16 + 4 * g + r, T - 1);
+                const size_t off = ((nb0 + n) * H + h) * D + vrow0 + 16 * mi + c;
+                if constexpr (F32IN) vf[mi][nb][r] = static_cast<const float*>(p.v)[off];
+                else vb[mi][nb][r] = static_cast<const unsigned short*>(p.v)[off];
+            }
         }
     }
     const int nl = min(lane, T - 1);
@@ -169,7 +201,8 @@ __attribute__((amdgpu_waves_per_eu(VShape<D, TM>::WPE))) void verify_kernel(cons
     // log P at the node before a chunk (read from any valid entry otherwise)
     const float* lbp = p.logp_out ? p.logp_out : p.a;
     const float lbase_ld = lbp[((p.t0 > 0 ? nb0 - 1 : nb0)) * H + h];
-    // this lane's S0 rows (A operand row c of each of the wave's 16-row blocks)
+    // this lane's S0 rows (A operand row c of each of the wave's 16-row
+    // blocks, and the B operand column c of K S0^T)
     // (one row block is written without the row-block loop: with it the
     // compiler's allocation of the 64-node kernel spills)
     float4 sreg[MBW][KS][2];
@@ -210,10 +243,10 @@ __attribute__((amdgpu_waves_per_eu(VShape<D, TM>::WPE))) void verify_kernel(cons
                 u16x4 hi, lo;
                 split4(__builtin_bit_cast(float4, qv), hi, lo);
                 *reinterpret_cast<u16x4*>(s_q + row * QKLD + col) = hi;
-                *reinterpret_cast<u16x4*>(s_qlo + row * QKLD + col) = lo;
+                *reinterpret_cast<u16x4*>(s_q + LO + row * QKLD + col) = lo;
                 split4(__builtin_bit_cast(float4, kv), hi, lo);
                 *reinterpret_cast<u16x4*>(s_k + row * QKLD + col) = hi;
-                *reinterpret_cast<u16x4*>(s_klo + row * QKLD + col) = lo;
+                *reinterpret_cast<u16x4*>(s_k + LO + row * QKLD + col) = lo;
             }
         }
     }
@@ -258,179 +291,103 @@ __attribute__((amdgpu_waves_per_eu(VShape<D, TM>::WPE))) void verify_kernel(cons
     __syncthreads();
     if (s_int[0]) return;  // invalid parent row: nothing is written
 
-    // 3. G blocks (mb, nb), nb <= mb, from K K^T; zero above the block
-    //    diagonal.  Items 0 .. NB-1 are the diagonal blocks: block (i, i)
-    //    goes to wave i % NW, which also solves the diagonal block of X from
-    //    its G registers.
-    for (int it = wave; it < NB * NB; it += NW) {
-        int mb, nb;
-        if (it < NB) {
-            mb = nb = it;
-        } else {
-            const int r = it - NB;  // ordered pairs mb != nb
-            mb = r / (NB - 1);
-            nb = r % (NB - 1);
-            if (nb >= mb) ++nb;
-        }
-        if (nb > mb) {  // above the diagonal: zero G (later M) and X
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int n = mb * 16 + 4 * g + r, m = nb * 16 + c;
-                s_g[n * FLD + m] = 0.f;
-                s_x[n * FLD + m] = 0.f;
-            }
-            continue;
-        }
-        floatx4 acc_g = {0.f, 0.f, 0.f, 0.f};
-        const unsigned short* krow_a = s_k + (mb * 16 + c) * QKLD;
-        const unsigned short* krow_b = s_k + (nb * 16 + c) * QKLD;
+    // 3a. diagonal blocks: X_ii^T.  K_i K_i^T in the C layout is G_ii[n][m]
+    //     before scaling (rows n = 16 i + 4 g + r, column m = 16 i + c).
+    for (int i = wave; i < NB; i += NW) {
+        floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+        const unsigned short* krow = s_k + (16 * i + c) * QKLD;
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
-            const bf16x8 bk = frag_row<D>(krow_b, s, g);
-            const bf16x8 ak = frag_row<D>(krow_a, s, g);
-            acc_g = mfma16x16x32(ak, bk, acc_g);
+            const bf16x8 bk = frag_row<D>(krow, s, g);
+            acc = mfma16x16x32(bk, bk, acc);
             if constexpr (F32IN) {
-                acc_g = mfma16x16x32(ak, frag_row<D>(s_klo + (nb * 16 + c) * QKLD, s, g), acc_g);
-                acc_g = mfma16x16x32(frag_row<D>(s_klo + (mb * 16 + c) * QKLD, s, g), bk, acc_g);
+                const bf16x8 bkl = frag_row<D>(krow + LO, s, g);
+                acc = mfma16x16x32(bk, bkl, acc);
+                acc = mfma16x16x32(bkl, bk, acc);
             }
         }
-        // lane (c, g) holds rows n = 16 mb + 4 g + r, column m = 16 nb + c
-        const int m = nb * 16 + c;
+        const int m = 16 * i + c;
         const float lpm = s_logp[m];
         float gv[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int n = mb * 16 + 4 * g + r;
-            const uint64_t anc = s_anc[n];
-            const bool on_path = m < T && n < T && (((anc | (1ull << n)) >> m) & 1ull);
-            const bool strict = on_path && m != n;
-            const float dec = on_path ? expf(s_logp[n] - lpm) : 0.f;
-            gv[r] = strict ? s_beta[n] * dec * acc_g[r] : 0.f;
-            s_g[n * FLD + m] = gv[r];
+            const int n = 16 * i + 4 * g + r;
+            const bool strict = ((s_anc[n] >> m) & 1ull) != 0ull;
+            gv[r] = strict ? s_beta[n] * expf(s_logp[n] - lpm) * acc[r] : 0.f;
         }
-        if (mb == nb) {
-            // X_ii = (I + G_ii)^{-1}: lane j < 16 solves column j,
-            //   x[r] = [r == j] - sum_{t < r} G[r][t] x[t],
-            // with G[r][t] read from lane t + 16 (r / 4), register r % 4
-            float x[16];
+        // row c of X = (I + G_ii)^{-1} in every lane of column c: from
+        // X (I + G) = I, X[c][t] = [t == c] - sum_{s > t} X[c][s] G[s][t],
+        // with G[s][t] read from lane t + 16 (s / 4), register s % 4
+        float x[16];
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                float acc = (r == c) ? 1.f : 0.f;
+        for (int t = 15; t >= 0; --t) {
+            float a = (t == c) ? 1.f : 0.f;
 #pragma unroll
-                for (int t = 0; t < r; ++t) acc -= readlane_f(gv[r & 3], t + 16 * (r >> 2)) * x[t];
-                x[r] = acc;
-            }
-            if (g == 0) {
-#pragma unroll
-                for (int r = 0; r < 16; ++r) s_x[(mb * 16 + r) * FLD + mb * 16 + c] = x[r];
-            }
+            for (int s = t + 1; s < 16; ++s) a -= x[s] * readlane_f(gv[s & 3], t + 16 * (s >> 2));
+            x[t] = a;
         }
-    }
-    __syncthreads();
-
-    // 4a. off-diagonal blocks of X, one block diagonal d = i - j per stage:
-    //     X_ij = -X_ii S, S = sum_{k=j}^{i-1} G_ik X_kj
-    for (int d = 1; d < NB; ++d) {
-        for (int it = wave; it < NB - d; it += NW) {
-            const int j = it, i = it + d;
-            const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
-            floatx4 sacc = {0.f, 0.f, 0.f, 0.f};
-            const float* grow = s_g + (16 * i + c) * FLD;
-            const float* xcol = s_x + 16 * j + c;
-            // k-steps of 32 nodes over [16 j, 16 i); runs outside read as zero
-            for (int s = j / 2; 32 * s < 16 * i; ++s) {
-                const int k0 = 32 * s + 4 * g;
-                const bool v0 = k0 >= 16 * j && k0 < 16 * i;
-                const bool v1 = k0 + 16 >= 16 * j && k0 + 16 < 16 * i;
-                const float4 a0 = v0 ? *reinterpret_cast<const float4*>(grow + k0) : z;
-                const float4 a1 = v1 ? *reinterpret_cast<const float4*>(grow + k0 + 16) : z;
-                // B[k][n] = X[k][16 j + n]: four rows down one column
-                const float4 b0 = v0 ? make_float4(xcol[(k0 + 0) * FLD], xcol[(k0 + 1) * FLD], xcol[(k0 + 2) * FLD],
-                                                   xcol[(k0 + 3) * FLD])
-                                     : z;
-                const float4 b1 = v1 ? make_float4(xcol[(k0 + 16) * FLD], xcol[(k0 + 17) * FLD],
-                                                   xcol[(k0 + 18) * FLD], xcol[(k0 + 19) * FLD])
-                                     : z;
-                bf16x8 ah, al, bh, bl;
-                split8(a0, a1, ah, al);
-                split8(b0, b1, bh, bl);
-                sacc = mma3(sacc, ah, al, bh, bl);
-            }
-            // S in C layout (lane (c, g): rows 4 g .. 4 g + 3 of column c) is
-            // already the B operand of a 16-deep product
-            bf16x8 sh, sl, ah, al;
-            split8(make_float4(sacc[0], sacc[1], sacc[2], sacc[3]), z, sh, sl);
-            split8(*reinterpret_cast<const float4*>(s_x + (16 * i + c) * FLD + 16 * i + 4 * g), z, ah, al);
-            floatx4 xacc = {0.f, 0.f, 0.f, 0.f};
-            xacc = mma3(xacc, ah, al, sh, sl);
+        // X_ii^T in the C layout: register r of lane (c, g) is X[c][4 g + r]
+        floatx4 xt;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) s_x[(16 * i + 4 * g + r) * FLD + 16 * j + c] = -xacc[r];
-        }
-        __syncthreads();
+        for (int r = 0; r < 4; ++r) xt[r] = g == 0 ? x[r] : g == 1 ? x[4 + r] : g == 2 ? x[8 + r] : x[12 + r];
+        tile_store(s_tl, i, lane, xt);
     }
 
-    // 4b. M = C X on the blocks (i, j), j <= i, into the G area
-    //     (M_ij = sum_{k=j}^{i} C_ik X_kj; every X block is final, so G is
-    //     no longer read).  The A operand, row n = 16 i + c of C at the
-    //     k-slots m = 32 s + 4 g + r and m + 16, comes from the K Q^T blocks
-    //     of node blocks 2 s and 2 s + 1 against block i: in the MFMA C
-    //     layout those hold exactly k_m . q_n for this lane's (n, m).
-    for (int it = wave; it < NB * (NB + 1) / 2; it += NW) {
-        int i = 0;
-        while ((i + 1) * (i + 2) / 2 <= it) ++i;
-        const int j = it - i * (i + 1) / 2;
-        const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
-        const int n = 16 * i + c;
-        const uint64_t path_n = s_anc[n] | (1ull << n);
-        const float lpn = s_logp[n];
-        const unsigned short* qrow = s_q + n * QKLD;
-        floatx4 macc = {0.f, 0.f, 0.f, 0.f};
-        const float* xcol = s_x + 16 * j + c;
-        for (int s = j / 2; 32 * s < 16 * (i + 1); ++s) {
-            const int k0 = 32 * s + 4 * g;
-            const bool v0 = k0 >= 16 * j && k0 < 16 * (i + 1);
-            const bool v1 = k0 + 16 >= 16 * j && k0 + 16 < 16 * (i + 1);
-            floatx4 t0 = {0.f, 0.f, 0.f, 0.f}, t1 = t0;  // k_m . q_n, m in blocks 2 s and 2 s + 1
+    // 3b. -G_ik^T (k < i) and C_ji^T (i <= j).  Item it covers the tile of
+    //     rows n in node block bn and columns m in block bm: A = k rows of
+    //     block bm, B = k or q rows of block bn, so the accumulator holds
+    //     k_m . k_n (or k_m . q_n) at register r of lane (c, g) for
+    //     m = 16 bm + 4 g + r, n = 16 bn + c.  The items start at wave NB so
+    //     that the waves holding a diagonal block take fewer of them.
+    {
+        const int nneg = NB * (NB - 1) / 2;
+        for (int it = (wave + NW - NB % NW) % NW; it < NB * NB; it += NW) {
+            const bool isc = it >= nneg;
+            int bn, bm, t;
+            if (!isc) {
+                int i = 1;
+                while (i * (i + 1) / 2 <= it) ++i;
+                bn = i;
+                bm = it - i * (i - 1) / 2;
+                t = S::TG0 + i * (i - 1) / 2 + bm;
+            } else {
+                const int rr = it - nneg;
+                int j = 0;
+                while ((j + 1) * (j + 2) / 2 <= rr) ++j;
+                bn = j;
+                bm = rr - j * (j + 1) / 2;
+                t = S::TC0 + j * (j + 1) / 2 + bm;
+            }
+            const unsigned short* arow = s_k + (16 * bm + c) * QKLD;
+            const unsigned short* brow = (isc ? s_q : s_k) + (16 * bn + c) * QKLD;
+            floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                const bf16x8 bq = frag_row<D>(qrow, ks, g);
-                const bf16x8 ak0 = frag_row<D>(s_k + (32 * s + c) * QKLD, ks, g);
-                const bf16x8 ak1 = frag_row<D>(s_k + (32 * s + 16 + c) * QKLD, ks, g);
-                t0 = mfma16x16x32(ak0, bq, t0);
-                t1 = mfma16x16x32(ak1, bq, t1);
+            for (int s = 0; s < KS; ++s) {
+                const bf16x8 fa = frag_row<D>(arow, s, g), fb = frag_row<D>(brow, s, g);
+                acc = mfma16x16x32(fa, fb, acc);
                 if constexpr (F32IN) {
-                    const bf16x8 bql = frag_row<D>(s_qlo + n * QKLD, ks, g);
-                    t0 = mfma16x16x32(ak0, bql, t0);
-                    t0 = mfma16x16x32(frag_row<D>(s_klo + (32 * s + c) * QKLD, ks, g), bq, t0);
-                    t1 = mfma16x16x32(ak1, bql, t1);
-                    t1 = mfma16x16x32(frag_row<D>(s_klo + (32 * s + 16 + c) * QKLD, ks, g), bq, t1);
+                    acc = mfma16x16x32(fa, frag_row<D>(brow + LO, s, g), acc);
+                    acc = mfma16x16x32(frag_row<D>(arow + LO, s, g), fb, acc);
                 }
             }
-            float ca[8];
+            const int n = 16 * bn + c;
+            // m on the path of n (C: n itself included; G: strict ancestors)
+            const uint64_t pathn = s_anc[n] | (isc ? (1ull << n) : 0ull);
+            const float lpn = s_logp[n], sc = isc ? 1.f : -s_beta[n];
+            floatx4 v;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int m0 = k0 + r, m1 = k0 + 16 + r;
-                ca[r] = (v0 && ((path_n >> m0) & 1ull)) ? expf(lpn - s_logp[m0]) * t0[r] : 0.f;
-                ca[4 + r] = (v1 && ((path_n >> m1) & 1ull)) ? expf(lpn - s_logp[m1]) * t1[r] : 0.f;
+                const int m = 16 * bm + 4 * g + r;
+                v[r] = ((pathn >> m) & 1ull) ? sc * expf(lpn - s_logp[m]) * acc[r] : 0.f;
             }
-            const float4 b0 = v0 ? make_float4(xcol[(k0 + 0) * FLD], xcol[(k0 + 1) * FLD], xcol[(k0 + 2) * FLD],
-                                               xcol[(k0 + 3) * FLD])
-                                 : z;
-            const float4 b1 = v1 ? make_float4(xcol[(k0 + 16) * FLD], xcol[(k0 + 17) * FLD],
-                                               xcol[(k0 + 18) * FLD], xcol[(k0 + 19) * FLD])
-                                 : z;
-            bf16x8 ah, al, bh, bl;
-            split8(make_float4(ca[0], ca[1], ca[2], ca[3]), make_float4(ca[4], ca[5], ca[6], ca[7]), ah, al);
-            split8(b0, b1, bh, bl);
-            macc = mma3(macc, ah, al, bh, bl);
+            tile_store(s_tl, t, lane, v);
         }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) s_g[(16 * i + 4 * g + r) * FLD + 16 * j + c] = macc[r];
     }
 
-    // 5. S0 Q^T and S0 K^T for the wave's value rows (A = S0 rows, split
-    //    hi + lo; B = Q / K rows).  Lane (c, g) ends with value rows
-    //    16 mi + 4 g + r and node n = 16 nb + c of each node block.
+    // 4. S0 Q^T (A = S0 rows, B = q rows: value-major, lane (c, g) holds
+    //    value rows 4 g + r of node 16 nb + c) and K S0^T (A = k rows,
+    //    B = S0 rows: node-major, nodes 16 nb + 4 g + r of value row c).
+    //    Both read only Q, K and registers, so they go before the barrier.
     floatx4 accq[MBW][NBM], acck[MBW][NBM];
 #pragma unroll
     for (int mi = 0; mi < MBW; ++mi) {
@@ -448,161 +405,102 @@ __attribute__((amdgpu_waves_per_eu(VShape<D, TM>::WPE))) void verify_kernel(cons
 #pragma unroll
         for (int nb = 0; nb < NBM; ++nb) {
             if (nb < NB) {
-                const bf16x8 bq = frag_row<D>(s_q + (nb * 16 + c) * QKLD, s, g);
-                const bf16x8 bk = frag_row<D>(s_k + (nb * 16 + c) * QKLD, s, g);
+                const unsigned short* qrow = s_q + (nb * 16 + c) * QKLD;
+                const unsigned short* krow = s_k + (nb * 16 + c) * QKLD;
+                const bf16x8 bq = frag_row<D>(qrow, s, g);
+                const bf16x8 bk = frag_row<D>(krow, s, g);
 #pragma unroll
                 for (int mi = 0; mi < MBW; ++mi) {
                     accq[mi][nb] = mfma16x16x32(sh[mi], bq, accq[mi][nb]);
                     accq[mi][nb] = mfma16x16x32(sl[mi], bq, accq[mi][nb]);
-                    acck[mi][nb] = mfma16x16x32(sh[mi], bk, acck[mi][nb]);
-                    acck[mi][nb] = mfma16x16x32(sl[mi], bk, acck[mi][nb]);
+                    acck[mi][nb] = mfma16x16x32(bk, sh[mi], acck[mi][nb]);
+                    acck[mi][nb] = mfma16x16x32(bk, sl[mi], acck[mi][nb]);
                 }
                 if constexpr (F32IN) {
-                    const bf16x8 bql = frag_row<D>(s_qlo + (nb * 16 + c) * QKLD, s, g);
-                    const bf16x8 bkl = frag_row<D>(s_klo + (nb * 16 + c) * QKLD, s, g);
+                    const bf16x8 bql = frag_row<D>(qrow + LO, s, g);
+                    const bf16x8 bkl = frag_row<D>(krow + LO, s, g);
 #pragma unroll
                     for (int mi = 0; mi < MBW; ++mi) {
                         accq[mi][nb] = mfma16x16x32(sh[mi], bql, accq[mi][nb]);
-                        acck[mi][nb] = mfma16x16x32(sh[mi], bkl, acck[mi][nb]);
+                        acck[mi][nb] = mfma16x16x32(bkl, sh[mi], acck[mi][nb]);
                     }
                 }
             }
         }
     }
-    // B0^T[i][n] = P_n (S0 q_n)[i];  R^T[i][n] = beta_n (v_n[i] - P_n (S0 k_n)[i])
-    floatx4 b0t[MBW][NBM];
-    float rtv[MBW][NBM][4];
+    // B0^T[v][n] = P_n (S0 q_n)[v] (the O^T accumulators start there);
+    // R[n][v] = beta_n (v_n[v] - P_n (S0 k_n)[v]), zero past T (beta = 0)
+    floatx4 acco[MBW][NBM], rn[MBW][NBM];
 #pragma unroll
     for (int nb = 0; nb < NBM; ++nb) {
-        const int n = nb * 16 + c;
-        const bool nv = nb < NB && n < T;
-        const float P = nv ? s_P[n] : 0.f, be = nv ? s_beta[n] : 0.f;
-#pragma unroll
-        for (int mi = 0; mi < MBW; ++mi) {
-            float vv[4];
-            if constexpr (F32IN) {
-                vv[0] = vf[mi][nb].x;
-                vv[1] = vf[mi][nb].y;
-                vv[2] = vf[mi][nb].z;
-                vv[3] = vf[mi][nb].w;
-            } else {
-#pragma unroll
-                for (int r = 0; r < 4; ++r) vv[r] = bf16_val(vb[mi][nb][r]);
-            }
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                b0t[mi][nb][r] = P * accq[mi][nb][r];
-                rtv[mi][nb][r] = nv ? be * (vv[r] - P * acck[mi][nb][r]) : 0.f;
-            }
-        }
-    }
-    __syncthreads();  // Q/K dead in every wave; X and M complete
-
-    // 6. U^T = R^T X^T and O^T = B0^T + R^T M^T (K = nodes, 32 per step).
-    //    R^T goes to the Q/K area; each wave reads back only the rows it
-    //    wrote (LDS keeps one wave's operations in order).
-    const int ksteps = (T16 + 31) / 32;
-    floatx4 accu[MBW][NBM], acco[MBW][NBM];
-#pragma unroll
-    for (int mi = 0; mi < MBW; ++mi) {
-#pragma unroll
-        for (int nb = 0; nb < NBM; ++nb) {
-            accu[mi][nb] = floatx4{0.f, 0.f, 0.f, 0.f};
-            acco[mi][nb] = b0t[mi][nb];
-        }
-    }
-    if constexpr (S::PACK) {
-        // R^T, X and M as packed hi | lo words, X and M converted in place
-        uint32_t* s_rtp = reinterpret_cast<uint32_t*>(s_rt);
-        uint32_t* s_xp = reinterpret_cast<uint32_t*>(s_x);
-        uint32_t* s_mp = reinterpret_cast<uint32_t*>(s_g);
-#pragma unroll
-        for (int mi = 0; mi < MBW; ++mi) {
-#pragma unroll
-            for (int nb = 0; nb < NBM; ++nb) {
-                if (nb < NB) {
-#pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        s_rtp[(wrow0 + 16 * mi + 4 * g + r) * FLD + nb * 16 + c] = pack_hilo(rtv[mi][nb][r]);
-                }
-            }
-        }
-        for (int e = tid; e < T16 * T16; e += NTHR) {
-            const int row = e / T16, col = e - row * T16;
-            s_xp[row * FLD + col] = pack_hilo(s_x[row * FLD + col]);
-            s_mp[row * FLD + col] = pack_hilo(s_g[row * FLD + col]);
-        }
-        __syncthreads();
-        for (int s = 0; s < ksteps; ++s) {
-            bf16x8 rh[MBW], rl[MBW];
-#pragma unroll
-            for (int mi = 0; mi < MBW; ++mi) frag_packed(s_rtp + (wrow0 + 16 * mi + c) * FLD, s, g, T16, rh[mi], rl[mi]);
-#pragma unroll
-            for (int nb = 0; nb < NBM; ++nb) {
-                // rows of node block nb of X and M vanish past the block
-                // (both are lower triangular): skip k-steps starting there
-                // (with at most 32 nodes there is one k-step, never skipped)
-                if (nb < NB && (TM <= 32 || 32 * s < 16 * (nb + 1))) {
-                    bf16x8 xh, xl, mh, ml;
-                    frag_packed(s_xp + (nb * 16 + c) * FLD, s, g, T16, xh, xl);
-                    frag_packed(s_mp + (nb * 16 + c) * FLD, s, g, T16, mh, ml);
-#pragma unroll
-                    for (int mi = 0; mi < MBW; ++mi) {
-                        accu[mi][nb] = mma3(accu[mi][nb], rh[mi], rl[mi], xh, xl);
-                        acco[mi][nb] = mma3(acco[mi][nb], rh[mi], rl[mi], mh, ml);
-                    }
-                }
-            }
-        }
-    } else {
-#pragma unroll
-        for (int mi = 0; mi < MBW; ++mi) {
-#pragma unroll
-            for (int nb = 0; nb < NBM; ++nb) {
-                if (nb < NB) {
-#pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        s_rt[(wrow0 + 16 * mi + 4 * g + r) * FLD + nb * 16 + c] = rtv[mi][nb][r];
-                }
-            }
-        }
-        for (int s = 0; s < ksteps; ++s) {
-            bf16x8 rh[MBW], rl[MBW];
+        if (nb < NB) {
+            const float Pc = s_P[nb * 16 + c];
+            const float4 P4 = *reinterpret_cast<const float4*>(s_P + nb * 16 + 4 * g);
+            const float4 B4 = *reinterpret_cast<const float4*>(s_beta + nb * 16 + 4 * g);
+            const float Pr[4] = {P4.x, P4.y, P4.z, P4.w}, Br[4] = {B4.x, B4.y, B4.z, B4.w};
 #pragma unroll
             for (int mi = 0; mi < MBW; ++mi) {
-                float4 a0, a1;
-                frag_f32(s_rt + (wrow0 + 16 * mi + c) * FLD, s, g, T16, a0, a1);
-                split8(a0, a1, rh[mi], rl[mi]);
-            }
 #pragma unroll
-            for (int nb = 0; nb < NBM; ++nb) {
-                if (nb < NB && (TM <= 32 || 32 * s < 16 * (nb + 1))) {  // as above
-                    float4 x0, x1, m0, m1;
-                    frag_f32(s_x + (nb * 16 + c) * FLD, s, g, T16, x0, x1);
-                    frag_f32(s_g + (nb * 16 + c) * FLD, s, g, T16, m0, m1);
-                    bf16x8 xh, xl, mh, ml;
-                    split8(x0, x1, xh, xl);
-                    split8(m0, m1, mh, ml);
-#pragma unroll
-                    for (int mi = 0; mi < MBW; ++mi) {
-                        accu[mi][nb] = mma3(accu[mi][nb], rh[mi], rl[mi], xh, xl);
-                        acco[mi][nb] = mma3(acco[mi][nb], rh[mi], rl[mi], mh, ml);
-                    }
+                for (int r = 0; r < 4; ++r) {
+                    float vv;
+                    if constexpr (F32IN) vv = vf[mi][nb][r];
+                    else vv = bf16_val(vb[mi][nb][r]);
+                    acco[mi][nb][r] = Pc * accq[mi][nb][r];
+                    rn[mi][nb][r] = Br[r] * (vv - Pr[r] * acck[mi][nb][r]);
                 }
             }
         }
     }
-    // lane (c, g): node n = 16 nb + c, value rows vrow0 + 16 mi + 4 g .. +3
+    __syncthreads();  // every factor tile written
+
+    // 5. forward substitution over node blocks; O^T block by block
+    u16x4 uh[MBW][NBM], ul[MBW][NBM];
 #pragma unroll
-    for (int mi = 0; mi < MBW; ++mi) {
+    for (int i = 0; i < NBM; ++i) {
+        if (i < NB) {
+            floatx4 y[MBW];
 #pragma unroll
-        for (int nb = 0; nb < NBM; ++nb) {
-            const int n = nb * 16 + c;
-            if (nb < NB && n < T) {
-                const size_t off = ((nb0 + n) * H + h) * D + vrow0 + 16 * mi + 4 * g;
-                st_stream(p.o + off, make_float4(acco[mi][nb][0], acco[mi][nb][1], acco[mi][nb][2], acco[mi][nb][3]));
-                if (p.u_out)
-                    st_stream(p.u_out + off, make_float4(accu[mi][nb][0], accu[mi][nb][1], accu[mi][nb][2], accu[mi][nb][3]));
+            for (int mi = 0; mi < MBW; ++mi) y[mi] = rn[mi][i];
+#pragma unroll
+            for (int k = 0; k < i; ++k) {  // Y -= G_ik U_k
+                u16x4 th, tl;
+                tile_load(s_tl, S::TG0 + i * (i - 1) / 2 + k, lane, th, tl);
+#pragma unroll
+                for (int mi = 0; mi < MBW; ++mi) y[mi] = mm16_acc(y[mi], th, tl, uh[mi][k], ul[mi][k]);
+            }
+            u16x4 xh, xl;
+            tile_load(s_tl, i, lane, xh, xl);
+            const int n = 16 * i + c;
+#pragma unroll
+            for (int mi = 0; mi < MBW; ++mi) {
+                u16x4 yh, yl;
+                split_x4(y[mi], yh, yl);
+                const floatx4 z = {0.f, 0.f, 0.f, 0.f};
+                split_x4(mm16_acc(z, xh, xl, yh, yl), uh[mi][i], ul[mi][i]);  // U_i = X_ii Y
+                if (p.u_out) {
+                    floatx4 ut = mm16_acc(z, yh, yl, xh, xl);  // U_i^T = Y^T X_ii^T
+                    keep_here(ut);
+                    if (n < T)
+                        st_stream(p.u_out + ((nb0 + n) * H + h) * D + vrow0 + 16 * mi + 4 * g,
+                                  make_float4(ut[0], ut[1], ut[2], ut[3]));
+                }
+            }
+#pragma unroll
+            for (int j = i; j < NBM; ++j) {  // O_j^T += U_i^T C_ji^T
+                if (j < NB) {
+                    u16x4 ch, cl;
+                    tile_load(s_tl, S::TC0 + j * (j + 1) / 2 + i, lane, ch, cl);
+#pragma unroll
+                    for (int mi = 0; mi < MBW; ++mi) acco[mi][j] = mm16_acc(acco[mi][j], uh[mi][i], ul[mi][i], ch, cl);
+                }
+            }
+#pragma unroll
+            for (int mi = 0; mi < MBW; ++mi) keep_here(acco[mi][i]);
+            if (n < T) {
+#pragma unroll
+                for (int mi = 0; mi < MBW; ++mi)
+                    st_stream(p.o + ((nb0 + n) * H + h) * D + vrow0 + 16 * mi + 4 * g,
+                              make_float4(acco[mi][i][0], acco[mi][i][1], acco[mi][i][2], acco[mi][i][3]));
             }
         }
     }
@@ -611,11 +509,8 @@ __attribute__((amdgpu_waves_per_eu(VShape<D, TM>::WPE))) void verify_kernel(cons
 // ---------------------------------------------------------------------------
 // T <= 16: one 16 x 16 node block, so one wave does the whole factor algebra
 // of the head in registers, and every wave of the block then handles 16
-// value rows of the head.  With a matrix P held in the MFMA C layout (lane (c, g), register r holds
-// P[4 g + r][c]), the same registers are the B operand of a 16-deep product
-// as they stand and the A operand of one with P transposed, so
-//   mm(P, Q) = P^T Q
-// needs no data movement.  K K^T is symmetric, so G and G^T (and C and C^T
+// value rows of the head, all products being mm(P, Q) = P^T Q on C-layout
+// registers (top of this file).  K K^T is symmetric, so G and G^T (and C and C^T
 // from Q K^T and K Q^T) come out of the accumulators directly, and
 //   X = (I + G)^-1 = (I - G)(I + G^2)(I + G^4)(I + G^8)      (G^16 = 0)
 // is built by repeated squaring, stopping at the stage the tree depth
@@ -624,14 +519,12 @@ __attribute__((amdgpu_waves_per_eu(VShape<D, TM>::WPE))) void verify_kernel(cons
 // through LDS in the same C layout (one float4 per lane), and the only LDS
 // staging is Q and K.
 
-// P^T Q for 16 x 16 fp32 matrices in C layout (hi + lo split, lo * lo dropped)
+// P^T Q for 16 x 16 fp32 matrices in the C layout
 __device__ __forceinline__ floatx4 mm16(const floatx4 P, const floatx4 Q) {
     u16x4 ph, pl, qh, ql;
-    split4(make_float4(P[0], P[1], P[2], P[3]), ph, pl);
-    split4(make_float4(Q[0], Q[1], Q[2], Q[3]), qh, ql);
-    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-    acc = mfma16x16x32(join(ph, pl), join(qh, qh), acc);  // (P_hi + P_lo)^T Q_hi
-    return mfma16x16x32(join(ph, zero4()), join(ql, zero4()), acc);  // + P_hi^T Q_lo
+    split_x4(P, ph, pl);
+    split_x4(Q, qh, ql);
+    return mm16_acc(floatx4{0.f, 0.f, 0.f, 0.f}, ph, pl, qh, ql);
 }
 
 // I + s P for a C-layout matrix (s = +1 or -1), lane (c, g)
