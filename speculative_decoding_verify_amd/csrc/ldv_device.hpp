@@ -145,6 +145,39 @@ __device__ __forceinline__ void st_stream(float* p, const float4 v) {
     __builtin_nontemporal_store(w, reinterpret_cast<global_ptr<f32x4>>((global_ptr<float>)p));
 }
 
+// Raw buffer views.  A view covers `bytes` bytes from a base address held in
+// scalar registers; the memory unit range-checks every access against it,
+// so loads at or past the end return zero and stores there are dropped.
+// The draft-row loads and output stores use one view per (sequence, head)
+// whose range ends at row T: rows past T then need no clamping, selects or
+// branches, and each access costs only its 32-bit offset.  Offsets go in
+// the vector operand (the scalar offset is left 0), and no access straddles
+// the end of a view.
+typedef __amdgpu_buffer_rsrc_t buf_t;
+constexpr int kBufWord3 = 0x00020000;  // descriptor word 3 of a raw (untyped) gfx9 buffer
+constexpr int kBufNT = 2;              // cache policy bits: non-temporal
+
+__device__ __forceinline__ buf_t make_buf(const void* p, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, (int)bytes, kBufWord3);
+}
+__device__ __forceinline__ u32x4 buf_ld128(buf_t b, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b128(b, off, 0, 0);
+}
+__device__ __forceinline__ float4 buf_ldf4(buf_t b, uint32_t off) {
+    const u32x4 r = __builtin_amdgcn_raw_buffer_load_b128(b, off, 0, 0);
+    return make_float4(__uint_as_float(r[0]), __uint_as_float(r[1]), __uint_as_float(r[2]), __uint_as_float(r[3]));
+}
+__device__ __forceinline__ float buf_ldf(buf_t b, uint32_t off) {
+    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(b, off, 0, 0));
+}
+__device__ __forceinline__ unsigned short buf_ld16(buf_t b, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b16(b, off, 0, 0);
+}
+__device__ __forceinline__ void buf_st_stream(buf_t b, uint32_t off, const float4 v) {
+    const f32x4 w = {v.x, v.y, v.z, v.w};
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, w), b, off, 0, kBufNT);
+}
+
 // Four bf16 values (8 bytes) from LDS or global memory.
 __device__ __forceinline__ u16x4 load_u16x4(const unsigned short* p) {
     return *reinterpret_cast<const u16x4*>(p);

@@ -38,7 +38,7 @@
 //   3. the factor tiles, spread over the waves: each is a 16 x 16 product of
 //      K or Q rows on MFMA, masked and decay-scaled in the accumulators and
 //      kept in LDS in the C layout as hi + lo terms:
-//        X_ii^T  (forward substitution in registers from G_ii),
+//        X_ii^T  (by repeated squaring of G_ii, on MFMA),
 //        -G_ik^T (k < i),  C_ji^T (i <= j);
 //   4. S0 Q^T (value-major) and K S0^T (node-major) on MFMA give B0^T and R
 //      for the wave's value rows;
@@ -57,37 +57,64 @@
 
 namespace ldv {
 
-// acc + P^T Q for 16 x 16 fp32 matrices in the C layout, given as hi + lo
-// bf16 terms: the 32 k-slots of the first MFMA pair P_hi and P_lo with
-// Q_hi, the second adds P_hi^T Q_lo (lo * lo dropped).
-__device__ __forceinline__ floatx4 mm16_acc(floatx4 acc, u16x4 ph, u16x4 pl, u16x4 qh, u16x4 ql) {
-    acc = mfma16x16x32(join(ph, pl), join(qh, qh), acc);
-    return mfma16x16x32(join(ph, zero4()), join(ql, zero4()), acc);
-}
+// A 16 x 16 fp32 matrix held in the C layout, as bf16 operand forms: the
+// pair [hi | lo] (k-slots 8 g .. 8 g + 3 take rows 4 g .. 4 g + 3 of the hi
+// term, 8 g + 4 .. 8 g + 7 the same rows of the lo term) and the doubled
+// forms [hi | hi], [lo | lo].  mm(P, Q) = P^T Q takes one operand as a pair
+// and the other doubled, on either side:
+//   P^T Q = MFMA([P_hi|P_lo], [Q_hi|Q_hi]) + MFMA([P_hi|P_lo], [Q_lo|Q_lo])
+//         = MFMA([P_hi|P_hi], [Q_hi|Q_lo]) + MFMA([P_lo|P_lo], [Q_hi|Q_lo])
+//         = (P_hi + P_lo)^T (Q_hi + Q_lo),
+// every cross term kept.  Factor tiles are stored doubled (read straight
+// into operand registers); values a wave produces and reuses are kept as
+// pairs (four registers).
+struct Frag16 {
+    bf16x8 pr, dh, dl;
+};
 
-// Makes v be computed at this point of the program.  An MFMA whose result
-// feeds only a store under a per-lane condition may otherwise be sunk into
-// that condition's exec-masked block together with its operand set-up,
-// which the masked lanes then skip although the MFMA reads their registers.
-__device__ __forceinline__ void keep_here(floatx4& v) { asm volatile("" : "+v"(v)); }
-
-__device__ __forceinline__ void split_x4(const floatx4 v, u16x4& hi, u16x4& lo) {
-    split4(make_float4(v[0], v[1], v[2], v[3]), hi, lo);
-}
-
-// A 16 x 16 factor tile in LDS: the hi terms of the 64 lanes' C-layout
-// registers, then the lo terms (8 bytes per lane each, conflict-free).
-__device__ __forceinline__ void tile_store(u16x4* tiles, int t, int lane, const floatx4 v) {
+__device__ __forceinline__ Frag16 frag16(const floatx4 v) {
     u16x4 hi, lo;
-    split_x4(v, hi, lo);
-    tiles[(2 * t) * kWave + lane] = hi;
-    tiles[(2 * t + 1) * kWave + lane] = lo;
+    split4(make_float4(v[0], v[1], v[2], v[3]), hi, lo);
+    return Frag16{join(hi, lo), join(hi, hi), join(lo, lo)};
 }
 
-__device__ __forceinline__ void tile_load(const u16x4* tiles, int t, int lane, u16x4& hi, u16x4& lo) {
-    hi = tiles[(2 * t) * kWave + lane];
-    lo = tiles[(2 * t + 1) * kWave + lane];
+__device__ __forceinline__ bf16x8 pair16(const floatx4 v) {
+    u16x4 hi, lo;
+    split4(make_float4(v[0], v[1], v[2], v[3]), hi, lo);
+    return join(hi, lo);
 }
+
+// acc + P^T Q, P as a pair and Q doubled
+__device__ __forceinline__ floatx4 mm16f(floatx4 acc, const bf16x8 p_pr, const bf16x8 q_dh, const bf16x8 q_dl) {
+    acc = mfma16x16x32(p_pr, q_dh, acc);
+    return mfma16x16x32(p_pr, q_dl, acc);
+}
+
+// acc + P^T Q, P doubled and Q as a pair
+__device__ __forceinline__ floatx4 mm16d(floatx4 acc, const bf16x8 p_dh, const bf16x8 p_dl, const bf16x8 q_pr) {
+    acc = mfma16x16x32(p_dh, q_pr, acc);
+    return mfma16x16x32(p_dl, q_pr, acc);
+}
+
+// P^T Q for 16 x 16 fp32 matrices in the C layout
+__device__ __forceinline__ floatx4 mm16(const floatx4 P, const floatx4 Q) {
+    const Frag16 fp = frag16(P), fq = frag16(Q);
+    return mm16f(floatx4{0.f, 0.f, 0.f, 0.f}, fp.pr, fq.dh, fq.dl);
+}
+
+// I + s P for a C-layout matrix (s = +1 or -1), lane (c, g)
+__device__ __forceinline__ floatx4 ident_plus(const floatx4 P, float sgn, int c, int g) {
+    floatx4 r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r[i] = sgn * P[i] + ((4 * g + i == c) ? 1.f : 0.f);
+    return r;
+}
+
+// Factor tiles in LDS, one operand form per slot: 16 bytes per lane, so
+// that a wave reads or writes a slot with conflict-free 128-bit accesses
+// straight from or into its operand registers.
+__device__ __forceinline__ void slot_store(bf16x8* slots, int s, int lane, const bf16x8 v) { slots[s * kWave + lane] = v; }
+__device__ __forceinline__ bf16x8 slot_load(const bf16x8* slots, int s, int lane) { return slots[s * kWave + lane]; }
 
 template <int D, int TM>
 struct VShape {
@@ -102,10 +129,12 @@ struct VShape {
     static constexpr int KS = (D + 31) / 32;  // MFMA k-steps over d_k
     static constexpr int QKLD = D + 8;        // bf16 row stride of Q/K in LDS
     static constexpr int NBM = TM / 16;       // 16-node blocks at most
-    // factor tiles: X_ii^T (NBM), -G_ik^T (k < i), C_ji^T (i <= j)
-    static constexpr int NTILE = NBM * (NBM + 1);
-    static constexpr int TG0 = NBM;                        // first -G tile
-    static constexpr int TC0 = NBM + NBM * (NBM - 1) / 2;  // first C tile
+    // factor tiles, doubled ([hi | hi] at slot s, [lo | lo] at s + 1):
+    // X_ii^T at 2 i, -G_ik^T (k < i) at SG0 + 2 (i (i - 1) / 2 + k),
+    // C_ji^T (i <= j) at SC0 + 2 (j (j + 1) / 2 + i)
+    static constexpr int SG0 = 2 * NBM;
+    static constexpr int SC0 = SG0 + NBM * (NBM - 1);
+    static constexpr int NSLOT = SC0 + NBM * (NBM + 1);
     // waves per SIMD the registers must allow: two blocks per CU at 64 nodes
     // (eight waves each), three at 32 nodes with two row blocks per wave,
     // four otherwise
@@ -117,8 +146,8 @@ struct VLds {
     using S = VShape<D, TM>;
     static constexpr int NPLANE = F32IN ? 4 : 2;  // q, k (hi and lo planes for fp32 input)
     static constexpr size_t qk = (size_t)NPLANE * TM * S::QKLD * 2;
-    static constexpr size_t off_t = (qk + 15) / 16 * 16;                          // factor tiles
-    static constexpr size_t off_anc = off_t + (size_t)S::NTILE * 2 * kWave * 8;  // uint64 [TM]
+    static constexpr size_t off_t = (qk + 15) / 16 * 16;                        // factor-tile slots
+    static constexpr size_t off_anc = off_t + (size_t)S::NSLOT * kWave * 16;  // uint64 [TM]
     static constexpr size_t off_f = off_anc + 8 * TM;  // float logp, P, beta [TM] each
     static constexpr size_t off_i = off_f + 12 * TM;   // int: bad flag
     static constexpr size_t total = off_i + 16;
@@ -139,7 +168,7 @@ __attribute__((amdgpu_waves_per_eu(VShape<D, TM>::WPE))) void verify_kernel(cons
     __shared__ __align__(16) unsigned char smem[L::total];
     unsigned short* s_q = reinterpret_cast<unsigned short*>(smem);
     unsigned short* s_k = s_q + TM * QKLD;
-    u16x4* s_tl = reinterpret_cast<u16x4*>(smem + L::off_t);
+    bf16x8* s_sl = reinterpret_cast<bf16x8*>(smem + L::off_t);
     uint64_t* s_anc = reinterpret_cast<uint64_t*>(smem + L::off_anc);
     float* s_logp = reinterpret_cast<float*>(smem + L::off_f);
     float* s_P = s_logp + TM;
@@ -156,73 +185,91 @@ __attribute__((amdgpu_waves_per_eu(VShape<D, TM>::WPE))) void verify_kernel(cons
     const size_t nb0 = (size_t)b * p.Ts + p.t0;  // node 0 of this sequence's (chunk of the) draft
     const int NB = (T + 15) >> 4;  // 16-node blocks in use
     const int T16 = NB * 16;
-    const int vrow0 = tile * BV + wave * 16 * MBW;  // first value row (of S0, o, u) of this wave
+    // first value row (of S0, o, u) of this wave; the wave index is read
+    // into a scalar register so that every view base below is scalar
+    const int vrow0 = tile * BV + __builtin_amdgcn_readfirstlane(wave) * 16 * MBW;
+    constexpr int ES = F32IN ? 4 : 2;  // bytes per q/k/v element
+    const uint32_t HD = (uint32_t)H * D;             // elements from one node to the next
+    const uint32_t span = (uint32_t)(T - 1) * HD;    // elements from node 0 to node T-1
+    const size_t hrow0 = nb0 * H + h;                // (node 0, head h) as a row of the [.., H, D] arrays
 
-    // 1. global loads.  Every small per-node input first, so that, loads
-    // completing in issue order, steps 2-3 can run while the S0 rows are in
-    // flight.  The loads are branch-free (indices clamped into range, values
-    // of rows past T dropped later by selects): a load under a branch, or a
-    // register overwritten while its load is pending, would make the
-    // compiler wait for every earlier memory operation.
+    // 1. global loads, through views that end at node T - 1 (rows past T
+    // read as zero, see make_buf).  Every small per-node input first, so
+    // that, loads completing in issue order, steps 2-3 can run while the S0
+    // rows are in flight; the parent row and gates go before q and k (a
+    // wait for them, which the compiler also places where their registers
+    // are reused, then waits for nothing else).  No load is under a branch:
+    // a load under a branch, or a register overwritten while its load is
+    // pending, would make the compiler wait for every earlier memory
+    // operation.  Lane n of each wave reads node n's parent and gates (a
+    // chain has no parent array: its view is empty).
+    const buf_t bpar = make_buf(p.parent ? p.parent + (size_t)b * T : nullptr, p.parent ? 4u * T : 0u);
+    const uint32_t gbytes = ((uint32_t)(T - 1) * H + 1) * 4;
+    const int par_ld = (int)__builtin_amdgcn_raw_buffer_load_b32(bpar, 4u * lane, 0, 0);
+    const float ga = buf_ldf(make_buf(p.a + hrow0, gbytes), 4u * lane * H);
+    const float gb = buf_ldf(make_buf(p.beta + hrow0, gbytes), 4u * lane * H);
+    // log P at the node before a chunk (read from any valid entry otherwise)
+    const float* lbp = p.logp_out ? p.logp_out : p.a;
+    const float lbase_ld = lbp[((p.t0 > 0 ? nb0 - 1 : nb0)) * H + h];
     u32x4 qreg[QKC], kreg[QKC];
+    {
+        const uint32_t qkbytes = (span + D) * ES;
+        const buf_t bq = make_buf(static_cast<const char*>(p.q) + hrow0 * D * ES, qkbytes);
+        const buf_t bk = make_buf(static_cast<const char*>(p.k) + hrow0 * D * ES, qkbytes);
 #pragma unroll
-    for (int i = 0; i < QKC; ++i) {
-        const int ch = tid + i * NTHR, row = min(ch / CPR, T - 1), col = (ch % CPR) * EPC;
-        const size_t off = (((nb0 + row) * H + h) * D + col) * (F32IN ? 4 : 2);
-        qreg[i] = *reinterpret_cast<const u32x4*>(static_cast<const char*>(p.q) + off);
-        kreg[i] = *reinterpret_cast<const u32x4*>(static_cast<const char*>(p.k) + off);
+        for (int i = 0; i < QKC; ++i) {
+            const int ch = tid + i * NTHR, row = ch / CPR, col = (ch % CPR) * EPC;
+            const uint32_t off = ((uint32_t)row * HD + col) * ES;
+            qreg[i] = buf_ld128(bq, off);
+            kreg[i] = buf_ld128(bk, off);
+        }
     }
     // v[n][vrow0 + 16 mi + c] for the nodes n = 16 nb + 4 g + r this lane
     // holds in R (node-major C layout)
     float vf[MBW][NBM][4];
     unsigned short vb[MBW][NBM][4];
+    {
+        const buf_t bv = make_buf(static_cast<const char*>(p.v) + (hrow0 * D + vrow0) * ES, (span + 16 * MBW) * ES);
+        const uint32_t voff = ((uint32_t)(4 * g) * HD + c) * ES;
 #pragma unroll
-    for (int mi = 0; mi < MBW; ++mi) {
+        for (int mi = 0; mi < MBW; ++mi) {
 #pragma unroll
-        for (int nb = 0; nb < NBM; ++nb) {
+            for (int nb = 0; nb < NBM; ++nb) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int n = min(nb * 16 + 4 * g + r, T - 1);
-                const size_t off = ((nb0 + n) * H + h) * D + vrow0 + 16 * mi + c;
-                if constexpr (F32IN) vf[mi][nb][r] = static_cast<const float*>(p.v)[off];
-                else vb[mi][nb][r] = static_cast<const unsigned short*>(p.v)[off];
+                for (int r = 0; r < 4; ++r) {
+                    const uint32_t off = voff + ((uint32_t)(16 * nb + r) * HD + 16 * mi) * ES;
+                    if constexpr (F32IN) vf[mi][nb][r] = buf_ldf(bv, off);
+                    else vb[mi][nb][r] = buf_ld16(bv, off);
+                }
             }
         }
     }
-    const int nl = min(lane, T - 1);
-    // a chain has no parent array: read the gate array instead (it has at
-    // least B * T entries) and discard the value
-    const global_ptr<const int32_t> parp =
-        (global_ptr<const int32_t>)(p.parent ? p.parent : reinterpret_cast<const int32_t*>(p.a));
-    const int par_ld = parp[(size_t)b * T + nl];
-    const size_t gi = (nb0 + nl) * H + h;
-    const float ga = p.a[gi];
-    const float gb = p.beta[gi];
-    // log P at the node before a chunk (read from any valid entry otherwise)
-    const float* lbp = p.logp_out ? p.logp_out : p.a;
-    const float lbase_ld = lbp[((p.t0 > 0 ? nb0 - 1 : nb0)) * H + h];
     // this lane's S0 rows (A operand row c of each of the wave's 16-row
     // blocks, and the B operand column c of K S0^T)
     // (one row block is written without the row-block loop: with it the
     // compiler's allocation of the 64-node kernel spills)
     float4 sreg[MBW][KS][2];
-    if constexpr (MBW == 1) {
-        const float* s0row = p.S0 + (((size_t)b * H + h) * D + vrow0 + c) * D;
-#pragma unroll
-        for (int s = 0; s < KS; ++s) {
-            const int k0 = 32 * s + 4 * g;
-            sreg[0][s][0] = (k0 < D) ? ld_stream(s0row + k0) : make_float4(0.f, 0.f, 0.f, 0.f);
-            sreg[0][s][1] = (k0 + 16 < D) ? ld_stream(s0row + k0 + 16) : make_float4(0.f, 0.f, 0.f, 0.f);
-        }
-    } else {
-#pragma unroll
-        for (int mi = 0; mi < MBW; ++mi) {
-            const float* s0row = p.S0 + (((size_t)b * H + h) * D + vrow0 + 16 * mi + c) * D;
+    {
+        const buf_t bs = make_buf(p.S0 + (((size_t)b * H + h) * D + vrow0) * D, 16u * MBW * D * 4);
+        const uint32_t soff = (uint32_t)(c * D + 4 * g) * 4;
+        const float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f);
+        if constexpr (MBW == 1) {
 #pragma unroll
             for (int s = 0; s < KS; ++s) {
                 const int k0 = 32 * s + 4 * g;
-                sreg[mi][s][0] = (k0 < D) ? ld_stream(s0row + k0) : make_float4(0.f, 0.f, 0.f, 0.f);
-                sreg[mi][s][1] = (k0 + 16 < D) ? ld_stream(s0row + k0 + 16) : make_float4(0.f, 0.f, 0.f, 0.f);
+                sreg[0][s][0] = (k0 < D) ? buf_ldf4(bs, soff + 128u * s) : z4;
+                sreg[0][s][1] = (k0 + 16 < D) ? buf_ldf4(bs, soff + 128u * s + 64u) : z4;
+            }
+        } else {
+#pragma unroll
+            for (int mi = 0; mi < MBW; ++mi) {
+#pragma unroll
+                for (int s = 0; s < KS; ++s) {
+                    const int k0 = 32 * s + 4 * g;
+                    const uint32_t o = soff + 64u * mi * D + 128u * s;
+                    sreg[mi][s][0] = (k0 < D) ? buf_ldf4(bs, o) : z4;
+                    sreg[mi][s][1] = (k0 + 16 < D) ? buf_ldf4(bs, o + 64u) : z4;
+                }
             }
         }
     }
@@ -234,8 +281,7 @@ __attribute__((amdgpu_waves_per_eu(VShape<D, TM>::WPE))) void verify_kernel(cons
     for (int i = 0; i < QKC; ++i) {
         const int ch = tid + i * NTHR, row = ch / CPR, col = (ch % CPR) * EPC;
         if (row < T16) {
-            const u32x4 z = {0u, 0u, 0u, 0u};
-            const u32x4 qv = row < T ? qreg[i] : z, kv = row < T ? kreg[i] : z;
+            const u32x4 qv = qreg[i], kv = kreg[i];  // zero past T
             if constexpr (!F32IN) {
                 *reinterpret_cast<u32x4*>(s_q + row * QKLD + col) = qv;
                 *reinterpret_cast<u32x4*>(s_k + row * QKLD + col) = kv;
@@ -291,8 +337,12 @@ __attribute__((amdgpu_waves_per_eu(VShape<D, TM>::WPE))) void verify_kernel(cons
     __syncthreads();
     if (s_int[0]) return;  // invalid parent row: nothing is written
 
-    // 3a. diagonal blocks: X_ii^T.  K_i K_i^T in the C layout is G_ii[n][m]
-    //     before scaling (rows n = 16 i + 4 g + r, column m = 16 i + c).
+    // 3a. diagonal blocks: X_ii^T.  K_i K_i^T is symmetric, so one
+    //     accumulator gives G_ii and G_ii^T in the C layout (register r of
+    //     lane (c, g): rows 16 i + 4 g + r, column 16 i + c), and
+    //       X_ii = (I + G_ii)^{-1} = (I - G)(I + G^2)(I + G^4)(I + G^8)
+    //     (G_ii is nilpotent: G^L = 0 for L the longest ancestor chain
+    //     inside the block, so the product stops at the first power >= L).
     for (int i = wave; i < NB; i += NW) {
         floatx4 acc = {0.f, 0.f, 0.f, 0.f};
         const unsigned short* krow = s_k + (16 * i + c) * QKLD;
@@ -306,42 +356,66 @@ __attribute__((amdgpu_waves_per_eu(VShape<D, TM>::WPE))) void verify_kernel(cons
                 acc = mfma16x16x32(bkl, bk, acc);
             }
         }
-        const int m = 16 * i + c;
-        const float lpm = s_logp[m];
-        float gv[4];
+        const int nc = 16 * i + c;
+        const uint64_t anc_c = s_anc[nc];
+        const float lpc = s_logp[nc], bec = s_beta[nc];
+        floatx4 G, Gt;  // G[16 i + 4 g + r][nc] and G[nc][16 i + 4 g + r]
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int n = 16 * i + 4 * g + r;
-            const bool strict = ((s_anc[n] >> m) & 1ull) != 0ull;
-            gv[r] = strict ? s_beta[n] * expf(s_logp[n] - lpm) * acc[r] : 0.f;
+            const int nr = 16 * i + 4 * g + r;
+            const float lpr = s_logp[nr];
+            G[r] = ((s_anc[nr] >> nc) & 1ull) ? s_beta[nr] * expf(lpr - lpc) * acc[r] : 0.f;
+            Gt[r] = ((anc_c >> nr) & 1ull) ? bec * expf(lpc - lpr) * acc[r] : 0.f;
         }
-        // row c of X = (I + G_ii)^{-1} in every lane of column c: from
-        // X (I + G) = I, X[c][t] = [t == c] - sum_{s > t} X[c][s] G[s][t],
-        // with G[s][t] read from lane t + 16 (s / 4), register s % 4
-        float x[16];
-#pragma unroll
-        for (int t = 15; t >= 0; --t) {
-            float a = (t == c) ? 1.f : 0.f;
-#pragma unroll
-            for (int s = t + 1; s < 16; ++s) a -= x[s] * readlane_f(gv[s & 3], t + 16 * (s >> 2));
-            x[t] = a;
+        const int L = __builtin_amdgcn_readfirstlane(wave_max_i(__popcll((anc_c >> (16 * i)) & 0xffffull) + 1));
+        floatx4 Xt = ident_plus(Gt, -1.f, c, g);  // (I - G)^T
+        if (L > 2) {
+            const floatx4 z = {0.f, 0.f, 0.f, 0.f};
+            floatx4 G2, G2t;
+            {
+                const Frag16 fg = frag16(G), fgt = frag16(Gt);
+                G2 = mm16f(z, fgt.pr, fg.dh, fg.dl);
+                G2t = L > 4 ? mm16f(z, fg.pr, fgt.dh, fgt.dl) : z;
+            }
+            Xt = mm16(ident_plus(G2, 1.f, c, g), Xt);  // ((I - G)(I + G^2))^T
+            if (L > 4) {
+                floatx4 G4, G4t;
+                {
+                    const Frag16 fg2 = frag16(G2), fg2t = frag16(G2t);
+                    G4 = mm16f(z, fg2t.pr, fg2.dh, fg2.dl);
+                    G4t = L > 8 ? mm16f(z, fg2.pr, fg2t.dh, fg2t.dl) : z;
+                }
+                Xt = mm16(ident_plus(G4, 1.f, c, g), Xt);
+                if (L > 8) Xt = mm16(ident_plus(mm16(G4t, G4), 1.f, c, g), Xt);
+            }
         }
-        // X_ii^T in the C layout: register r of lane (c, g) is X[c][4 g + r]
-        floatx4 xt;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) xt[r] = g == 0 ? x[r] : g == 1 ? x[4 + r] : g == 2 ? x[8 + r] : x[12 + r];
-        tile_store(s_tl, i, lane, xt);
+        const Frag16 fx = frag16(Xt);
+        slot_store(s_sl, 2 * i, lane, fx.dh);
+        slot_store(s_sl, 2 * i + 1, lane, fx.dl);
     }
 
     // 3b. -G_ik^T (k < i) and C_ji^T (i <= j).  Item it covers the tile of
     //     rows n in node block bn and columns m in block bm: A = k rows of
     //     block bm, B = k or q rows of block bn, so the accumulator holds
     //     k_m . k_n (or k_m . q_n) at register r of lane (c, g) for
-    //     m = 16 bm + 4 g + r, n = 16 bn + c.  The items start at wave NB so
-    //     that the waves holding a diagonal block take fewer of them.
+    //     m = 16 bm + 4 g + r, n = 16 bn + c.  With more waves than node
+    //     blocks, a diagonal block counts as two items: the waves without
+    //     one take C consecutive items each, the others share the rest.
     {
-        const int nneg = NB * (NB - 1) / 2;
-        for (int it = (wave + NW - NB % NW) % NW; it < NB * NB; it += NW) {
+        const int nneg = NB * (NB - 1) / 2, nitem = NB * NB;
+        int it0 = wave, it1 = nitem, step = NW;
+        if (NW > NB) {
+            const int C = (2 * NB + nitem + NW - 1) / NW;
+            if (wave >= NB) {
+                it0 = (wave - NB) * C;
+                it1 = min(it0 + C, nitem);
+                step = 1;
+            } else {
+                it0 = (NW - NB) * C + wave;
+                step = NB;
+            }
+        }
+        for (int it = it0; it < it1; it += step) {
             const bool isc = it >= nneg;
             int bn, bm, t;
             if (!isc) {
@@ -349,14 +423,14 @@ __attribute__((amdgpu_waves_per_eu(VShape<D, TM>::WPE))) void verify_kernel(cons
                 while (i * (i + 1) / 2 <= it) ++i;
                 bn = i;
                 bm = it - i * (i - 1) / 2;
-                t = S::TG0 + i * (i - 1) / 2 + bm;
+                t = S::SG0 + 2 * (i * (i - 1) / 2 + bm);
             } else {
                 const int rr = it - nneg;
                 int j = 0;
                 while ((j + 1) * (j + 2) / 2 <= rr) ++j;
                 bn = j;
                 bm = rr - j * (j + 1) / 2;
-                t = S::TC0 + j * (j + 1) / 2 + bm;
+                t = S::SC0 + 2 * (j * (j + 1) / 2 + bm);
             }
             const unsigned short* arow = s_k + (16 * bm + c) * QKLD;
             const unsigned short* brow = (isc ? s_q : s_k) + (16 * bn + c) * QKLD;
@@ -380,7 +454,9 @@ __attribute__((amdgpu_waves_per_eu(VShape<D, TM>::WPE))) void verify_kernel(cons
                 const int m = 16 * bm + 4 * g + r;
                 v[r] = ((pathn >> m) & 1ull) ? sc * expf(lpn - s_logp[m]) * acc[r] : 0.f;
             }
-            tile_store(s_tl, t, lane, v);
+            const Frag16 fv = frag16(v);
+            slot_store(s_sl, t, lane, fv.dh);
+            slot_store(s_sl, t + 1, lane, fv.dl);
         }
     }
 
@@ -388,53 +464,64 @@ __attribute__((amdgpu_waves_per_eu(VShape<D, TM>::WPE))) void verify_kernel(cons
     //    value rows 4 g + r of node 16 nb + c) and K S0^T (A = k rows,
     //    B = S0 rows: node-major, nodes 16 nb + 4 g + r of value row c).
     //    Both read only Q, K and registers, so they go before the barrier.
-    floatx4 accq[MBW][NBM], acck[MBW][NBM];
+    //    Two passes keep the register peak down: K S0^T and R (the v
+    //    registers die), then S0 Q^T and B0^T from the S0 operands kept as
+    //    hi / lo terms.  With one row block per wave, all S0 registers are
+    //    split first and R is formed node block by node block; with two
+    //    (and the registers to spare) each k-step splits its own S0
+    //    registers, so the S0 loads are waited for one step at a time.  (The
+    //    other orders make the compiler spill.)
+    bf16x8 sh[MBW][KS], sl[MBW][KS];
+    floatx4 acck[MBW][NBM];
+    if constexpr (MBW > 1) {
 #pragma unroll
-    for (int mi = 0; mi < MBW; ++mi) {
+        for (int mi = 0; mi < MBW; ++mi) {
 #pragma unroll
-        for (int nb = 0; nb < NBM; ++nb) {
-            accq[mi][nb] = floatx4{0.f, 0.f, 0.f, 0.f};
-            acck[mi][nb] = floatx4{0.f, 0.f, 0.f, 0.f};
+            for (int nb = 0; nb < NBM; ++nb) acck[mi][nb] = floatx4{0.f, 0.f, 0.f, 0.f};
         }
-    }
 #pragma unroll
-    for (int s = 0; s < KS; ++s) {
-        bf16x8 sh[MBW], sl[MBW];
+        for (int s = 0; s < KS; ++s) {
 #pragma unroll
-        for (int mi = 0; mi < MBW; ++mi) split8(sreg[mi][s][0], sreg[mi][s][1], sh[mi], sl[mi]);
+            for (int mi = 0; mi < MBW; ++mi) split8(sreg[mi][s][0], sreg[mi][s][1], sh[mi][s], sl[mi][s]);
 #pragma unroll
-        for (int nb = 0; nb < NBM; ++nb) {
-            if (nb < NB) {
-                const unsigned short* qrow = s_q + (nb * 16 + c) * QKLD;
-                const unsigned short* krow = s_k + (nb * 16 + c) * QKLD;
-                const bf16x8 bq = frag_row<D>(qrow, s, g);
-                const bf16x8 bk = frag_row<D>(krow, s, g);
-#pragma unroll
-                for (int mi = 0; mi < MBW; ++mi) {
-                    accq[mi][nb] = mfma16x16x32(sh[mi], bq, accq[mi][nb]);
-                    accq[mi][nb] = mfma16x16x32(sl[mi], bq, accq[mi][nb]);
-                    acck[mi][nb] = mfma16x16x32(bk, sh[mi], acck[mi][nb]);
-                    acck[mi][nb] = mfma16x16x32(bk, sl[mi], acck[mi][nb]);
-                }
-                if constexpr (F32IN) {
-                    const bf16x8 bql = frag_row<D>(qrow + LO, s, g);
-                    const bf16x8 bkl = frag_row<D>(krow + LO, s, g);
+            for (int nb = 0; nb < NBM; ++nb) {
+                if (nb < NB) {
+                    const unsigned short* krow = s_k + (nb * 16 + c) * QKLD;
+                    const bf16x8 bk = frag_row<D>(krow, s, g);
 #pragma unroll
                     for (int mi = 0; mi < MBW; ++mi) {
-                        accq[mi][nb] = mfma16x16x32(sh[mi], bql, accq[mi][nb]);
-                        acck[mi][nb] = mfma16x16x32(bkl, sh[mi], acck[mi][nb]);
+                        acck[mi][nb] = mfma16x16x32(bk, sh[mi][s], acck[mi][nb]);
+                        acck[mi][nb] = mfma16x16x32(bk, sl[mi][s], acck[mi][nb]);
+                    }
+                    if constexpr (F32IN) {
+                        const bf16x8 bkl = frag_row<D>(krow + LO, s, g);
+#pragma unroll
+                        for (int mi = 0; mi < MBW; ++mi) acck[mi][nb] = mfma16x16x32(bkl, sh[mi][s], acck[mi][nb]);
                     }
                 }
             }
         }
+    } else {
+#pragma unroll
+        for (int s = 0; s < KS; ++s) split8(sreg[0][s][0], sreg[0][s][1], sh[0][s], sl[0][s]);
     }
-    // B0^T[v][n] = P_n (S0 q_n)[v] (the O^T accumulators start there);
     // R[n][v] = beta_n (v_n[v] - P_n (S0 k_n)[v]), zero past T (beta = 0)
-    floatx4 acco[MBW][NBM], rn[MBW][NBM];
+    floatx4 rn[MBW][NBM];
 #pragma unroll
     for (int nb = 0; nb < NBM; ++nb) {
         if (nb < NB) {
-            const float Pc = s_P[nb * 16 + c];
+            if constexpr (MBW == 1) {
+                floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+                const unsigned short* krow = s_k + (nb * 16 + c) * QKLD;
+#pragma unroll
+                for (int s = 0; s < KS; ++s) {
+                    const bf16x8 bk = frag_row<D>(krow, s, g);
+                    acc = mfma16x16x32(bk, sh[0][s], acc);
+                    acc = mfma16x16x32(bk, sl[0][s], acc);
+                    if constexpr (F32IN) acc = mfma16x16x32(frag_row<D>(krow + LO, s, g), sh[0][s], acc);
+                }
+                acck[0][nb] = acc;
+            }
             const float4 P4 = *reinterpret_cast<const float4*>(s_P + nb * 16 + 4 * g);
             const float4 B4 = *reinterpret_cast<const float4*>(s_beta + nb * 16 + 4 * g);
             const float Pr[4] = {P4.x, P4.y, P4.z, P4.w}, Br[4] = {B4.x, B4.y, B4.z, B4.w};
@@ -445,16 +532,53 @@ __attribute__((amdgpu_waves_per_eu(VShape<D, TM>::WPE))) void verify_kernel(cons
                     float vv;
                     if constexpr (F32IN) vv = vf[mi][nb][r];
                     else vv = bf16_val(vb[mi][nb][r]);
-                    acco[mi][nb][r] = Pc * accq[mi][nb][r];
                     rn[mi][nb][r] = Br[r] * (vv - Pr[r] * acck[mi][nb][r]);
                 }
             }
         }
     }
+    // B0^T[v][n] = P_n (S0 q_n)[v]; the O^T accumulators start there
+    floatx4 acco[MBW][NBM];
+#pragma unroll
+    for (int nb = 0; nb < NBM; ++nb) {
+        if (nb < NB) {
+            floatx4 acc[MBW];
+#pragma unroll
+            for (int mi = 0; mi < MBW; ++mi) acc[mi] = floatx4{0.f, 0.f, 0.f, 0.f};
+            const unsigned short* qrow = s_q + (nb * 16 + c) * QKLD;
+#pragma unroll
+            for (int s = 0; s < KS; ++s) {
+                const bf16x8 bq = frag_row<D>(qrow, s, g);
+#pragma unroll
+                for (int mi = 0; mi < MBW; ++mi) {
+                    acc[mi] = mfma16x16x32(sh[mi][s], bq, acc[mi]);
+                    acc[mi] = mfma16x16x32(sl[mi][s], bq, acc[mi]);
+                }
+                if constexpr (F32IN) {
+                    const bf16x8 bql = frag_row<D>(qrow + LO, s, g);
+#pragma unroll
+                    for (int mi = 0; mi < MBW; ++mi) acc[mi] = mfma16x16x32(sh[mi][s], bql, acc[mi]);
+                }
+            }
+            const float Pc = s_P[nb * 16 + c];
+#pragma unroll
+            for (int mi = 0; mi < MBW; ++mi) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) acco[mi][nb][r] = Pc * acc[mi][r];
+            }
+        }
+    }
     __syncthreads();  // every factor tile written
 
-    // 5. forward substitution over node blocks; O^T block by block
-    u16x4 uh[MBW][NBM], ul[MBW][NBM];
+    // 5. forward substitution over node blocks; O^T block by block.  Output
+    //    views: lane (c, g) stores node 16 i + c, values vrow0 + 16 mi + 4 g
+    //    .. +3; stores of nodes past T fall outside the views and are
+    //    dropped (no per-lane branch around the MFMAs that feed them).
+    const uint32_t obytes = (span + 16 * MBW) * 4;
+    const buf_t bo = make_buf(p.o + hrow0 * D + vrow0, obytes);
+    const buf_t bu = make_buf(p.u_out ? p.u_out + hrow0 * D + vrow0 : nullptr, p.u_out ? obytes : 0u);
+    const uint32_t ooff = ((uint32_t)c * HD + 4 * g) * 4;
+    bf16x8 upr[MBW][NBM];  // U_i as pairs
 #pragma unroll
     for (int i = 0; i < NBM; ++i) {
         if (i < NB) {
@@ -463,44 +587,41 @@ __attribute__((amdgpu_waves_per_eu(VShape<D, TM>::WPE))) void verify_kernel(cons
             for (int mi = 0; mi < MBW; ++mi) y[mi] = rn[mi][i];
 #pragma unroll
             for (int k = 0; k < i; ++k) {  // Y -= G_ik U_k
-                u16x4 th, tl;
-                tile_load(s_tl, S::TG0 + i * (i - 1) / 2 + k, lane, th, tl);
+                const int sg = S::SG0 + 2 * (i * (i - 1) / 2 + k);
+                const bf16x8 gdh = slot_load(s_sl, sg, lane), gdl = slot_load(s_sl, sg + 1, lane);
 #pragma unroll
-                for (int mi = 0; mi < MBW; ++mi) y[mi] = mm16_acc(y[mi], th, tl, uh[mi][k], ul[mi][k]);
+                for (int mi = 0; mi < MBW; ++mi) y[mi] = mm16d(y[mi], gdh, gdl, upr[mi][k]);
             }
-            u16x4 xh, xl;
-            tile_load(s_tl, i, lane, xh, xl);
-            const int n = 16 * i + c;
+            const bf16x8 xdh = slot_load(s_sl, 2 * i, lane), xdl = slot_load(s_sl, 2 * i + 1, lane);
+            const uint32_t oo = ooff + (uint32_t)(16 * i) * HD * 4;
+            const floatx4 z = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int mi = 0; mi < MBW; ++mi) {
-                u16x4 yh, yl;
-                split_x4(y[mi], yh, yl);
-                const floatx4 z = {0.f, 0.f, 0.f, 0.f};
-                split_x4(mm16_acc(z, xh, xl, yh, yl), uh[mi][i], ul[mi][i]);  // U_i = X_ii Y
+                const bf16x8 ypr = pair16(y[mi]);
+                upr[mi][i] = pair16(mm16d(z, xdh, xdl, ypr));  // U_i = X_ii Y
                 if (p.u_out) {
-                    floatx4 ut = mm16_acc(z, yh, yl, xh, xl);  // U_i^T = Y^T X_ii^T
-                    keep_here(ut);
-                    if (n < T)
-                        st_stream(p.u_out + ((nb0 + n) * H + h) * D + vrow0 + 16 * mi + 4 * g,
-                                  make_float4(ut[0], ut[1], ut[2], ut[3]));
+                    const floatx4 ut = mm16f(z, ypr, xdh, xdl);  // U_i^T = Y^T X_ii^T
+                    buf_st_stream(bu, oo + 64u * mi, make_float4(ut[0], ut[1], ut[2], ut[3]));
+                }
+            }
+            {  // O_i^T += U_i^T C_ii^T completes block i: store it at once (in
+               // the same basic block as the MFMA that feeds it)
+                const int sc = S::SC0 + 2 * (i * (i + 1) / 2 + i);
+                const bf16x8 cdh = slot_load(s_sl, sc, lane), cdl = slot_load(s_sl, sc + 1, lane);
+#pragma unroll
+                for (int mi = 0; mi < MBW; ++mi) {
+                    const floatx4 ov = mm16f(acco[mi][i], upr[mi][i], cdh, cdl);
+                    buf_st_stream(bo, oo + 64u * mi, make_float4(ov[0], ov[1], ov[2], ov[3]));
                 }
             }
 #pragma unroll
-            for (int j = i; j < NBM; ++j) {  // O_j^T += U_i^T C_ji^T
+            for (int j = i + 1; j < NBM; ++j) {  // O_j^T += U_i^T C_ji^T
                 if (j < NB) {
-                    u16x4 ch, cl;
-                    tile_load(s_tl, S::TC0 + j * (j + 1) / 2 + i, lane, ch, cl);
+                    const int sc = S::SC0 + 2 * (j * (j + 1) / 2 + i);
+                    const bf16x8 cdh = slot_load(s_sl, sc, lane), cdl = slot_load(s_sl, sc + 1, lane);
 #pragma unroll
-                    for (int mi = 0; mi < MBW; ++mi) acco[mi][j] = mm16_acc(acco[mi][j], uh[mi][i], ul[mi][i], ch, cl);
+                    for (int mi = 0; mi < MBW; ++mi) acco[mi][j] = mm16f(acco[mi][j], upr[mi][i], cdh, cdl);
                 }
-            }
-#pragma unroll
-            for (int mi = 0; mi < MBW; ++mi) keep_here(acco[mi][i]);
-            if (n < T) {
-#pragma unroll
-                for (int mi = 0; mi < MBW; ++mi)
-                    st_stream(p.o + ((nb0 + n) * H + h) * D + vrow0 + 16 * mi + 4 * g,
-                              make_float4(acco[mi][i][0], acco[mi][i][1], acco[mi][i][2], acco[mi][i][3]));
             }
         }
     }
@@ -518,22 +639,6 @@ __attribute__((amdgpu_waves_per_eu(VShape<D, TM>::WPE))) void verify_kernel(cons
 // U^T = R^T X^T, O^T = B0^T + R^T M^T.  X^T and M^T reach the other waves
 // through LDS in the same C layout (one float4 per lane), and the only LDS
 // staging is Q and K.
-
-// P^T Q for 16 x 16 fp32 matrices in the C layout
-__device__ __forceinline__ floatx4 mm16(const floatx4 P, const floatx4 Q) {
-    u16x4 ph, pl, qh, ql;
-    split_x4(P, ph, pl);
-    split_x4(Q, qh, ql);
-    return mm16_acc(floatx4{0.f, 0.f, 0.f, 0.f}, ph, pl, qh, ql);
-}
-
-// I + s P for a C-layout matrix (s = +1 or -1), lane (c, g)
-__device__ __forceinline__ floatx4 ident_plus(const floatx4 P, float sgn, int c, int g) {
-    floatx4 r;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) r[i] = sgn * P[i] + ((4 * g + i == c) ? 1.f : 0.f);
-    return r;
-}
 
 template <int D>
 struct W16Shape {
