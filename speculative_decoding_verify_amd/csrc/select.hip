@@ -11,10 +11,17 @@
 //
 // Two launches on the caller's stream:
 //   1. argmax_kernel: one workgroup per logits row (B x (T+1) rows of V
-//      values), 16-byte loads with eight in flight per thread, a per-thread
-//      running (value, index) and a wave then workgroup reduction.  The rule,
+//      values), 16-byte loads with eight in flight per thread.  The rule,
 //      identical everywhere: the larger value wins, equal values go to the
-//      lower index, NaN never wins (+0 == -0), an all-NaN row gives 0.  The
+//      lower index, NaN never wins (+0 == -0), an all-NaN row gives 0.
+//      Each thread visits its 16-byte chunks in increasing index order and
+//      keeps the chunk with the strictly largest maximum (so the earliest
+//      of equal maxima), with one max per element (fmaxf, which never
+//      returns NaN over a number) and one compare per chunk; at the end it
+//      reads its chosen chunk again for the first element equal to that
+//      maximum.  Elements outside whole chunks, the wave and workgroup
+//      reductions, and rows whose largest value is -inf (where no chunk
+//      maximum beats the starting value) use the full rule.  The
 //      comparisons are exact in fp32 (bf16 widens exactly), so the argmax
 //      does not depend on the order of the reduction.  HBM-bound: the
 //      logits are read once.
@@ -30,7 +37,7 @@
 
 namespace ldv {
 
-constexpr int kArgThreads = 512;
+constexpr int kArgThreads = 256;
 constexpr int kArgUnroll = 8;  // 16-byte loads in flight per thread
 
 // (v, i) replaces (bv, bi) when v is larger, or equal with a lower index;
@@ -48,6 +55,55 @@ __device__ __forceinline__ float elem(const unsigned char* row, int i) {
     else return bf16_val(reinterpret_cast<const unsigned short*>(row)[i]);
 }
 
+// Value k of a 16-byte chunk.
+template <bool F32>
+__device__ __forceinline__ float chunk_elem(const u32x4 r, int k) {
+    if constexpr (F32) return __uint_as_float(r[k]);
+    else return __uint_as_float((k & 1) ? (r[k >> 1] & 0xffff0000u) : (r[k >> 1] << 16));
+}
+
+// Largest value of a chunk; NaN never wins (fmaxf returns the number), a
+// chunk of NaN gives NaN.
+template <bool F32>
+__device__ __forceinline__ float chunk_max(const u32x4 r) {
+    constexpr int EPC = F32 ? 4 : 8;
+    float m = chunk_elem<F32>(r, 0);
+#pragma unroll
+    for (int k = 1; k < EPC; ++k) m = fmaxf(m, chunk_elem<F32>(r, k));
+    return m;
+}
+
+// Position of the first element of a chunk equal to v.
+template <bool F32>
+__device__ __forceinline__ int chunk_find(const u32x4 r, float v) {
+    constexpr int EPC = F32 ? 4 : 8;
+    int e = EPC - 1;
+#pragma unroll
+    for (int k = EPC - 2; k >= 0; --k) e = chunk_elem<F32>(r, k) == v ? k : e;
+    return e;
+}
+
+// Workgroup-wide argmax of (bv, bi) under the full rule; every thread gets
+// the result.
+__device__ __forceinline__ void block_take_max(float& bv, int& bi, float* s_v, int* s_i, int tid) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        const float ov = __shfl_xor(bv, off, kWave);
+        const int oi = __shfl_xor(bi, off, kWave);
+        take_max(ov, oi, bv, bi);
+    }
+    __syncthreads();  // earlier readers of s_v / s_i are done
+    if ((tid & (kWave - 1)) == 0) {
+        s_v[tid / kWave] = bv;
+        s_i[tid / kWave] = bi;
+    }
+    __syncthreads();
+    bv = s_v[0];
+    bi = s_i[0];
+#pragma unroll
+    for (int w = 1; w < kArgThreads / kWave; ++w) take_max(s_v[w], s_i[w], bv, bi);
+}
+
 template <bool F32>
 __global__ __launch_bounds__(kArgThreads) void argmax_kernel(const SelectArgs p) {
     constexpr int ES = F32 ? 4 : 2;    // bytes per element
@@ -56,7 +112,7 @@ __global__ __launch_bounds__(kArgThreads) void argmax_kernel(const SelectArgs p)
     __shared__ float s_v[kArgThreads / kWave];
     __shared__ int s_i[kArgThreads / kWave];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x;
     const int V = p.V;
     const size_t row = blockIdx.x;
     const unsigned char* base = static_cast<const unsigned char*>(p.logits) + row * (size_t)V * ES;
@@ -66,51 +122,61 @@ __global__ __launch_bounds__(kArgThreads) void argmax_kernel(const SelectArgs p)
     const int head = mis ? min(EPC - mis, V) : 0;
     const int nbody = (V - head) / EPC;
     const int tail0 = head + nbody * EPC;
-
-    float bv = -__builtin_inff();
-    int bi = INT_MAX;
-    if (tid < head) take_max(elem<F32>(base, tid), tid, bv, bi);
     const global_ptr<const u32x4> body = (global_ptr<const u32x4>)(base + (size_t)head * ES);
-    for (int c0 = 0; c0 < nbody; c0 += STEP) {
+
+    // the thread's chunks c0 + tid + u * kArgThreads, in increasing order:
+    // a strictly larger maximum is the only update needed
+    float cv = -__builtin_inff();
+    int cb = -1;
+    const int nfull = nbody / STEP;
+    for (int it = 0; it < nfull; ++it) {
+        const int c0 = it * STEP + tid;
         u32x4 r[kArgUnroll];
 #pragma unroll
-        for (int u = 0; u < kArgUnroll; ++u) r[u] = body[min(c0 + tid + u * kArgThreads, nbody - 1)];
+        for (int u = 0; u < kArgUnroll; ++u) r[u] = body[c0 + u * kArgThreads];
 #pragma unroll
         for (int u = 0; u < kArgUnroll; ++u) {
-            const int cidx = c0 + tid + u * kArgThreads;
-            if (cidx < nbody) {
-                const int i0 = head + cidx * EPC;
-                if constexpr (F32) {
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) take_max(__uint_as_float(r[u][e]), i0 + e, bv, bi);
-                } else {
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        take_max(__uint_as_float(r[u][e] << 16), i0 + 2 * e, bv, bi);
-                        take_max(__uint_as_float(r[u][e] & 0xffff0000u), i0 + 2 * e + 1, bv, bi);
-                    }
-                }
+            const float m = chunk_max<F32>(r[u]);
+            if (m > cv) {
+                cv = m;
+                cb = c0 + u * kArgThreads;
             }
         }
     }
+    if (nfull * STEP < nbody) {  // the last, partial step (loads clamped into the row)
+        const int c0 = nfull * STEP + tid;
+        u32x4 r[kArgUnroll];
+#pragma unroll
+        for (int u = 0; u < kArgUnroll; ++u) r[u] = body[min(c0 + u * kArgThreads, nbody - 1)];
+#pragma unroll
+        for (int u = 0; u < kArgUnroll; ++u) {
+            const float m = chunk_max<F32>(r[u]);
+            if (c0 + u * kArgThreads < nbody && m > cv) {
+                cv = m;
+                cb = c0 + u * kArgThreads;
+            }
+        }
+    }
+    float bv = -__builtin_inff();
+    int bi = INT_MAX;
+    if (cb >= 0) {  // the first element of the chosen chunk equal to its maximum
+        bv = cv;
+        bi = head + cb * EPC + chunk_find<F32>(body[cb], cv);
+    }
+    if (tid < head) take_max(elem<F32>(base, tid), tid, bv, bi);
     for (int i = tail0 + tid; i < V; i += kArgThreads) take_max(elem<F32>(base, i), i, bv, bi);
+    block_take_max(bv, bi, s_v, s_i, tid);
 
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-        const float ov = __shfl_xor(bv, off, kWave);
-        const int oi = __shfl_xor(bi, off, kWave);
-        take_max(ov, oi, bv, bi);
+    if (bi == INT_MAX || bv == -__builtin_inff()) {
+        // the row's largest value is -inf (or every value is NaN): no chunk
+        // maximum beat the starting value, so scan every element under the
+        // full rule (the same decision in every thread)
+        bv = -__builtin_inff();
+        bi = INT_MAX;
+        for (int i = tid; i < V; i += kArgThreads) take_max(elem<F32>(base, i), i, bv, bi);
+        block_take_max(bv, bi, s_v, s_i, tid);
     }
-    if (lane == 0) {
-        s_v[wave] = bv;
-        s_i[wave] = bi;
-    }
-    __syncthreads();
-    if (tid == 0) {
-#pragma unroll
-        for (int w = 1; w < kArgThreads / kWave; ++w) take_max(s_v[w], s_i[w], bv, bi);
-        p.target[row] = bi == INT_MAX ? 0 : bi;  // a row of NaN: 0
-    }
+    if (tid == 0) p.target[row] = bi == INT_MAX ? 0 : bi;  // a row of NaN: 0
 }
 
 __global__ __launch_bounds__(256) void walk_kernel(const SelectArgs p) {

@@ -140,3 +140,80 @@ def test_select_then_commit(ldv, orc):
     assert st == 0
     from gpu_util import check
     check("select -> commit", S, ref)
+
+
+def _special_rows(rng, R, V):
+    """fp32 rows (uint32 bit patterns) for the edge cases of the argmax rule,
+    eight kinds in turn; rows are long enough that every thread of a row
+    visits several chunks."""
+    x = rng.standard_normal((R, V)).astype(np.float32)
+    snan_rows = []
+    for r in range(R):
+        k = r % 8
+        if k == 0:  # NaN, +-inf and -0 scattered: the first +inf wins
+            m = rng.random(V)
+            x[r, m < 0.05] = np.nan
+            x[r, (m >= 0.05) & (m < 0.06)] = -np.inf
+            x[r, (m >= 0.06) & (m < 0.0603)] = np.inf
+            x[r, (m >= 0.0603) & (m < 0.08)] = -0.0
+        elif k == 1:  # NaN, then -inf everywhere: the first -inf
+            x[r] = -np.inf
+            x[r, :10] = np.nan
+        elif k == 2:  # all NaN: 0
+            x[r] = np.nan
+        elif k == 3:  # one maximum at two places far apart, NaN before the first
+            p1, p2 = sorted(int(i) for i in rng.choice(V, 2, replace=False))
+            x[r, p1] = x[r, p2] = 50.0
+            x[r, :p1:7] = np.nan
+        elif k == 4:  # the maximum at the last element
+            x[r, V - 1] = 50.0
+        elif k == 5:  # the maximum at element 0 and again in the middle
+            x[r, 0] = x[r, V // 2] = 50.0
+        elif k == 6:  # signalling-NaN patterns around a finite maximum
+            x[r, int(rng.integers(0, V))] = 50.0
+            snan_rows.append(r)
+        else:  # the maximum is zero, -0 first and +0 later
+            x[r] = -np.abs(x[r]) - 1.0
+            p1, p2 = sorted(int(i) for i in rng.choice(V, 2, replace=False))
+            x[r, p1], x[r, p2] = -0.0, 0.0
+    return x, snan_rows
+
+
+@pytest.mark.parametrize("V,dtype", [(50003, "f32"), (151936, "bf16"), (32005, "bf16")])
+def test_select_specials_long_rows(ldv, orc, V, dtype):
+    """Argmax edge cases on rows long enough for full eight-chunk steps:
+    NaN (quiet and signalling) never wins, equal values go to the lower
+    index across chunks and threads, +0 == -0, rows whose largest value is
+    -inf, all-NaN rows; odd V puts every other row off a 16-byte boundary."""
+    rng = np.random.default_rng(7100 + V)
+    B, T = 2, 7
+    x, snan_rows = _special_rows(rng, B * (T + 1), V)
+    if dtype == "f32":
+        bits = x.view(np.uint32).copy()
+        for r in snan_rows:
+            idx = rng.choice(V, 200, replace=False)
+            bits[r, idx[:100]] = 0x7F800001
+            bits[r, idx[100:]] = 0xFF800001
+        ref = bits.view(np.float32)
+        lg = torch.from_numpy(ref.reshape(B, T + 1, V).copy()).cuda()
+    else:
+        u = x.view(np.uint32)
+        nan = np.isnan(x)
+        # round to nearest even on the top 16 bits; NaN kept quiet
+        b16 = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+        b16[nan] = ((u[nan] >> 16) | 0x40).astype(np.uint16)
+        for r in snan_rows:
+            idx = rng.choice(V, 200, replace=False)
+            b16[r, idx[:100]] = 0x7F81
+            b16[r, idx[100:]] = 0xFF81
+        ref = (b16.astype(np.uint32) << 16).view(np.float32)
+        lg = torch.from_numpy(b16.view(np.int16).reshape(B, T + 1, V).copy()).cuda().view(torch.bfloat16)
+    ref = ref.reshape(B, T + 1, V)
+    tokens = rng.integers(0, V, size=(B, T)).astype(np.int32)
+    st = torch.zeros(1, dtype=torch.int32, device="cuda")
+    tg, acc, alen, bonus = (t.cpu().numpy() for t in ldv.select_accepted(lg, dev(tokens), None, status=st))
+    rt, racc, ralen, rbonus, rs = orc.select(ref, tokens, None)
+    assert int(st.item()) == rs == 0
+    assert np.array_equal(tg, rt), "targets %s vs %s" % (tg.ravel()[:16], rt.ravel()[:16])
+    assert np.array_equal(acc, racc) and np.array_equal(alen, ralen) and np.array_equal(bonus, rbonus)
+    print("select specials V%d %s targets %s" % (V, dtype, tg.ravel().tolist()), flush=True)
