@@ -22,22 +22,23 @@
 // C layout (lane (c, g), register r holds P[4 g + r][c]), the same registers
 // are the B operand of a 16-deep product as they stand and the A operand of
 // one with P transposed, so mm(P, Q) = P^T Q needs no data movement; fp32
-// operands go in as bf16 hi + lo terms (two MFMAs, lo * lo dropped).
+// operands go in as bf16 hi + lo terms (two MFMAs, see Frag16).
 //
-// Drafts of up to 16 nodes go to verify_t16_kernel (below).  Longer ones
-// use one workgroup per (sequence, head, value tile of BV columns): G and C
-// do not depend on the value channel (Eq. (7) context), so value tiles are
-// independent; at d = 128 a tile is the whole head, so the T x T factor work
-// is done once per head.  Each wave owns one 16-row value block of the tile
-// (two at 32 nodes).  Per workgroup:
-//   1. issue the loads of q, k, v, the gates and the parent row, then of the
-//      wave's S0 rows (fp32) straight into MFMA operand registers; the S0
-//      loads stay in flight through steps 2-3;
+// One kernel serves drafts of up to 16, 32 and 64 nodes (TM), with one
+// workgroup per (sequence, head, value tile of BV columns): G and C do not
+// depend on the value channel (Eq. (7) context), so value tiles are
+// independent; at d = 128 a tile is the whole head, so the T x T factor
+// work is done once per head.  Each wave owns one 16-row value block of the
+// tile (two at 32 nodes).  Per workgroup:
+//   1. issue the loads of the parent row and gates, q, k and v (through
+//      buffer views that end at node T - 1), then of the wave's S0 rows
+//      (fp32) straight into MFMA operand registers; the S0 loads stay in
+//      flight through steps 2-3;
 //   2. stage Q, K (bf16) in LDS; wave 0 turns the parent row into ancestor
 //      masks and log P by pointer doubling;
 //   3. the factor tiles, spread over the waves: each is a 16 x 16 product of
 //      K or Q rows on MFMA, masked and decay-scaled in the accumulators and
-//      kept in LDS in the C layout as hi + lo terms:
+//      kept in LDS as doubled bf16 operands:
 //        X_ii^T  (by repeated squaring of G_ii, on MFMA),
 //        -G_ik^T (k < i),  C_ji^T (i <= j);
 //   4. S0 Q^T (value-major) and K S0^T (node-major) on MFMA give B0^T and R
@@ -119,9 +120,9 @@ __device__ __forceinline__ bf16x8 slot_load(const bf16x8* slots, int s, int lane
 template <int D, int TM>
 struct VShape {
     // At d = 128 a block keeps the whole head (BV = 128), so the factor work
-    // is done once per head: eight waves of 16 value rows at 64 nodes, four
-    // waves of two 16-row blocks (MBW = 2) at 32 nodes, where each factor
-    // tile read from LDS then serves two row blocks.
+    // is done once per head: eight waves of 16 value rows at 16 and 64
+    // nodes, four waves of two 16-row blocks (MBW = 2) at 32 nodes, where
+    // each factor tile read from LDS then serves two row blocks.
     static constexpr int BV = (D >= 128) ? 128 : (D >= 64 ? 64 : D);
     static constexpr int MBW = (TM == 32 && D >= 128) ? 2 : 1;  // 16-row blocks per wave
     static constexpr int NT = D / BV;         // value tiles per head
@@ -627,257 +628,6 @@ __attribute__((amdgpu_waves_per_eu(VShape<D, TM>::WPE))) void verify_kernel(cons
     }
 }
 
-// ---------------------------------------------------------------------------
-// T <= 16: one 16 x 16 node block, so one wave does the whole factor algebra
-// of the head in registers, and every wave of the block then handles 16
-// value rows of the head, all products being mm(P, Q) = P^T Q on C-layout
-// registers (top of this file).  K K^T is symmetric, so G and G^T (and C and C^T
-// from Q K^T and K Q^T) come out of the accumulators directly, and
-//   X = (I + G)^-1 = (I - G)(I + G^2)(I + G^4)(I + G^8)      (G^16 = 0)
-// is built by repeated squaring, stopping at the stage the tree depth
-// allows.  Then M^T = X^T C^T, R and B0^T from the state products, and
-// U^T = R^T X^T, O^T = B0^T + R^T M^T.  X^T and M^T reach the other waves
-// through LDS in the same C layout (one float4 per lane), and the only LDS
-// staging is Q and K.
-
-template <int D>
-struct W16Shape {
-    static constexpr int BV = D >= 64 ? 64 : D;  // value rows per block
-    static constexpr int NT = D / BV;            // blocks per head
-    static constexpr int NW = BV / 16;           // waves per block, 16 value rows each
-    static constexpr int KS = (D + 31) / 32;     // MFMA k-steps over d_k
-    static constexpr int QKLD = D + 8;           // bf16 row stride of Q/K in LDS
-};
-
-template <int D, bool F32IN>
-__global__ __launch_bounds__((W16Shape<D>::NW * kWave)) void verify_t16_kernel(const VerifyArgs p) {
-    using S = W16Shape<D>;
-    constexpr int BV = S::BV, NW = S::NW, KS = S::KS, QKLD = S::QKLD;
-    constexpr int NTHR = NW * kWave;
-    constexpr int EPC = F32IN ? 4 : 8;                 // elements per 16-byte chunk
-    constexpr int CPR = D / EPC;                       // chunks per q/k row
-    constexpr int QKC = (16 * CPR + NTHR - 1) / NTHR;  // q (and k) chunks per thread
-    constexpr int NPLANE = F32IN ? 4 : 2;
-
-    __shared__ __align__(16) unsigned short s_qk[NPLANE * 16 * QKLD];
-    __shared__ float4 s_xt[kWave], s_mt[kWave];  // X^T and M^T in the C layout, one float4 per lane
-    unsigned short* s_q = s_qk;
-    unsigned short* s_k = s_qk + 16 * QKLD;
-    unsigned short* s_qlo = s_k + 16 * QKLD;  // fp32 input only
-    unsigned short* s_klo = s_qlo + 16 * QKLD;
-
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int c = lane & 15, g = lane >> 4;
-    const int T = p.T, H = p.H;
-    const unsigned bid = xcd_remap(blockIdx.x, gridDim.x);
-    const int tile = (int)(bid % S::NT);
-    const int bh = (int)(bid / S::NT);
-    const int h = bh % H, b = bh / H;
-    const size_t nb0 = (size_t)b * p.Ts + p.t0;  // node 0 of this sequence's (chunk of the) draft
-    const int vrow0 = tile * BV + wave * 16;
-
-    // 1. loads, small ones first, branch-free (rows clamped into range)
-    u32x4 qreg[QKC], kreg[QKC];
-#pragma unroll
-    for (int i = 0; i < QKC; ++i) {
-        const int ch = tid + i * NTHR, row = min(ch / CPR, T - 1), col = (ch % CPR) * EPC;
-        const size_t off = (((nb0 + row) * H + h) * D + col) * (F32IN ? 4 : 2);
-        qreg[i] = *reinterpret_cast<const u32x4*>(static_cast<const char*>(p.q) + off);
-        kreg[i] = *reinterpret_cast<const u32x4*>(static_cast<const char*>(p.k) + off);
-    }
-    // v[n][vrow0 + c] for the nodes n = 4 g + r this lane holds in R
-    float vv[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const size_t off = ((nb0 + min(4 * g + r, T - 1)) * H + h) * D + vrow0 + c;
-        if constexpr (F32IN) vv[r] = static_cast<const float*>(p.v)[off];
-        else vv[r] = bf16_val(static_cast<const unsigned short*>(p.v)[off]);
-    }
-    const int nq = min(c, T - 1);
-    const global_ptr<const int32_t> parp =
-        (global_ptr<const int32_t>)(p.parent ? p.parent : reinterpret_cast<const int32_t*>(p.a));
-    const int par_ld = parp[(size_t)b * T + nq];
-    const size_t gi = (nb0 + nq) * H + h;
-    const float ga = p.a[gi];
-    const float gb = p.beta[gi];
-    const float* lbp = p.logp_out ? p.logp_out : p.a;  // log P before a chunk
-    const float lbase_ld = lbp[((p.t0 > 0 ? nb0 - 1 : nb0)) * H + h];
-    const float* s0row = p.S0 + (((size_t)b * H + h) * D + vrow0 + c) * D;
-    float4 sreg[KS][2];
-#pragma unroll
-    for (int s = 0; s < KS; ++s) {
-        const int k0 = 32 * s + 4 * g;
-        sreg[s][0] = (k0 < D) ? ld_stream(s0row + k0) : make_float4(0.f, 0.f, 0.f, 0.f);
-        sreg[s][1] = (k0 + 16 < D) ? ld_stream(s0row + k0 + 16) : make_float4(0.f, 0.f, 0.f, 0.f);
-    }
-    asm volatile("" ::: "memory");  // keep the loads above ahead of any use of them
-
-    // 2a. Q, K rows into LDS (rows T .. 15 zero)
-#pragma unroll
-    for (int i = 0; i < QKC; ++i) {
-        const int ch = tid + i * NTHR, row = ch / CPR, col = (ch % CPR) * EPC;
-        if (row < 16) {
-            const u32x4 z = {0u, 0u, 0u, 0u};
-            const u32x4 qv = row < T ? qreg[i] : z, kv = row < T ? kreg[i] : z;
-            if constexpr (!F32IN) {
-                *reinterpret_cast<u32x4*>(s_q + row * QKLD + col) = qv;
-                *reinterpret_cast<u32x4*>(s_k + row * QKLD + col) = kv;
-            } else {
-                u16x4 hi, lo;
-                split4(__builtin_bit_cast(float4, qv), hi, lo);
-                *reinterpret_cast<u16x4*>(s_q + row * QKLD + col) = hi;
-                *reinterpret_cast<u16x4*>(s_qlo + row * QKLD + col) = lo;
-                split4(__builtin_bit_cast(float4, kv), hi, lo);
-                *reinterpret_cast<u16x4*>(s_k + row * QKLD + col) = hi;
-                *reinterpret_cast<u16x4*>(s_klo + row * QKLD + col) = lo;
-            }
-        }
-    }
-
-    // 2b. topology, in every wave and every 16-lane group: lane (c, g) is node c
-    const bool valid = c < T;
-    const int par = p.parent ? par_ld : c - 1;
-    const bool bad = valid && (par < -1 || par >= c);
-    if (__ballot(bad) != 0ull) {  // the same verdict in every wave of the block
-        if (tid == 0 && tile == 0 && p.status) atomicOr(p.status, LDV_STATUS_BAD_PARENT);
-        return;  // invalid parent row: nothing is written
-    }
-    unsigned set = valid ? (1u << c) : 0u;  // path segment from c up to (not including) jmp
-    int jmp = valid ? par : -1;
-    float ls = valid ? fmaxf(logf(ga), -87.f) : 0.f;
-    int dep = valid ? 1 : 0;
-#pragma unroll
-    for (int it = 0; it < 4; ++it) {
-        const int src = (jmp >= 0 ? jmp : c) + 16 * g;
-        const unsigned set_j = __shfl(set, src, kWave);
-        const float ls_j = __shfl(ls, src, kWave);
-        const int dep_j = __shfl(dep, src, kWave);
-        const int jmp_j = __shfl(jmp, src, kWave);
-        if (jmp >= 0) {
-            set |= set_j;
-            ls += ls_j;
-            dep += dep_j;
-            jmp = jmp_j;
-        }
-    }
-    const unsigned anc = set & ~(1u << c);
-    const float lp = ls, Pc = valid ? expf(ls) : 0.f, bec = valid ? gb : 0.f;
-    if (tile == 0 && wave == 0 && g == 0 && valid && p.logp_out)
-        p.logp_out[(nb0 + c) * H + h] = lp + (p.t0 > 0 ? lbase_ld : 0.f);
-    // node data for the rows n = 4 g + r of the C layout
-    unsigned anc_r[4];
-    float lp_r[4], P_r[4], be_r[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const int src = 4 * g + r;
-        anc_r[r] = __shfl(anc, src, kWave);
-        lp_r[r] = __shfl(lp, src, kWave);
-        P_r[r] = __shfl(Pc, src, kWave);
-        be_r[r] = __shfl(bec, src, kWave);
-    }
-    __syncthreads();  // Q, K staged
-
-    // 3. wave 0: G, G^T, C, C^T from K K^T, Q K^T, K Q^T (rows 4 g + r,
-    //    column c); X = (I + G)^-1 by repeated squaring; M^T = X^T C^T
-    if (wave == 0) {
-        const int maxdep = wave_max_i(dep);
-        floatx4 kk = {0.f, 0.f, 0.f, 0.f}, qk = kk, kq = kk;
-#pragma unroll
-        for (int s = 0; s < KS; ++s) {
-            const bf16x8 bq = frag_row<D>(s_q + c * QKLD, s, g), bk = frag_row<D>(s_k + c * QKLD, s, g);
-            kk = mfma16x16x32(bk, bk, kk);
-            qk = mfma16x16x32(bq, bk, qk);
-            kq = mfma16x16x32(bk, bq, kq);
-            if constexpr (F32IN) {
-                const bf16x8 bql = frag_row<D>(s_qlo + c * QKLD, s, g), bkl = frag_row<D>(s_klo + c * QKLD, s, g);
-                kk = mfma16x16x32(bk, bkl, kk);
-                kk = mfma16x16x32(bkl, bk, kk);
-                qk = mfma16x16x32(bq, bkl, qk);
-                qk = mfma16x16x32(bql, bk, qk);
-                kq = mfma16x16x32(bk, bql, kq);
-                kq = mfma16x16x32(bkl, bq, kq);
-            }
-        }
-        floatx4 G, Gt, Ct;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int n = 4 * g + r, m = c;
-            const bool both = n < T && m < T;
-            const bool m_on_n = both && ((((anc_r[r] | (1u << n)) >> m) & 1u) != 0u);
-            const bool n_on_m = both && ((((anc | (1u << m)) >> n) & 1u) != 0u);
-            const float dnm = m_on_n ? expf(lp_r[r] - lp) : 0.f;  // P_n / P_m
-            const float dmn = n_on_m ? expf(lp - lp_r[r]) : 0.f;  // P_m / P_n
-            G[r] = (m_on_n && m != n) ? be_r[r] * dnm * kk[r] : 0.f;
-            Gt[r] = (n_on_m && m != n) ? bec * dmn * kk[r] : 0.f;
-            Ct[r] = dmn * kq[r];
-        }
-        floatx4 X = ident_plus(G, -1.f, c, g), Xt = ident_plus(Gt, -1.f, c, g);  // I - G
-        if (maxdep > 2) {
-            floatx4 Gp = mm16(Gt, G), Gpt = mm16(G, Gt);  // G^2, (G^2)^T
-            for (int stage = 2; stage < maxdep; stage *= 2) {
-                const floatx4 Bm = ident_plus(Gp, 1.f, c, g);
-                const floatx4 Xn = mm16(Xt, Bm), Xnt = mm16(Bm, Xt);  // X (I + G^p) and its transpose
-                X = Xn;
-                Xt = Xnt;
-                if (2 * stage < maxdep) {
-                    const floatx4 Gq = mm16(Gpt, Gp), Gqt = mm16(Gp, Gpt);
-                    Gp = Gq;
-                    Gpt = Gqt;
-                }
-            }
-        }
-        const floatx4 Mt = mm16(X, Ct);  // M^T = X^T C^T
-        s_xt[lane] = make_float4(Xt[0], Xt[1], Xt[2], Xt[3]);
-        s_mt[lane] = make_float4(Mt[0], Mt[1], Mt[2], Mt[3]);
-    }
-    __syncthreads();
-
-    // 4. state products for this wave's 16 value rows: B0^T from S0 Q^T
-    //    (rows = values, column c = node), K S0^T for R (rows = nodes)
-    floatx4 sq = {0.f, 0.f, 0.f, 0.f}, ks = sq;
-#pragma unroll
-    for (int s = 0; s < KS; ++s) {
-        bf16x8 sh, sl;
-        split8(sreg[s][0], sreg[s][1], sh, sl);
-        const bf16x8 bq = frag_row<D>(s_q + c * QKLD, s, g), bk = frag_row<D>(s_k + c * QKLD, s, g);
-        sq = mfma16x16x32(sh, bq, sq);
-        sq = mfma16x16x32(sl, bq, sq);
-        ks = mfma16x16x32(bk, sh, ks);
-        ks = mfma16x16x32(bk, sl, ks);
-        if constexpr (F32IN) {
-            sq = mfma16x16x32(sh, frag_row<D>(s_qlo + c * QKLD, s, g), sq);
-            ks = mfma16x16x32(frag_row<D>(s_klo + c * QKLD, s, g), sh, ks);
-        }
-    }
-    floatx4 B0t, R;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        B0t[r] = Pc * sq[r];                        // B0^T[value 4g+r][node c]
-        R[r] = be_r[r] * (vv[r] - P_r[r] * ks[r]);  // R[node 4g+r][value c]; 0 past T
-    }
-
-    // 5. U^T = R^T X^T and O^T = B0^T + R^T M^T; lane (c, g) holds node c,
-    //    values vrow0 + 4 g .. +3
-    const float4 xt4 = s_xt[lane], mt4 = s_mt[lane];
-    const floatx4 Xt = {xt4.x, xt4.y, xt4.z, xt4.w}, Mt = {mt4.x, mt4.y, mt4.z, mt4.w};
-    const floatx4 Ut = mm16(R, Xt);
-    const floatx4 RMt = mm16(R, Mt);
-    if (c < T) {
-        const size_t off = ((nb0 + c) * H + h) * D + vrow0 + 4 * g;
-        st_stream(p.o + off, make_float4(B0t[0] + RMt[0], B0t[1] + RMt[1], B0t[2] + RMt[2], B0t[3] + RMt[3]));
-        if (p.u_out) st_stream(p.u_out + off, make_float4(Ut[0], Ut[1], Ut[2], Ut[3]));
-    }
-}
-
-template <int D, bool F32IN>
-static hipError_t launch_t16(const VerifyArgs& a, hipStream_t st) {
-    using S = W16Shape<D>;
-    const long long nblk = (long long)a.B * a.H * S::NT;
-    if (nblk <= 0) return hipSuccess;
-    hipLaunchKernelGGL((verify_t16_kernel<D, F32IN>), dim3((unsigned)nblk), dim3(S::NW * kWave), 0, st, a);
-    return hipGetLastError();
-}
-
 template <int D, int TM, bool F32IN>
 static hipError_t launch_t(const VerifyArgs& a, hipStream_t st) {
     using S = VShape<D, TM>;
@@ -889,7 +639,7 @@ static hipError_t launch_t(const VerifyArgs& a, hipStream_t st) {
 
 template <int D, bool F32IN>
 static hipError_t launch_d(const VerifyArgs& a, hipStream_t st) {
-    if (a.T <= 16) return launch_t16<D, F32IN>(a, st);
+    if (a.T <= 16) return launch_t<D, 16, F32IN>(a, st);
     if (a.T <= 32) return launch_t<D, 32, F32IN>(a, st);
     return launch_t<D, 64, F32IN>(a, st);
 }
