@@ -17,9 +17,9 @@
 //      Each thread visits its 16-byte chunks in increasing index order and
 //      keeps the chunk with the strictly largest maximum (so the earliest
 //      of equal maxima), with one max per element (fmaxf, which never
-//      returns NaN over a number) and one compare per chunk; at the end it
-//      reads its chosen chunk again for the first element equal to that
-//      maximum.  Elements outside whole chunks, the wave and workgroup
+//      returns NaN over a number) and one compare per chunk; it keeps that
+//      chunk's 16 bytes in registers and at the end finds in them the first
+//      element equal to the maximum.  Elements outside whole chunks, the wave and workgroup
 //      reductions, and rows whose largest value is -inf (where no chunk
 //      maximum beats the starting value) use the full rule.  The
 //      comparisons are exact in fp32 (bf16 widens exactly), so the argmax
@@ -128,6 +128,7 @@ __global__ __launch_bounds__(kArgThreads) void argmax_kernel(const SelectArgs p)
     // a strictly larger maximum is the only update needed
     float cv = -__builtin_inff();
     int cb = -1;
+    u32x4 cr = {0u, 0u, 0u, 0u};  // the chosen chunk itself (re-reading it would miss L2)
     const int nfull = nbody / STEP;
     for (int it = 0; it < nfull; ++it) {
         const int c0 = it * STEP + tid;
@@ -140,6 +141,7 @@ __global__ __launch_bounds__(kArgThreads) void argmax_kernel(const SelectArgs p)
             if (m > cv) {
                 cv = m;
                 cb = c0 + u * kArgThreads;
+                cr = r[u];
             }
         }
     }
@@ -154,6 +156,7 @@ __global__ __launch_bounds__(kArgThreads) void argmax_kernel(const SelectArgs p)
             if (c0 + u * kArgThreads < nbody && m > cv) {
                 cv = m;
                 cb = c0 + u * kArgThreads;
+                cr = r[u];
             }
         }
     }
@@ -161,7 +164,7 @@ __global__ __launch_bounds__(kArgThreads) void argmax_kernel(const SelectArgs p)
     int bi = INT_MAX;
     if (cb >= 0) {  // the first element of the chosen chunk equal to its maximum
         bv = cv;
-        bi = head + cb * EPC + chunk_find<F32>(body[cb], cv);
+        bi = head + cb * EPC + chunk_find<F32>(cr, cv);
     }
     if (tid < head) take_max(elem<F32>(base, tid), tid, bv, bi);
     for (int i = tail0 + tid; i < V; i += kArgThreads) take_max(elem<F32>(base, i), i, bv, bi);
