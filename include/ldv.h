@@ -85,7 +85,9 @@ extern "C" {
  *   u_out and logp_out are the factors ldv_commit_state needs; pass both or
  *   neither (NULL, NULL: no commit will follow).
  * A sequence whose parent row is invalid gets LDV_STATUS_BAD_PARENT and none
- * of its outputs are written.
+ * of its outputs are written.  T * H * dk * 4 must stay below 4 GiB (each
+ * (sequence, head) is accessed through views with 32-bit byte offsets);
+ * larger shapes return LDV_ERR_UNSUPPORTED.
  */
 int ldv_verify_tree(int B, int T, int H, int dk, int dv, int qkv_dtype,
                     const void* q, const void* k, const void* v,

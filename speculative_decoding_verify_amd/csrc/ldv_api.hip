@@ -30,6 +30,9 @@ int check_verify(int B, int T, int H, int dk, int dv, int dt, const void* q, con
         !aligned(status, 4))
         return LDV_ERR_ARG;
     if ((long long)B * H * 2 > 0x7fffffffLL || (long long)B * T > 0x7fffffffLL) return LDV_ERR_UNSUPPORTED;
+    // each (sequence, head) is read and written through views of T rows of
+    // H * d elements with 32-bit byte offsets
+    if ((long long)T * H * dk * 4 > 0xffffffffLL) return LDV_ERR_UNSUPPORTED;
     return 1;  // proceed
 }
 
@@ -77,6 +80,7 @@ LDV_EXPORT int ldv_verify_chain_long(int B, int T, int H, int dk, int dv, int qk
         !aligned(logp_out, 4) || !aligned(status, 4))
         return LDV_ERR_ARG;
     if ((long long)B * H * 4 > 0x7fffffffLL || (long long)B * T > 0x7fffffffLL) return LDV_ERR_UNSUPPORTED;
+    if ((long long)(T < LDV_MAX_T ? T : LDV_MAX_T) * H * dk * 4 > 0xffffffffLL) return LDV_ERR_UNSUPPORTED;
     if (S_work) {  // S_work must not overlap S0 (the first chunk reads S0 while later ones write S_work)
         const char *w0 = reinterpret_cast<const char*>(S_work), *s0 = reinterpret_cast<const char*>(S0);
         const size_t bytes = (size_t)B * H * dk * dv * 4;

@@ -57,6 +57,9 @@ def test_verify_argument_codes(lib):
     assert verify_chain(lib, T=65) == -2
     assert verify_chain(lib, dk=96, dv=96) == -2
     assert verify_chain(lib, dk=128, dv=64) == -2
+    # T * H * dk * 4 reaches 4 GiB: beyond the 32-bit offsets of a (sequence, head) view
+    assert verify_chain(lib, T=64, H=1 << 17) == -2
+    assert verify_chain(lib, T=16, H=1 << 17, B=0) == 0
     assert verify_chain(lib, B=0) == 0
     assert verify_chain(lib, T=0, q=None) == 0
     # the tree call also needs a parent array
@@ -125,7 +128,7 @@ def test_select_argument_codes(lib):
 
 def test_verify_chain_long_argument_codes(lib):
     c = lambda **kw: lib.ldv_verify_chain_long(
-        kw.get("B", 1), kw.get("T", 100), 1, kw.get("d", 128), kw.get("d", 128), kw.get("dt", 0), FAKE, FAKE, FAKE,
+        kw.get("B", 1), kw.get("T", 100), kw.get("H", 1), kw.get("d", 128), kw.get("d", 128), kw.get("dt", 0), FAKE, FAKE, FAKE,
         FAKE, FAKE, kw.get("S0", FAKE), FAKE, kw.get("u", FAKE), kw.get("lp", FAKE), kw.get("w", ctypes.c_void_p(0x900000)),
         None, None)
     assert c(u=None) == -1 and c(lp=None) == -1
@@ -134,6 +137,7 @@ def test_verify_chain_long_argument_codes(lib):
     assert c(w=MIS) == -1
     assert c(T=(1 << 20) + 1) == -2
     assert c(d=48) == -2
+    assert c(H=1 << 17) == -2                 # a 64-node chunk of 2^17 heads: 4 GiB per view
     assert c(B=0) == 0 and c(T=0) == 0
     # commit: a chain may be long, a tree may not
     k = lambda T, par: lib.ldv_commit_state(1, T, 1, 128, 128, 0, FAKE, FAKE, FAKE, par, FAKE, FAKE, FAKE, None, None)
