@@ -246,16 +246,32 @@ class Runner:
 
 
 def measure_peaks(torch):
-    """Achievable peaks on this GPU: a 2 GiB device-to-device copy (HBM read
-    plus write) and an 8192^3 bf16 GEMM (hipBLASLt through torch.matmul), each
-    the best of 5 timed runs after a warm-up."""
+    """Achievable peaks on this GPU, each the best of 5 timed runs after a
+    warm-up: a 2 GiB device-to-device copy (HBM read plus write); a loop of
+    independent v_mfma_f32_16x16x32_bf16 chains on every SIMD
+    (libldv_peaks.so, four waves per SIMD); and an 8192^3 bf16 GEMM
+    (hipBLASLt through torch.matmul)."""
+    import ctypes
     n = (2 << 30) // 4
     src = torch.ones(n, device="cuda")
     dst = torch.empty(n, device="cuda")
     a = torch.randn(8192, 8192, device="cuda", dtype=torch.bfloat16)
     b = torch.randn(8192, 8192, device="cuda", dtype=torch.bfloat16)
+    plib = ctypes.CDLL(os.path.join(ROOT, "speculative_decoding_verify_amd", "libldv_peaks.so"))
+    plib.ldv_peak_mfma.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    plib.ldv_peak_mfma_flops.argtypes = [ctypes.c_int]
+    plib.ldv_peak_mfma_flops.restype = ctypes.c_double
+    nblk = 4 * torch.cuda.get_device_properties(0).multi_processor_count
+    pout = torch.empty(nblk * 256, device="cuda")
+
+    def mfma_loop():
+        rc = plib.ldv_peak_mfma(nblk, ctypes.c_void_p(pout.data_ptr()),
+                                ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+        assert rc == 0, "MFMA probe launch failed (%d)" % rc
+
     out = {}
     for name, fn, work in (("copy_GB_s", lambda: dst.copy_(src), 2 * n * 4 / 1e9),
+                           ("bf16_mfma_loop_TFLOP_s", mfma_loop, plib.ldv_peak_mfma_flops(nblk) / 1e12),
                            ("bf16_gemm_TFLOP_s", lambda: torch.matmul(a, b), 2 * 8192 ** 3 / 1e12)):
         fn()
         torch.cuda.synchronize()
@@ -269,7 +285,7 @@ def measure_peaks(torch):
             t = e0.elapsed_time(e1) * 1e-3
             best = t if best is None else min(best, t)
         out[name] = work / best
-    del src, dst, a, b
+    del src, dst, a, b, pout
     torch.cuda.empty_cache()
     return out
 
@@ -409,6 +425,8 @@ def main():
     if peaks:
         for v in kern.values():
             v["hbm_frac_of_measured_copy"] = v["GB_s"] / peaks["copy_GB_s"]
+            if "mfma_frac" in v:
+                v["mfma_frac_of_measured_loop"] = v["mfma_frac"] * BF16_PEAK_TFLOPS / peaks["bf16_mfma_loop_TFLOP_s"]
     if "read_block" in kern:
         kern["read_block"].update({"P": run.P2, "Qn": run.Qn2})
     if "select" in kern:

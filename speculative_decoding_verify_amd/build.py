@@ -1,4 +1,5 @@
-"""Build the HIP library libldv.so in-tree for gfx950 with hipcc."""
+"""Build the HIP library libldv.so (and the measurement probe libldv_peaks.so)
+in-tree for gfx950 with hipcc."""
 from __future__ import annotations
 
 import os
@@ -11,6 +12,10 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libldv.so")
 SOURCES = ["verify.hip", "commit.hip", "gather.hip", "read.hip", "select.hip", "ldv_api.hip"]
+# the MFMA-rate probe of the measurement harness: a library of its own, so
+# that libldv.so exports exactly the calls include/ldv.h declares
+PEAKS_LIB = os.path.join(HERE, "libldv_peaks.so")
+PEAKS_SOURCES = ["peaks.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -41,13 +46,15 @@ def build(verbose: bool = False, jobs: int = 4) -> str:
         return obj
 
     with ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(compile_one, SOURCES))
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC"] + objs + ["-o", tmp]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
+        objs = list(ex.map(compile_one, SOURCES + PEAKS_SOURCES))
+    nmain = len(SOURCES)
+    for lib, lobjs in ((LIB, objs[:nmain]), (PEAKS_LIB, objs[nmain:])):
+        tmp = lib + ".tmp%d" % os.getpid()
+        cmd = [HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC"] + lobjs + ["-o", tmp]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, lib)
     return LIB
 
 
