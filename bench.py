@@ -195,6 +195,8 @@ class Runner:
             self.slot = cuda(x["slot"])
             self.queries = cuda(x["queries"], dt)
             self.go = torch.empty((wl.B, wl.P, wl.H, wl.Qn, wl.D), device="cuda")
+            if next_rows:  # drafter features: one bf16 row of H * Qn * D reads per (sequence, position)
+                self.gfeat = torch.empty((wl.B, wl.P, wl.H * wl.Qn * wl.D), device="cuda", dtype=torch.bfloat16)
         self.next = None
         if next_rows:
             r = make_block_read_inputs(wl)
@@ -228,6 +230,9 @@ class Runner:
 
     def gather(self, i):
         self.ldv.gather_states(self.pool, self.slot, self.queries, o=self.go, status=self.status)
+
+    def gather_packed(self, i):
+        self.ldv.gather_states_packed(self.pool, self.slot, self.queries, self.gfeat, col=0, status=self.status)
 
     def read(self, i):
         s = self.sets[i % len(self.sets)]
@@ -404,6 +409,10 @@ def main():
         names.append(("gather", run.gather, alg["gather"]))
     if not args.no_next:
         read_bytes, sel_bytes = algorithmic_next(wl, run.P2, run.Qn2)
+        if wl.P > 0:  # the gather's reads written into packed bf16 drafter features
+            esz = 2 if wl.qkv == "bf16" else 4
+            pk = wl.B * wl.P * wl.H * (wl.D * wl.D * 4 + wl.Qn * wl.D * esz + wl.Qn * wl.D * 2) + wl.B * wl.P * 4
+            names.append(("gather_packed_bf16", run.gather_packed, pk))
         names.append(("read_block", run.read, read_bytes))
         if wl.V > 0:
             names.append(("select", run.select, sel_bytes))
@@ -416,7 +425,7 @@ def main():
     kern["verify"]["alg_flops"] = alg["verify_flops"]
     kern["verify"]["mfma_frac"] = alg["verify_flops"] / (kern["verify"]["us"] * 1e-6) / (BF16_PEAK_TFLOPS * 1e12)
     # o = S q products of the state reads (2 d^2 flops per query)
-    for name, nq in (("gather", wl.B * wl.P * wl.H * wl.Qn),
+    for name, nq in (("gather", wl.B * wl.P * wl.H * wl.Qn), ("gather_packed_bf16", wl.B * wl.P * wl.H * wl.Qn),
                      ("read_block", wl.B * (run.P2 if not args.no_next else 0) * wl.H * (run.Qn2 if not args.no_next else 0))):
         if name in kern and nq:
             fl = 2.0 * wl.D * wl.D * nq

@@ -204,6 +204,37 @@ int ldv_read_block_states(int B, int T, int H, int dk, int dv, int P, int Qn, in
                           int* status, void* stream);
 
 /*
+ * The state reads written straight into packed drafter features.  The
+ * ReaDy page's drafter combines target hidden features with the
+ * position-specific state reads (Fig. 2a); its state reader fuses state
+ * preparation and feature packing so that no intermediate tensor is
+ * materialised (Fig. 3).  The pages do not give the feature layout, so the
+ * destination is any row-major matrix: reading p of sequence b fills row
+ * b * P + p (row stride feat_ld elements) at
+ *     feat[(b * P + p) * feat_ld + feat_col + (h * Qn + i) * dv + v]
+ *         = o[b, p, h, i, v]
+ * for every head h, query i < Qn and value v (the o of ldv_gather_states /
+ * ldv_read_block_states); every other element of feat is left as it is (the
+ * caller's hidden features, for instance).  feat_dtype is LDV_F32, or
+ * LDV_BF16 for values rounded to nearest even from the same fp32 results.
+ * Requirements (LDV_ERR_ARG otherwise): queries given and Qn > 0;
+ * feat_col + H * Qn * dv <= feat_ld; feat_ld and feat_col multiples of 4;
+ * feat aligned to 16 bytes (fp32) or 8 bytes (bf16).  The other arguments,
+ * checks and status bits are those of the unpacked call; the gather form
+ * writes no state copies.
+ */
+int ldv_gather_states_packed(int B, int P, int H, int dk, int dv, int num_slots, int Qn, int q_dtype,
+                             const float* pool, const int32_t* slot, const void* queries,
+                             void* feat, long long feat_ld, long long feat_col, int feat_dtype,
+                             int* status, void* stream);
+int ldv_read_block_states_packed(int B, int T, int H, int dk, int dv, int P, int Qn, int qk_dtype,
+                                 const void* k, const float* u, const float* logp,
+                                 const int32_t* parent, const float* S0, const int32_t* pos,
+                                 const void* queries,
+                                 void* feat, long long feat_ld, long long feat_col, int feat_dtype,
+                                 int* status, void* stream);
+
+/*
  * Greedy selection of the accepted node, on the device.  Verification fixes
  * the accepted prefix (ReaDy page, Fig. 2a) and only the node selected after
  * sampling keeps its state (Bole page, summary and section IV); with greedy

@@ -48,8 +48,9 @@ __global__ __launch_bounds__((GShape<D>::NWA * kWave)) void gather_kernel(const 
         return;
     }
     const float* src = p.pool + ((size_t)s * H + h) * D * D;
-    const bool reads = p.queries && p.o && p.Qn > 0;
-    const size_t qo_base = ((size_t)bp * H + h) * (size_t)p.Qn;
+    const bool reads = p.queries && p.o.base && p.Qn > 0;
+    const size_t qo_base = ((size_t)bp * H + h) * (size_t)p.Qn;           // queries row of query 0
+    const size_t o_base = bp * p.o.ld + p.o.col + (size_t)h * p.Qn * D;  // o element of query 0
 
     // queries of the first 16-column block (the common case is Qn <= 16)
     // before the state, so that waiting for them leaves the state in flight.
@@ -152,7 +153,8 @@ __global__ __launch_bounds__((GShape<D>::NWA * kWave)) void gather_kernel(const 
 #pragma unroll
             for (int mi = 0; mi < MBW; ++mi) {
                 const int row0 = ((part * NWA + wave) * MBW + mi) * 16 + 4 * g;
-                st_stream(p.o + (qo_base + col) * D + row0, make_float4(acc[mi][0], acc[mi][1], acc[mi][2], acc[mi][3]));
+                st_stream_out4(p.o.base, p.o.bf16, o_base + (size_t)col * D + row0,
+                               make_float4(acc[mi][0], acc[mi][1], acc[mi][2], acc[mi][3]));
             }
         }
     }

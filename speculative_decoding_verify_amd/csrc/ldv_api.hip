@@ -123,18 +123,29 @@ LDV_EXPORT int ldv_commit_state(int B, int T, int H, int dk, int dv, int k_dtype
     return e == hipSuccess ? LDV_OK : LDV_ERR_LAUNCH;
 }
 
-LDV_EXPORT int ldv_gather_states(int B, int P, int H, int dk, int dv, int num_slots, int Qn, int q_dtype,
-                                 const float* pool, const int32_t* slot, const void* queries, float* o,
-                                 float* states_out, int* status, void* stream) {
+namespace {
+
+// Checks of a packed destination: fp32 or bf16, rows of ld elements holding
+// H * Qn * dv values from column col, vector-aligned.
+int check_packed(int H, int Qn, int dv, const void* feat, long long ld, long long col, int dt) {
+    if (!feat || (dt != LDV_BF16 && dt != LDV_F32)) return LDV_ERR_ARG;
+    if (ld < 0 || col < 0 || col + (long long)H * Qn * dv > ld) return LDV_ERR_ARG;
+    if (ld % 4 != 0 || col % 4 != 0 || !aligned(feat, dt == LDV_F32 ? 16 : 8)) return LDV_ERR_ARG;
+    return 1;
+}
+
+int gather_common(int B, int P, int H, int dk, int dv, int num_slots, int Qn, int q_dtype, const float* pool,
+                  const int32_t* slot, const void* queries, ldv::ReadOut o, float* states_out, int* status,
+                  void* stream) {
     if (B < 0 || P < 0 || H < 0 || dk <= 0 || dv <= 0 || num_slots < 0) return LDV_ERR_ARG;
     if (q_dtype != LDV_BF16 && q_dtype != LDV_F32) return LDV_ERR_ARG;
-    if ((queries == nullptr) != (o == nullptr)) return LDV_ERR_ARG;
+    if ((queries == nullptr) != (o.base == nullptr)) return LDV_ERR_ARG;
     if (queries && Qn < 0) return LDV_ERR_ARG;
     if (dk != dv || !supported_d(dk)) return LDV_ERR_UNSUPPORTED;
     if (B == 0 || P == 0 || H == 0) return LDV_OK;
     if (!pool || !slot) return LDV_ERR_ARG;
-    if (!aligned(pool, 16) || !aligned(queries, 16) || !aligned(o, 16) || !aligned(states_out, 16) ||
-        !aligned(slot, 4) || !aligned(status, 4))
+    if (!aligned(pool, 16) || !aligned(queries, 16) || !aligned(o.base, o.bf16 ? 8 : 16) ||
+        !aligned(states_out, 16) || !aligned(slot, 4) || !aligned(status, 4))
         return LDV_ERR_ARG;
     if ((long long)B * P * H > 0x7fffffffLL) return LDV_ERR_UNSUPPORTED;
     ldv::GatherArgs args{B, P, H, dk, num_slots, queries ? Qn : 0, pool, slot, queries, o, states_out, status};
@@ -142,17 +153,17 @@ LDV_EXPORT int ldv_gather_states(int B, int P, int H, int dk, int dv, int num_sl
     return e == hipSuccess ? LDV_OK : LDV_ERR_LAUNCH;
 }
 
-LDV_EXPORT int ldv_read_block_states(int B, int T, int H, int dk, int dv, int P, int Qn, int qk_dtype,
-                                     const void* k, const float* u, const float* logp, const int32_t* parent,
-                                     const float* S0, const int32_t* pos, const void* queries, float* o,
-                                     int* status, void* stream) {
+int read_common(int B, int T, int H, int dk, int dv, int P, int Qn, int qk_dtype, const void* k, const float* u,
+                const float* logp, const int32_t* parent, const float* S0, const int32_t* pos, const void* queries,
+                ldv::ReadOut o, int* status, void* stream) {
     if (B < 0 || T < 0 || H < 0 || P < 0 || Qn < 0 || dk <= 0 || dv <= 0) return LDV_ERR_ARG;
     if (qk_dtype != LDV_BF16 && qk_dtype != LDV_F32) return LDV_ERR_ARG;
     if (dk != dv || !supported_d(dk) || T > LDV_MAX_T) return LDV_ERR_UNSUPPORTED;
     if (B == 0 || T == 0 || H == 0 || P == 0 || Qn == 0) return LDV_OK;
-    if (!k || !u || !logp || !S0 || !pos || !queries || !o) return LDV_ERR_ARG;
-    if (!aligned(k, 16) || !aligned(u, 16) || !aligned(S0, 16) || !aligned(queries, 16) || !aligned(o, 16) ||
-        !aligned(logp, 4) || !aligned(parent, 4) || !aligned(pos, 4) || !aligned(status, 4))
+    if (!k || !u || !logp || !S0 || !pos || !queries || !o.base) return LDV_ERR_ARG;
+    if (!aligned(k, 16) || !aligned(u, 16) || !aligned(S0, 16) || !aligned(queries, 16) ||
+        !aligned(o.base, o.bf16 ? 8 : 16) || !aligned(logp, 4) || !aligned(parent, 4) || !aligned(pos, 4) ||
+        !aligned(status, 4))
         return LDV_ERR_ARG;
     if ((long long)P * Qn > 0x7fffffffLL ||
         (long long)B * H * 2 * (((long long)P * Qn + 63) / 64) > 0x7fffffffLL)
@@ -160,6 +171,47 @@ LDV_EXPORT int ldv_read_block_states(int B, int T, int H, int dk, int dv, int P,
     ldv::ReadArgs args{B, T, H, dk, P, Qn, k, u, logp, parent, S0, pos, queries, o, status};
     hipError_t e = ldv::launch_read(args, qk_dtype == LDV_F32, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? LDV_OK : LDV_ERR_LAUNCH;
+}
+
+}  // namespace
+
+LDV_EXPORT int ldv_gather_states(int B, int P, int H, int dk, int dv, int num_slots, int Qn, int q_dtype,
+                                 const float* pool, const int32_t* slot, const void* queries, float* o,
+                                 float* states_out, int* status, void* stream) {
+    const ldv::ReadOut out{o, (size_t)(H > 0 ? H : 0) * (Qn > 0 ? Qn : 0) * (dv > 0 ? dv : 0), 0, 0};
+    return gather_common(B, P, H, dk, dv, num_slots, Qn, q_dtype, pool, slot, queries, out, states_out, status,
+                         stream);
+}
+
+LDV_EXPORT int ldv_gather_states_packed(int B, int P, int H, int dk, int dv, int num_slots, int Qn, int q_dtype,
+                                        const float* pool, const int32_t* slot, const void* queries, void* feat,
+                                        long long feat_ld, long long feat_col, int feat_dtype, int* status,
+                                        void* stream) {
+    if (!queries || Qn <= 0) return LDV_ERR_ARG;
+    const int c = check_packed(H, Qn, dv, feat, feat_ld, feat_col, feat_dtype);
+    if (c != 1) return c;
+    const ldv::ReadOut out{feat, (size_t)feat_ld, (size_t)feat_col, feat_dtype == LDV_BF16};
+    return gather_common(B, P, H, dk, dv, num_slots, Qn, q_dtype, pool, slot, queries, out, nullptr, status, stream);
+}
+
+LDV_EXPORT int ldv_read_block_states(int B, int T, int H, int dk, int dv, int P, int Qn, int qk_dtype,
+                                     const void* k, const float* u, const float* logp, const int32_t* parent,
+                                     const float* S0, const int32_t* pos, const void* queries, float* o,
+                                     int* status, void* stream) {
+    const ldv::ReadOut out{o, (size_t)(H > 0 ? H : 0) * (Qn > 0 ? Qn : 0) * (dv > 0 ? dv : 0), 0, 0};
+    return read_common(B, T, H, dk, dv, P, Qn, qk_dtype, k, u, logp, parent, S0, pos, queries, out, status, stream);
+}
+
+LDV_EXPORT int ldv_read_block_states_packed(int B, int T, int H, int dk, int dv, int P, int Qn, int qk_dtype,
+                                            const void* k, const float* u, const float* logp, const int32_t* parent,
+                                            const float* S0, const int32_t* pos, const void* queries, void* feat,
+                                            long long feat_ld, long long feat_col, int feat_dtype, int* status,
+                                            void* stream) {
+    if (Qn <= 0) return LDV_ERR_ARG;
+    const int c = check_packed(H, Qn, dv, feat, feat_ld, feat_col, feat_dtype);
+    if (c != 1) return c;
+    const ldv::ReadOut out{feat, (size_t)feat_ld, (size_t)feat_col, feat_dtype == LDV_BF16};
+    return read_common(B, T, H, dk, dv, P, Qn, qk_dtype, k, u, logp, parent, S0, pos, queries, out, status, stream);
 }
 
 LDV_EXPORT int ldv_select_accepted(int B, int T, int V, int logits_dtype, const void* logits,

@@ -178,6 +178,18 @@ __device__ __forceinline__ void buf_st_stream(buf_t b, uint32_t off, const float
     __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, w), b, off, 0, kBufNT);
 }
 
+// Four consecutive output values at element `off` of `base`: fp32 (16 bytes)
+// or bf16 rounded to nearest even (8 bytes), non-temporal either way.
+__device__ __forceinline__ void st_stream_out4(void* base, int bf16, size_t off, const float4 v) {
+    if (bf16) {
+        const u16x4 w = {bf16_bits(v.x), bf16_bits(v.y), bf16_bits(v.z), bf16_bits(v.w)};
+        __builtin_nontemporal_store(w, reinterpret_cast<global_ptr<u16x4>>(
+                                           (global_ptr<unsigned short>)(static_cast<unsigned short*>(base) + off)));
+    } else {
+        st_stream(static_cast<float*>(base) + off, v);
+    }
+}
+
 // Four bf16 values (8 bytes) from LDS or global memory.
 __device__ __forceinline__ u16x4 load_u16x4(const unsigned short* p) {
     return *reinterpret_cast<const u16x4*>(p);

@@ -42,12 +42,22 @@ struct CommitArgs {
     int* status;
 };
 
+// Destination of the o values of state reads: for reading p of sequence b,
+// row b * P + p of a matrix with a row stride of `ld` elements, elements
+// col + (h * Qn + i) * D + v for head h, query i, value v; fp32, or bf16
+// rounded to nearest even.  The o tensor [B, P, H, Qn, D] is the case
+// ld = H * Qn * D, col = 0, fp32; a drafter feature buffer is any other.
+struct ReadOut {
+    void* base;  // NULL: no reads
+    size_t ld, col;
+    int bf16;
+};
 struct GatherArgs {
     int B, P, H, D, num_slots, Qn;
     const float* pool;
     const int32_t* slot;
     const void* queries;  // may be NULL
-    float* o;             // may be NULL
+    ReadOut o;            // base may be NULL
     float* states_out;    // may be NULL
     int* status;
 };
@@ -61,7 +71,7 @@ struct ReadArgs {
     const float* S0;
     const int32_t* pos;
     const void* queries;
-    float* o;
+    ReadOut o;
     int* status;  // may be NULL
 };
 

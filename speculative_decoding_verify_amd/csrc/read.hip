@@ -314,8 +314,8 @@ __global__ __launch_bounds__((RShape<D, TM>::NW * kWave)) void read_kernel(const
         const int f = f0 + cb * 16 + c, j = jcol[cb];
         if (f < NQT && j >= -1 && j < T) {
             const int pp = f / Qn, ii = f - pp * Qn;
-            const size_t off = ((((size_t)b * P + pp) * H + h) * Qn + ii) * D + vrow0 + 4 * g;
-            st_stream(p.o + off, make_float4(acc[cb][0], acc[cb][1], acc[cb][2], acc[cb][3]));
+            const size_t off = ((size_t)b * P + pp) * p.o.ld + p.o.col + ((size_t)h * Qn + ii) * D + vrow0 + 4 * g;
+            st_stream_out4(p.o.base, p.o.bf16, off, make_float4(acc[cb][0], acc[cb][1], acc[cb][2], acc[cb][3]));
         }
     }
     // positions outside [-1, T-1]: reported by the blocks of head 0, tile 0

@@ -49,6 +49,10 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.ldv_commit_state.argtypes = [i, i, i, i, i, i, vp, fp, fp, ip, ip, fp, fp, ip, vp]
     lib.ldv_gather_states.argtypes = [i, i, i, i, i, i, i, i, fp, ip, vp, fp, fp, ip, vp]
     lib.ldv_read_block_states.argtypes = [i, i, i, i, i, i, i, i, vp, fp, fp, ip, fp, ip, vp, fp, ip, vp]
+    ll = ctypes.c_longlong
+    lib.ldv_gather_states_packed.argtypes = [i, i, i, i, i, i, i, i, fp, ip, vp, vp, ll, ll, i, ip, vp]
+    lib.ldv_read_block_states_packed.argtypes = [i, i, i, i, i, i, i, i, vp, fp, fp, ip, fp, ip, vp, vp, ll, ll, i,
+                                                 ip, vp]
     lib.ldv_select_accepted.argtypes = [i, i, i, i, vp, ip, ip, ip, ip, ip, ip, ip, vp]
     for f in ("ldv_verify_tree", "ldv_verify_chain", "ldv_verify_chain_long", "ldv_commit_state", "ldv_gather_states",
               "ldv_read_block_states", "ldv_select_accepted", "ldv_version"):
@@ -289,6 +293,80 @@ def read_block_states(k, u, logp, S0, pos, queries, parent=None, o=None, status=
         B, T, H, dk, dv, P, Qn, code, _ptr(k), _ptr(u), _ptr(logp), _ptr(parent), _ptr(S0), _ptr(pos),
         _ptr(queries), _ptr(o), _ptr(status), _stream(stream)))
     return o
+
+
+def _feat(feat, B, P, width, col):
+    """A packed destination: a contiguous [B, P, W] or [B * P, W] tensor,
+    fp32 or bf16, with columns col .. col + width - 1 to be written.
+    Returns (dtype code, W)."""
+    _dev(feat, "feat")
+    if feat.dtype == torch.float32:
+        code = LDV_F32
+    elif feat.dtype == torch.bfloat16:
+        code = LDV_BF16
+    else:
+        raise TypeError("feat must be float32 or bfloat16 (got %s)" % feat.dtype)
+    if tuple(feat.shape[:-1]) not in ((B, P), (B * P,)):
+        raise ValueError("feat must have shape [B, P, W] or [B * P, W] (got %s)" % (tuple(feat.shape),))
+    W = feat.shape[-1]
+    if col < 0 or col + width > W:
+        raise ValueError("columns %d .. %d do not fit rows of %d" % (col, col + width - 1, W))
+    return code, W
+
+
+def gather_states_packed(pool, slot, queries, feat, col=0, status=None, stream=None):
+    """The reads of gather_states written straight into packed drafter
+    features: row b * P + p of ``feat`` gets o[b, p] (heads, queries, values
+    in that order) at columns col .. col + H * Qn * dv - 1, as fp32 or as bf16
+    (feat's dtype); every other element of feat is left as it is.  No state
+    copies.  Returns feat."""
+    _dev(pool, "pool", torch.float32)
+    num_slots, H, dv, dk = pool.shape
+    _dev(slot, "slot", torch.int32)
+    B, P = slot.shape
+    _dev(queries, "queries")
+    code = _qkv_code(queries)
+    if queries.dim() != 5 or tuple(queries.shape[:3]) != (B, P, H) or queries.shape[4] != dk:
+        raise ValueError("queries must have shape [B, P, H, Qn, dk]")
+    Qn = queries.shape[3]
+    fcode, W = _feat(feat, B, P, H * Qn * dv, col)
+    if status is not None:
+        _dev(status, "status", torch.int32)
+    _check("ldv_gather_states_packed", load().ldv_gather_states_packed(
+        B, P, H, dk, dv, num_slots, Qn, code, _ptr(pool), _ptr(slot), _ptr(queries), _ptr(feat), W, col, fcode,
+        _ptr(status), _stream(stream)))
+    return feat
+
+
+def read_block_states_packed(k, u, logp, S0, pos, queries, feat, col=0, parent=None, status=None, stream=None):
+    """The reads of read_block_states written straight into packed drafter
+    features, laid out as in gather_states_packed.  Returns feat."""
+    _dev(k, "k")
+    B, T, H, dk = k.shape
+    code = _qkv_code(k)
+    _dev(u, "u", torch.float32)
+    if u.dim() != 4 or tuple(u.shape[:3]) != (B, T, H):
+        raise ValueError("u must have shape [B, T, H, dv]")
+    dv = u.shape[3]
+    _dev(logp, "logp", torch.float32, (B, T, H))
+    _dev(S0, "S0", torch.float32, (B, H, dv, dk))
+    _dev(pos, "pos", torch.int32)
+    if pos.dim() != 2 or pos.shape[0] != B:
+        raise ValueError("pos must have shape [B, P]")
+    P = pos.shape[1]
+    _dev(queries, "queries", k.dtype)
+    if queries.dim() != 5 or tuple(queries.shape[:3]) != (B, P, H) or queries.shape[4] != dk:
+        raise ValueError("queries must have shape [B, P, H, Qn, dk]")
+    Qn = queries.shape[3]
+    if parent is not None:
+        _dev(parent, "parent", torch.int32, (B, T))
+    fcode, W = _feat(feat, B, P, H * Qn * dv, col)
+    if status is not None:
+        _dev(status, "status", torch.int32)
+    _check("ldv_read_block_states_packed", load().ldv_read_block_states_packed(
+        B, T, H, dk, dv, P, Qn, code, _ptr(k), _ptr(u), _ptr(logp), _ptr(parent), _ptr(S0), _ptr(pos),
+        _ptr(queries), _ptr(feat), W, col, fcode, _ptr(status), _stream(stream)))
+    return feat
 
 
 def select_accepted(logits, tokens, parent=None, target=None, accepted=None, accepted_len=None,

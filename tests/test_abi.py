@@ -142,3 +142,31 @@ def test_verify_chain_long_argument_codes(lib):
     # commit: a chain may be long, a tree may not
     k = lambda T, par: lib.ldv_commit_state(1, T, 1, 128, 128, 0, FAKE, FAKE, FAKE, par, FAKE, FAKE, FAKE, None, None)
     assert k(65, FAKE) == -2
+
+
+def test_packed_argument_codes(lib):
+    """Packed state reads: destination checks happen on the host."""
+    LD = 3 * 16 * 128  # H * Qn * dv of the calls below
+
+    def g(**kw):
+        return lib.ldv_gather_states_packed(
+            kw.get("B", 1), 1, 3, kw.get("d", 128), kw.get("d", 128), 4, kw.get("Qn", 16), 0, FAKE, FAKE,
+            kw.get("q", FAKE), kw.get("feat", FAKE), kw.get("ld", LD + 8), kw.get("col", 8), kw.get("fdt", 0), None,
+            None)
+
+    def r(**kw):
+        return lib.ldv_read_block_states_packed(
+            kw.get("B", 1), 8, 3, 128, 128, 1, kw.get("Qn", 16), 0, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE,
+            kw.get("feat", FAKE), kw.get("ld", LD), kw.get("col", 0), kw.get("fdt", 1), None, None)
+
+    for call in (g, r):
+        assert call(feat=None) == -1
+        assert call(fdt=5) == -1
+        assert call(ld=LD - 4, col=0) == -1        # the reads do not fit a row
+        assert call(ld=LD + 6, col=2) == -1        # column not a multiple of 4
+        assert call(ld=LD + 2, col=0) == -1        # row stride not a multiple of 4
+        assert call(Qn=0) == -1
+        assert call(feat=MIS) == -1                # 4-byte aligned: neither fp32 (16) nor bf16 (8)
+        assert call(B=0) == 0
+    assert g(q=None) == -1
+    assert g(d=96) == -2
