@@ -40,6 +40,10 @@ def test_graph_replays_match_eager(ldv):
     acc = torch.empty((B,), dtype=torch.int32, device="cuda")
     alen, bonus = torch.empty_like(acc), torch.empty_like(acc)
     Sc = torch.empty_like(S0)
+    # packed drafter features: the gather's reads after 4 columns of other
+    # features, the in-block reads in bf16
+    gf = torch.zeros((B, wl.P, 4 + H * wl.Qn * D), device="cuda")  # columns 0..3 are never written
+    rf = torch.empty((B, r["pos"].shape[1], H * 8 * D), device="cuda", dtype=torch.bfloat16)
     st = torch.zeros(1, dtype=torch.int32, device="cuda")
 
     def path():
@@ -48,8 +52,10 @@ def test_graph_replays_match_eager(ldv):
         ldv.select_accepted(logits, tokens, par, target=tg, accepted=acc, accepted_len=alen, bonus=bonus, status=st)
         ldv.commit_state(k, u, lp, acc, S0, S_out=Sc, parent=par, status=st)
         ldv.gather_states(pool, slot, gq, o=go, status=st)
+        ldv.gather_states_packed(pool, slot, gq, gf, col=4, status=st)
+        ldv.read_block_states_packed(k, u, lp, S0, pos, rq, rf, parent=par, status=st)
 
-    outs = (o, u, lp, ro, tg, acc, alen, bonus, Sc, go)
+    outs = (o, u, lp, ro, tg, acc, alen, bonus, Sc, go, gf, rf)
     path()
     torch.cuda.synchronize()
     want = [t.clone() for t in outs]
