@@ -152,11 +152,15 @@ struct VLds {
     static constexpr size_t off_f = off_anc + 8 * TM;  // float logp, P, beta [TM] each
     static constexpr size_t off_i = off_f + 12 * TM;   // int: bad flag
     static constexpr size_t total = off_i + 16;
+    // waves per SIMD that the registers must allow: the shape's target, or
+    // fewer where this block's LDS (160 KiB per CU) already caps residency
+    static constexpr int lds_waves = (int)(163840 / total) * S::NW / 4;
+    static constexpr int WPE = lds_waves < 1 ? 1 : (lds_waves < S::WPE ? lds_waves : S::WPE);
 };
 
 template <int D, int TM, bool F32IN>
 __global__ __launch_bounds__((VShape<D, TM>::NW * kWave))
-__attribute__((amdgpu_waves_per_eu(VShape<D, TM>::WPE))) void verify_kernel(const VerifyArgs p) {
+__attribute__((amdgpu_waves_per_eu(VLds<D, TM, F32IN>::WPE))) void verify_kernel(const VerifyArgs p) {
     using S = VShape<D, TM>;
     using L = VLds<D, TM, F32IN>;
     constexpr int BV = S::BV, NW = S::NW, KS = S::KS, QKLD = S::QKLD, NBM = S::NBM, MBW = S::MBW;
