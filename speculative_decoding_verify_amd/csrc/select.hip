@@ -11,7 +11,8 @@
 //
 // Two launches on the caller's stream:
 //   1. argmax_kernel: one workgroup per logits row (B x (T+1) rows of V
-//      values), 16-byte loads with eight in flight per thread.  The rule,
+//      values; 256 threads, or 512 when there are few rows), 16-byte loads
+//      with eight in flight per thread.  The rule,
 //      identical everywhere: the larger value wins, equal values go to the
 //      lower index, NaN never wins (+0 == -0), an all-NaN row gives 0.
 //      Each thread visits its 16-byte chunks in increasing index order and
@@ -37,7 +38,13 @@
 
 namespace ldv {
 
-constexpr int kArgThreads = 256;
+// Threads per logits row: 256 when there are enough rows to fill the GPU
+// (kArgFillRows or more), else 512 so that a few rows still keep more loads
+// in flight (1024 measured slower: fewer chunks per thread, a longer
+// reduction).
+constexpr int kArgThreadsWide = 512;
+constexpr int kArgThreadsNarrow = 256;
+constexpr int kArgFillRows = 1024;
 constexpr int kArgUnroll = 8;  // 16-byte loads in flight per thread
 
 // (v, i) replaces (bv, bi) when v is larger, or equal with a lower index;
@@ -85,6 +92,7 @@ __device__ __forceinline__ int chunk_find(const u32x4 r, float v) {
 
 // Workgroup-wide argmax of (bv, bi) under the full rule; every thread gets
 // the result.
+template <int NTHR>
 __device__ __forceinline__ void block_take_max(float& bv, int& bi, float* s_v, int* s_i, int tid) {
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) {
@@ -101,16 +109,16 @@ __device__ __forceinline__ void block_take_max(float& bv, int& bi, float* s_v, i
     bv = s_v[0];
     bi = s_i[0];
 #pragma unroll
-    for (int w = 1; w < kArgThreads / kWave; ++w) take_max(s_v[w], s_i[w], bv, bi);
+    for (int w = 1; w < NTHR / kWave; ++w) take_max(s_v[w], s_i[w], bv, bi);
 }
 
-template <bool F32>
-__global__ __launch_bounds__(kArgThreads) void argmax_kernel(const SelectArgs p) {
+template <bool F32, int NTHR>
+__global__ __launch_bounds__(NTHR) void argmax_kernel(const SelectArgs p) {
     constexpr int ES = F32 ? 4 : 2;    // bytes per element
     constexpr int EPC = 16 / ES;       // elements per 16-byte chunk
-    constexpr int STEP = kArgThreads * kArgUnroll;
-    __shared__ float s_v[kArgThreads / kWave];
-    __shared__ int s_i[kArgThreads / kWave];
+    constexpr int STEP = NTHR * kArgUnroll;
+    __shared__ float s_v[NTHR / kWave];
+    __shared__ int s_i[NTHR / kWave];
 
     const int tid = threadIdx.x;
     const int V = p.V;
@@ -124,7 +132,7 @@ __global__ __launch_bounds__(kArgThreads) void argmax_kernel(const SelectArgs p)
     const int tail0 = head + nbody * EPC;
     const global_ptr<const u32x4> body = (global_ptr<const u32x4>)(base + (size_t)head * ES);
 
-    // the thread's chunks c0 + tid + u * kArgThreads, in increasing order:
+    // the thread's chunks c0 + tid + u * NTHR, in increasing order:
     // a strictly larger maximum is the only update needed
     float cv = -__builtin_inff();
     int cb = -1;
@@ -134,13 +142,13 @@ __global__ __launch_bounds__(kArgThreads) void argmax_kernel(const SelectArgs p)
         const int c0 = it * STEP + tid;
         u32x4 r[kArgUnroll];
 #pragma unroll
-        for (int u = 0; u < kArgUnroll; ++u) r[u] = body[c0 + u * kArgThreads];
+        for (int u = 0; u < kArgUnroll; ++u) r[u] = body[c0 + u * NTHR];
 #pragma unroll
         for (int u = 0; u < kArgUnroll; ++u) {
             const float m = chunk_max<F32>(r[u]);
             if (m > cv) {
                 cv = m;
-                cb = c0 + u * kArgThreads;
+                cb = c0 + u * NTHR;
                 cr = r[u];
             }
         }
@@ -149,13 +157,13 @@ __global__ __launch_bounds__(kArgThreads) void argmax_kernel(const SelectArgs p)
         const int c0 = nfull * STEP + tid;
         u32x4 r[kArgUnroll];
 #pragma unroll
-        for (int u = 0; u < kArgUnroll; ++u) r[u] = body[min(c0 + u * kArgThreads, nbody - 1)];
+        for (int u = 0; u < kArgUnroll; ++u) r[u] = body[min(c0 + u * NTHR, nbody - 1)];
 #pragma unroll
         for (int u = 0; u < kArgUnroll; ++u) {
             const float m = chunk_max<F32>(r[u]);
-            if (c0 + u * kArgThreads < nbody && m > cv) {
+            if (c0 + u * NTHR < nbody && m > cv) {
                 cv = m;
-                cb = c0 + u * kArgThreads;
+                cb = c0 + u * NTHR;
                 cr = r[u];
             }
         }
@@ -167,8 +175,8 @@ __global__ __launch_bounds__(kArgThreads) void argmax_kernel(const SelectArgs p)
         bi = head + cb * EPC + chunk_find<F32>(cr, cv);
     }
     if (tid < head) take_max(elem<F32>(base, tid), tid, bv, bi);
-    for (int i = tail0 + tid; i < V; i += kArgThreads) take_max(elem<F32>(base, i), i, bv, bi);
-    block_take_max(bv, bi, s_v, s_i, tid);
+    for (int i = tail0 + tid; i < V; i += NTHR) take_max(elem<F32>(base, i), i, bv, bi);
+    block_take_max<NTHR>(bv, bi, s_v, s_i, tid);
 
     if (bi == INT_MAX || bv == -__builtin_inff()) {
         // the row's largest value is -inf (or every value is NaN): no chunk
@@ -176,8 +184,8 @@ __global__ __launch_bounds__(kArgThreads) void argmax_kernel(const SelectArgs p)
         // full rule (the same decision in every thread)
         bv = -__builtin_inff();
         bi = INT_MAX;
-        for (int i = tid; i < V; i += kArgThreads) take_max(elem<F32>(base, i), i, bv, bi);
-        block_take_max(bv, bi, s_v, s_i, tid);
+        for (int i = tid; i < V; i += NTHR) take_max(elem<F32>(base, i), i, bv, bi);
+        block_take_max<NTHR>(bv, bi, s_v, s_i, tid);
     }
     if (tid == 0) p.target[row] = bi == INT_MAX ? 0 : bi;  // a row of NaN: 0
 }
@@ -222,10 +230,18 @@ __global__ __launch_bounds__(256) void walk_kernel(const SelectArgs p) {
 hipError_t launch_select(const SelectArgs& a, bool f32_logits, hipStream_t stream) {
     const long long rows = (long long)a.B * (a.T + 1);
     if (rows <= 0) return hipSuccess;
-    if (f32_logits)
-        hipLaunchKernelGGL(argmax_kernel<true>, dim3((unsigned)rows), dim3(kArgThreads), 0, stream, a);
-    else
-        hipLaunchKernelGGL(argmax_kernel<false>, dim3((unsigned)rows), dim3(kArgThreads), 0, stream, a);
+    const dim3 grid((unsigned)rows);
+    if (rows >= kArgFillRows) {
+        if (f32_logits)
+            hipLaunchKernelGGL((argmax_kernel<true, kArgThreadsNarrow>), grid, dim3(kArgThreadsNarrow), 0, stream, a);
+        else
+            hipLaunchKernelGGL((argmax_kernel<false, kArgThreadsNarrow>), grid, dim3(kArgThreadsNarrow), 0, stream, a);
+    } else {
+        if (f32_logits)
+            hipLaunchKernelGGL((argmax_kernel<true, kArgThreadsWide>), grid, dim3(kArgThreadsWide), 0, stream, a);
+        else
+            hipLaunchKernelGGL((argmax_kernel<false, kArgThreadsWide>), grid, dim3(kArgThreadsWide), 0, stream, a);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(walk_kernel, dim3((unsigned)((a.B + 3) / 4)), dim3(256), 0, stream, a);
