@@ -1,4 +1,5 @@
-// Device helpers shared by the verify, commit and gather kernels (gfx950).
+// Device helpers shared by the verify, commit, gather, read and selection
+// kernels (gfx950).
 //
 // MFMA tile used throughout: v_mfma_f32_16x16x32_bf16.  For one wave (64
 // lanes, g = lane / 16, c = lane % 16):
@@ -92,45 +93,6 @@ __device__ __forceinline__ floatx4 mma3(floatx4 acc, bf16x8 ah, bf16x8 al, bf16x
     return mfma16x16x32(al, bh, acc);
 }
 
-// An fp32 value packed as its two bf16 terms in one 32-bit word: the hi term
-// in the low half, the lo term in the high half.  A matrix that several
-// waves read as MFMA operands is packed once, so that each read only
-// separates the halves.
-__device__ __forceinline__ uint32_t pack_hilo(float x) {
-    const unsigned short h = bf16_bits(x);
-    const unsigned short l = bf16_bits(x - bf16_val(h));
-    return (uint32_t)h | ((uint32_t)l << 16);
-}
-
-// Eight packed values of one row as the hi and lo A/B fragments of k-step s
-// (runs k0 = 32 s + 4 g and k0 + 16; a run at or past `klim` reads as zero).
-__device__ __forceinline__ void frag_packed(const uint32_t* row, int s, int g, int klim, bf16x8& hi, bf16x8& lo) {
-    const int k0 = 32 * s + 4 * g;
-    const u32x4 z = {0u, 0u, 0u, 0u};
-    const u32x4 p0 = (k0 < klim) ? *reinterpret_cast<const u32x4*>(row + k0) : z;
-    const u32x4 p1 = (k0 + 16 < klim) ? *reinterpret_cast<const u32x4*>(row + k0 + 16) : z;
-    const u16x8 a = __builtin_bit_cast(u16x8, p0), b = __builtin_bit_cast(u16x8, p1);
-    const u16x8 h = {a[0], a[2], a[4], a[6], b[0], b[2], b[4], b[6]};
-    const u16x8 l = {a[1], a[3], a[5], a[7], b[1], b[3], b[5], b[7]};
-    hi = __builtin_bit_cast(bf16x8, h);
-    lo = __builtin_bit_cast(bf16x8, l);
-}
-
-// Eight fp32 values of one matrix row as an A/B fragment of k-step s: the
-// runs k0 = 32 s + 4 g and k0 + 16; a run at or past `klim` reads as zero.
-__device__ __forceinline__ void frag_f32(const float* row, int s, int g, int klim, float4& a, float4& b) {
-    const int k0 = 32 * s + 4 * g;
-    const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
-    a = (k0 < klim) ? *reinterpret_cast<const float4*>(row + k0) : z;
-    b = (k0 + 16 < klim) ? *reinterpret_cast<const float4*>(row + k0 + 16) : z;
-}
-
-// The value of a float register in lane `src` (a compile-time or uniform
-// index), broadcast to the whole wave through a scalar register.
-__device__ __forceinline__ float readlane_f(float v, int src) {
-    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), src));
-}
-
 // Streaming accesses: data read or written exactly once per call (states,
 // outputs).  Outputs go through non-temporal stores, which let HBM mix the
 // write stream with the read stream at less loss; the state reads stay
@@ -213,12 +175,6 @@ __device__ __forceinline__ unsigned xcd_remap(unsigned bid, unsigned nblocks) {
     return (x < rem) ? x * (per + 1) + t : rem * (per + 1) + (x - rem) * per + t;
 }
 
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, kWave));
-    return v;
-}
-
 __device__ __forceinline__ int wave_max_i(int v) {
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) v = max(v, __shfl_xor(v, off, kWave));
@@ -230,12 +186,6 @@ __device__ __forceinline__ uint64_t shfl_u64(uint64_t v, int src) {
     lo = __shfl(lo, src, kWave);
     hi = __shfl(hi, src, kWave);
     return ((uint64_t)hi << 32) | lo;
-}
-
-// Index of the i-th set bit (i counted from 0) of a uniform 64-bit mask.
-__device__ __forceinline__ int nth_set_bit(uint64_t m, int i) {
-    for (int j = 0; j < i; ++j) m &= m - 1;
-    return __builtin_ctzll(m);
 }
 
 }  // namespace ldv
