@@ -17,10 +17,14 @@
 //   1. issue the loads of the query chunk, K, the U tile, log P, the
 //      positions and the parent row, then the wave's S0 rows straight into
 //      MFMA operand registers (they stay in flight through steps 2-3);
-//   2. stage Q, K and the U tile in LDS; wave 0 turns the parent row into
-//      ancestor-or-self masks by pointer doubling;
-//   3. W[m, f] = [m on path(j_f)] exp(log P_j - log P_m) (k_m . q_f) on MFMA,
-//      one 16-query column block per wave;
+//   2. stage Q, K in LDS; wave 0 turns the parent row into ancestor-or-self
+//      masks by pointer doubling;
+//   3. W[m, f] = [m on path(j_f)] exp(log P_j - log P_m) (k_m . q_f) on
+//      MFMA, one 16-query column block per wave, into registers, then
+//      S0 Q^T on MFMA; once every wave is done with Q and K, W^T and U^T go
+//      as bf16 hi and lo planes into their place, so that LDS holds little
+//      more than Q and K (four blocks per CU at 64 nodes) and step 4 splits
+//      nothing;
 //   4. O^T = (S0 Q^T) diag(P_j) + U^T W on MFMA (S0, U and W carried as
 //      bf16 hi + lo terms), float4 stores.
 #include <limits.h>
@@ -41,8 +45,7 @@ struct RShape {
     static constexpr int NQ = 64;                // queries per block (one per lane of wave 0)
     static constexpr int NCB = NQ / 16;          // 16-query column blocks
     static constexpr int QKLD = D + 8;           // bf16 row stride of Q / K in LDS
-    static constexpr int ULD = BV + 4;           // fp32 row stride of the U tile
-    static constexpr int WLD = NQ + 4;           // fp32 row stride of W
+    static constexpr int WTLD = TM + 8;          // bf16 row stride of the W^T planes
     static constexpr int NKS = (TM + 31) / 32;   // MFMA k-steps over nodes
     static constexpr int LOG2TM = TM <= 16 ? 4 : (TM <= 32 ? 5 : 6);
 };
@@ -52,35 +55,41 @@ struct RLds {
     using S = RShape<D, TM>;
     static constexpr int NPL = F32IN ? 2 : 1;  // bf16 planes per operand (hi, then lo)
     static constexpr size_t off_k = (size_t)NPL * S::NQ * S::QKLD * 2;
-    static constexpr size_t off_u = off_k + (size_t)NPL * TM * S::QKLD * 2;
-    static constexpr size_t off_w = off_u + (size_t)TM * S::ULD * 4;
-    static constexpr size_t off_anc = off_w + (size_t)TM * S::WLD * 4;
+    static constexpr size_t qk = off_k + (size_t)NPL * TM * S::QKLD * 2;
+    // once Q and K are dead, their area holds the W^T hi and lo planes
+    // [NQ][WTLD] and the U^T hi and lo planes [BV][WTLD] (bf16)
+    static constexpr size_t off_ut = (size_t)2 * S::NQ * S::WTLD * 2;
+    static constexpr size_t wu = off_ut + (size_t)2 * S::BV * S::WTLD * 2;
+    static constexpr size_t off_anc = ((qk > wu ? qk : wu) + 15) / 16 * 16;
     static constexpr size_t off_lp = off_anc + 8 * TM;
     static constexpr size_t off_pos = off_lp + 4 * TM;
     static constexpr size_t off_flag = off_pos + 4 * S::NQ;
     static constexpr size_t total = off_flag + 16;
+    // waves per SIMD the registers must allow: what this block's LDS
+    // (160 KiB per CU) lets reside, at most four
+    static constexpr int lds_waves = (int)(163840 / total) * S::NW / 4;
+    static constexpr int WPE = lds_waves < 1 ? 1 : (lds_waves < 4 ? lds_waves : 4);
 };
 
 template <int D, int TM, bool F32IN>
-__global__ __launch_bounds__((RShape<D, TM>::NW * kWave)) void read_kernel(const ReadArgs p) {
+__global__ __launch_bounds__((RShape<D, TM>::NW * kWave))
+__attribute__((amdgpu_waves_per_eu(RLds<D, TM, F32IN>::WPE))) void read_kernel(const ReadArgs p) {
     using S = RShape<D, TM>;
     using L = RLds<D, TM, F32IN>;
     constexpr int BV = S::BV, NW = S::NW, KS = S::KS, NQ = S::NQ, NCB = S::NCB;
-    constexpr int QKLD = S::QKLD, ULD = S::ULD, WLD = S::WLD, NKS = S::NKS;
+    constexpr int QKLD = S::QKLD, WTLD = S::WTLD, NKS = S::NKS;
     constexpr int NTHR = NW * kWave;
     constexpr int EPC = F32IN ? 4 : 8;  // elements per 16-byte chunk
     constexpr int CPR = D / EPC;        // chunks per q/k row
     constexpr int QC = (NQ * CPR + NTHR - 1) / NTHR;
     constexpr int KC = (TM * CPR + NTHR - 1) / NTHR;
-    constexpr int U4 = BV / 4;  // float4 chunks per U row of the tile
-    constexpr int UC = (TM * U4 + NTHR - 1) / NTHR;
     static_assert(NQ == kWave, "one query column per lane of wave 0");
 
     __shared__ __align__(16) unsigned char smem[L::total];
     unsigned short* s_q = reinterpret_cast<unsigned short*>(smem);           // [NQ][QKLD] hi, then lo
     unsigned short* s_k = reinterpret_cast<unsigned short*>(smem + L::off_k);  // [TM][QKLD] hi, then lo
-    float* s_u = reinterpret_cast<float*>(smem + L::off_u);                  // [TM][ULD]
-    float* s_w = reinterpret_cast<float*>(smem + L::off_w);                  // [TM][WLD]
+    unsigned short* s_wt = reinterpret_cast<unsigned short*>(smem);          // [NQ][WTLD] hi, then lo (after Q, K)
+    unsigned short* s_ut = reinterpret_cast<unsigned short*>(smem + L::off_ut);  // [BV][WTLD] hi, then lo (after Q, K)
     uint64_t* s_anc = reinterpret_cast<uint64_t*>(smem + L::off_anc);       // [TM]
     float* s_lp = reinterpret_cast<float*>(smem + L::off_lp);                // [TM]
     int* s_pos = reinterpret_cast<int*>(smem + L::off_pos);                  // [NQ]
@@ -98,7 +107,7 @@ __global__ __launch_bounds__((RShape<D, TM>::NW * kWave)) void read_kernel(const
     const unsigned bh = r1 / S::NT;
     const int h = (int)(bh % (unsigned)H), b = (int)(bh / (unsigned)H);
     const int f0 = ch * NQ;
-    const int vrow0 = tile * BV + wave * 16;
+    const int vrow0 = tile * BV + __builtin_amdgcn_readfirstlane(wave) * 16;
 
     // 1. loads, small ones first, branch-free (indices clamped into range;
     // values past the ends are dropped when LDS is written)
@@ -120,14 +129,6 @@ __global__ __launch_bounds__((RShape<D, TM>::NW * kWave)) void read_kernel(const
         const size_t off = ((((size_t)b * T + m) * H + h) * D + col) * (F32IN ? 4 : 2);
         kreg[i] = *reinterpret_cast<const u32x4*>(static_cast<const char*>(p.k) + off);
     }
-    float4 ureg[UC];
-#pragma unroll
-    for (int i = 0; i < UC; ++i) {
-        const int chunk = tid + i * NTHR;
-        const int m = min(chunk / U4, T - 1);
-        ureg[i] = *reinterpret_cast<const float4*>(p.u + (((size_t)b * T + m) * H + h) * D + tile * BV +
-                                                   4 * (chunk % U4));
-    }
     const int nl = min(lane, T - 1);
     const float lp_ld = p.logp[((size_t)b * T + nl) * H + h];
     // a chain has no parent array: read the log-gate array instead (it has at
@@ -146,9 +147,20 @@ __global__ __launch_bounds__((RShape<D, TM>::NW * kWave)) void read_kernel(const
         sreg[s][0] = (k0 < D) ? ld_stream(s0row + k0) : make_float4(0.f, 0.f, 0.f, 0.f);
         sreg[s][1] = (k0 + 16 < D) ? ld_stream(s0row + k0 + 16) : make_float4(0.f, 0.f, 0.f, 0.f);
     }
+    // the U tile (nodes x this block's BV values), float4 per thread
+    constexpr int U4 = BV / 4;  // float4 chunks per U row of the tile
+    constexpr int UC = (TM * U4 + NTHR - 1) / NTHR;
+    float4 ureg[UC];
+#pragma unroll
+    for (int i = 0; i < UC; ++i) {
+        const int chunk = tid + i * NTHR;
+        const int m = min(chunk / U4, T - 1);
+        ureg[i] = *reinterpret_cast<const float4*>(p.u + (((size_t)b * T + m) * H + h) * D + tile * BV +
+                                                   4 * (chunk % U4));
+    }
     asm volatile("" ::: "memory");  // keep the loads above ahead of any use of them
 
-    // 2a. stage Q, K, U (rows past the ends zero)
+    // 2a. stage Q, K (rows past the ends zero)
     const u32x4 z4 = {0u, 0u, 0u, 0u};
 #pragma unroll
     for (int i = 0; i < QC; ++i) {
@@ -179,13 +191,6 @@ __global__ __launch_bounds__((RShape<D, TM>::NW * kWave)) void read_kernel(const
                 *reinterpret_cast<u16x4*>(s_k + (TM + row) * QKLD + col) = lo;
             }
         }
-    }
-#pragma unroll
-    for (int i = 0; i < UC; ++i) {
-        const int chunk = tid + i * NTHR, m = chunk / U4;
-        if (m < TM)
-            *reinterpret_cast<float4*>(s_u + m * ULD + 4 * (chunk % U4)) =
-                m < T ? ureg[i] : make_float4(0.f, 0.f, 0.f, 0.f);
     }
 
     // 2b. wave 0: per-query positions, log P, ancestor-or-self masks
@@ -228,39 +233,44 @@ __global__ __launch_bounds__((RShape<D, TM>::NW * kWave)) void read_kernel(const
         return;  // invalid parent row: nothing of the sequence is written
     }
 
-    // 3. W[m][f] = [m on path(j_f)] (P_j / P_m) k_m . q_f, column block cb
+    // 3a. W[m][f] = [m on path(j_f)] (P_j / P_m) k_m . q_f for the wave's
+    //     column blocks (needs only Q, K: it runs while the S0 rows are in
+    //     flight), kept in registers until Q and K are dead
+    constexpr int CBW = (NCB + NW - 1) / NW;  // column blocks per wave
+    floatx4 wreg[CBW][TM / 16];
 #pragma unroll
-    for (int cb = wave; cb < NCB; cb += NW) {
-        const int fcol = cb * 16 + c;
-        const int j = s_pos[fcol];
-        const bool node = j >= 0 && j < T;
-        const uint64_t am = node ? s_anc[j] : 0ull;
-        const float lpj = node ? s_lp[j] : 0.f;
+    for (int t = 0; t < CBW; ++t) {
+        const int cb = wave + t * NW;
+        if (cb < NCB) {
+            const int fcol = cb * 16 + c;
+            const int j = s_pos[fcol];
+            const bool node = j >= 0 && j < T;
+            const uint64_t am = node ? s_anc[j] : 0ull;
+            const float lpj = node ? s_lp[j] : 0.f;
 #pragma unroll
-        for (int mb = 0; mb < TM / 16; ++mb) {
-            floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+            for (int mb = 0; mb < TM / 16; ++mb) {
+                floatx4 w = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int s = 0; s < KS; ++s) {
-                const bf16x8 bk = frag_row<D>(s_k + (mb * 16 + c) * QKLD, s, g);
-                const bf16x8 bq = frag_row<D>(s_q + fcol * QKLD, s, g);
-                acc = mfma16x16x32(bk, bq, acc);
-                if constexpr (F32IN) {
-                    acc = mfma16x16x32(bk, frag_row<D>(s_q + (NQ + fcol) * QKLD, s, g), acc);
-                    acc = mfma16x16x32(frag_row<D>(s_k + (TM + mb * 16 + c) * QKLD, s, g), bq, acc);
+                for (int s = 0; s < KS; ++s) {
+                    const bf16x8 bk = frag_row<D>(s_k + (mb * 16 + c) * QKLD, s, g);
+                    const bf16x8 bq = frag_row<D>(s_q + fcol * QKLD, s, g);
+                    w = mfma16x16x32(bk, bq, w);
+                    if constexpr (F32IN) {
+                        w = mfma16x16x32(bk, frag_row<D>(s_q + (NQ + fcol) * QKLD, s, g), w);
+                        w = mfma16x16x32(frag_row<D>(s_k + (TM + mb * 16 + c) * QKLD, s, g), bq, w);
+                    }
                 }
-            }
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int m = mb * 16 + 4 * g + r;
-                s_w[m * WLD + fcol] = ((am >> m) & 1ull) ? expf(lpj - s_lp[m]) * acc[r] : 0.f;
+                for (int r = 0; r < 4; ++r) {
+                    const int m = mb * 16 + 4 * g + r;
+                    wreg[t][mb][r] = ((am >> m) & 1ull) ? expf(lpj - s_lp[m]) * w[r] : 0.f;
+                }
             }
         }
     }
-    __syncthreads();
-
-    // 4. O^T = (S0 Q^T) diag(P_j) + U^T W for the wave's 16 value rows:
-    //    lane (c, g) of column block cb holds query f0 + 16 cb + c, values
-    //    vrow0 + 4 g .. +3
+    // 3b. S0 Q^T for the wave's 16 value rows (once the S0 rows are in):
+    //     lane (c, g) of column block cb holds query f0 + 16 cb + c, values
+    //     vrow0 + 4 g .. +3
     floatx4 acc[NCB];
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) acc[cb] = floatx4{0.f, 0.f, 0.f, 0.f};
@@ -276,6 +286,43 @@ __global__ __launch_bounds__((RShape<D, TM>::NW * kWave)) void read_kernel(const
             if constexpr (F32IN) acc[cb] = mfma16x16x32(sh, frag_row<D>(s_q + (NQ + cb * 16 + c) * QKLD, s, g), acc[cb]);
         }
     }
+
+    __syncthreads();  // Q and K dead in every wave
+    // 3c. W^T into the Q / K area as bf16 hi and lo planes: row f, the four
+    //     nodes 16 mb + 4 g .. +3 of this lane
+#pragma unroll
+    for (int t = 0; t < CBW; ++t) {
+        const int cb = wave + t * NW;
+        if (cb < NCB) {
+            const int f = cb * 16 + c;
+#pragma unroll
+            for (int mb = 0; mb < TM / 16; ++mb) {
+                u16x4 hi, lo;
+                split4(make_float4(wreg[t][mb][0], wreg[t][mb][1], wreg[t][mb][2], wreg[t][mb][3]), hi, lo);
+                *reinterpret_cast<u16x4*>(s_wt + f * WTLD + mb * 16 + 4 * g) = hi;
+                *reinterpret_cast<u16x4*>(s_wt + (NQ + f) * WTLD + mb * 16 + 4 * g) = lo;
+            }
+        }
+    }
+    //     U^T likewise: the four values of this thread's chunk of node m go
+    //     to rows v .. v + 3 of the U^T planes (nodes past T zero)
+#pragma unroll
+    for (int i = 0; i < UC; ++i) {
+        const int chunk = tid + i * NTHR, m = chunk / U4, v = 4 * (chunk % U4);
+        if (m < TM) {
+            const float4 uv = m < T ? ureg[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+            u16x4 hi, lo;
+            split4(uv, hi, lo);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                s_ut[(v + e) * WTLD + m] = hi[e];
+                s_ut[(BV + v + e) * WTLD + m] = lo[e];
+            }
+        }
+    }
+    __syncthreads();
+
+    // 4. O^T = (S0 Q^T) diag(P_j) + U^T W
     int jcol[NCB];
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) {
@@ -285,27 +332,15 @@ __global__ __launch_bounds__((RShape<D, TM>::NW * kWave)) void read_kernel(const
 #pragma unroll
         for (int r = 0; r < 4; ++r) acc[cb][r] *= Pj;
     }
+    const unsigned short* urow = s_ut + (wave * 16 + c) * WTLD;  // U^T row of value vrow0 + c
 #pragma unroll
     for (int s = 0; s < NKS; ++s) {
-        const int m0 = 32 * s + 4 * g;
-        float uu[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int m = m0 + (e & 3) + (e >> 2) * 16;
-            uu[e] = m < TM ? s_u[m * ULD + wave * 16 + c] : 0.f;
-        }
-        bf16x8 uh, ul;
-        split8(make_float4(uu[0], uu[1], uu[2], uu[3]), make_float4(uu[4], uu[5], uu[6], uu[7]), uh, ul);
+        const bf16x8 uh = frag_row<TM>(urow, s, g), ul = frag_row<TM>(urow + BV * WTLD, s, g);
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb) {
-            float ww[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int m = m0 + (e & 3) + (e >> 2) * 16;
-                ww[e] = m < TM ? s_w[m * WLD + cb * 16 + c] : 0.f;
-            }
-            bf16x8 wh, wl;
-            split8(make_float4(ww[0], ww[1], ww[2], ww[3]), make_float4(ww[4], ww[5], ww[6], ww[7]), wh, wl);
+            const unsigned short* wrow = s_wt + (cb * 16 + c) * WTLD;
+            const bf16x8 wh = frag_row<TM>(wrow, s, g);
+            const bf16x8 wl = frag_row<TM>(wrow + NQ * WTLD, s, g);
             acc[cb] = mma3(acc[cb], uh, ul, wh, wl);
         }
     }
