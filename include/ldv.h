@@ -36,6 +36,13 @@
  *   - Alignment: q, k, v, S0, o, u, S_out, pool, queries, states_out need 16
  *     bytes; the [B, T, H] gate/log arrays, index arrays and status need 4.
  *   - Supported sizes: d_k == d_v in {16, 32, 64, 128}; 1 <= T <= 64.
+ *   - Drafts of different lengths in one batch: T is the batch's largest
+ *     draft; a shorter draft is padded with nodes placed after its real
+ *     ones (each under any earlier node, or a root) with draft token -1.
+ *     A node's outputs depend only on its own root-to-node path (Eq. (2)),
+ *     so padding leaves every real node's o, u and log P unchanged, and
+ *     ldv_select_accepted never accepts a node whose token is outside
+ *     [0, V), so the committed state is always a real node's.
  */
 #ifndef LDV_H
 #define LDV_H
