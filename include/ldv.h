@@ -36,6 +36,12 @@
  *   - Alignment: q, k, v, S0, o, u, S_out, pool, queries, states_out need 16
  *     bytes; the [B, T, H] gate/log arrays, index arrays and status need 4.
  *   - Supported sizes: d_k == d_v in {16, 32, 64, 128}; 1 <= T <= 64.
+ *   - One launch holds at most 2^32 - 1 work-items (the dispatch grid size
+ *     is 32 bits), so B * H <= 2^23 - 1 for verify, B * H <= 2^22 - 1 for
+ *     commit and long chains, B * P * H <= 2^23 - 1 for the gathers,
+ *     B * H * ceil(P * Qn / 64) <= 2^23 - 1 for the in-block reads and
+ *     B * (T + 1) <= 2^23 - 1 for selection; larger shapes return
+ *     LDV_ERR_UNSUPPORTED.
  *   - Drafts of different lengths in one batch: T is the batch's largest
  *     draft; a shorter draft is padded with nodes placed after its real
  *     ones (each under any earlier node, or a root) with draft token -1.

@@ -15,6 +15,13 @@ bool aligned(const void* p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p
 
 bool supported_d(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
 
+// A launch dispatches at most 2^32 - 1 work-items (the dispatch packet's grid
+// size is 32 bits).  `units` independent units of at most `per_unit`
+// work-items each must fit: verify 512 per (sequence, head), commit 1024 per
+// (sequence, head), gather 512 per (sequence, position, head), the in-block
+// read 512 per (sequence, head, chunk of 64 queries), selection 512 per row.
+bool grid_fits(long long units, long long per_unit) { return units * per_unit <= 0xffffffffLL; }
+
 // Shared checks of the verify calls.
 int check_verify(int B, int T, int H, int dk, int dv, int dt, const void* q, const void* k, const void* v,
                  const float* a, const float* beta, const float* S0, const float* o, const float* u_out,
@@ -29,7 +36,7 @@ int check_verify(int B, int T, int H, int dk, int dv, int dt, const void* q, con
         !aligned(u_out, 16) || !aligned(a, 4) || !aligned(beta, 4) || !aligned(logp_out, 4) ||
         !aligned(status, 4))
         return LDV_ERR_ARG;
-    if ((long long)B * H * 2 > 0x7fffffffLL || (long long)B * T > 0x7fffffffLL) return LDV_ERR_UNSUPPORTED;
+    if (!grid_fits((long long)B * H, 512) || (long long)B * T > 0x7fffffffLL) return LDV_ERR_UNSUPPORTED;
     // each (sequence, head) is read and written through views of T rows of
     // H * d elements with 32-bit byte offsets
     if ((long long)T * H * dk * 4 > 0xffffffffLL) return LDV_ERR_UNSUPPORTED;
@@ -79,7 +86,7 @@ LDV_EXPORT int ldv_verify_chain_long(int B, int T, int H, int dk, int dv, int qk
         !aligned(u_out, 16) || !aligned(S_work, 16) || !aligned(a, 4) || !aligned(beta, 4) ||
         !aligned(logp_out, 4) || !aligned(status, 4))
         return LDV_ERR_ARG;
-    if ((long long)B * H * 4 > 0x7fffffffLL || (long long)B * T > 0x7fffffffLL) return LDV_ERR_UNSUPPORTED;
+    if (!grid_fits((long long)B * H, 1024) || (long long)B * T > 0x7fffffffLL) return LDV_ERR_UNSUPPORTED;
     if ((long long)(T < LDV_MAX_T ? T : LDV_MAX_T) * H * dk * 4 > 0xffffffffLL) return LDV_ERR_UNSUPPORTED;
     if (S_work) {  // S_work must not overlap S0 (the first chunk reads S0 while later ones write S_work)
         const char *w0 = reinterpret_cast<const char*>(S_work), *s0 = reinterpret_cast<const char*>(S0);
@@ -116,8 +123,7 @@ LDV_EXPORT int ldv_commit_state(int B, int T, int H, int dk, int dv, int k_dtype
     if (!aligned(k, 16) || !aligned(u, 16) || !aligned(S0, 16) || !aligned(S_out, 16) || !aligned(logp, 4) ||
         !aligned(parent, 4) || !aligned(accepted, 4) || !aligned(status, 4))
         return LDV_ERR_ARG;
-    if ((long long)B * H * 4 > 0x7fffffffLL) return LDV_ERR_UNSUPPORTED;
-    if ((long long)B * T > 0x7fffffffLL) return LDV_ERR_UNSUPPORTED;
+    if (!grid_fits((long long)B * H, 1024) || (long long)B * T > 0x7fffffffLL) return LDV_ERR_UNSUPPORTED;
     ldv::CommitArgs args{B, T, H, dk, T, 0, -2, k, u, logp, parent, accepted, S0, S_out, status};
     hipError_t e = ldv::launch_commit(args, k_dtype == LDV_F32, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? LDV_OK : LDV_ERR_LAUNCH;
@@ -147,7 +153,7 @@ int gather_common(int B, int P, int H, int dk, int dv, int num_slots, int Qn, in
     if (!aligned(pool, 16) || !aligned(queries, 16) || !aligned(o.base, o.bf16 ? 8 : 16) ||
         !aligned(states_out, 16) || !aligned(slot, 4) || !aligned(status, 4))
         return LDV_ERR_ARG;
-    if ((long long)B * P * H > 0x7fffffffLL) return LDV_ERR_UNSUPPORTED;
+    if (!grid_fits((long long)B * P * H, 512)) return LDV_ERR_UNSUPPORTED;
     ldv::GatherArgs args{B, P, H, dk, num_slots, queries ? Qn : 0, pool, slot, queries, o, states_out, status};
     hipError_t e = ldv::launch_gather(args, q_dtype == LDV_F32, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? LDV_OK : LDV_ERR_LAUNCH;
@@ -165,8 +171,7 @@ int read_common(int B, int T, int H, int dk, int dv, int P, int Qn, int qk_dtype
         !aligned(o.base, o.bf16 ? 8 : 16) || !aligned(logp, 4) || !aligned(parent, 4) || !aligned(pos, 4) ||
         !aligned(status, 4))
         return LDV_ERR_ARG;
-    if ((long long)P * Qn > 0x7fffffffLL ||
-        (long long)B * H * 2 * (((long long)P * Qn + 63) / 64) > 0x7fffffffLL)
+    if ((long long)P * Qn > 0x7fffffffLL || !grid_fits((long long)B * H * (((long long)P * Qn + 63) / 64), 512))
         return LDV_ERR_UNSUPPORTED;
     ldv::ReadArgs args{B, T, H, dk, P, Qn, k, u, logp, parent, S0, pos, queries, o, status};
     hipError_t e = ldv::launch_read(args, qk_dtype == LDV_F32, static_cast<hipStream_t>(stream));
@@ -227,7 +232,7 @@ LDV_EXPORT int ldv_select_accepted(int B, int T, int V, int logits_dtype, const 
         !aligned(target, 4) || !aligned(accepted, 4) || !aligned(accepted_len, 4) || !aligned(bonus, 4) ||
         !aligned(status, 4))
         return LDV_ERR_ARG;
-    if ((long long)B * (T + 1) > 0x7fffffffLL) return LDV_ERR_UNSUPPORTED;
+    if (!grid_fits((long long)B * (T + 1), 512)) return LDV_ERR_UNSUPPORTED;
     ldv::SelectArgs args{B, T, V, logits, tokens, parent, target, accepted, accepted_len, bonus, status};
     hipError_t e = ldv::launch_select(args, logits_dtype == LDV_F32, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? LDV_OK : LDV_ERR_LAUNCH;
@@ -237,7 +242,9 @@ LDV_EXPORT const char* ldv_status_string(int code) {
     switch (code) {
         case LDV_OK: return "ok";
         case LDV_ERR_ARG: return "invalid argument (null pointer, negative size, bad dtype or misaligned pointer)";
-        case LDV_ERR_UNSUPPORTED: return "unsupported size (need d_k == d_v in {16, 32, 64, 128} and T <= 64)";
+        case LDV_ERR_UNSUPPORTED:
+            return "unsupported size (d_k == d_v in {16, 32, 64, 128}, T <= 64 except for chains, and the size "
+                   "limits of the call)";
         case LDV_ERR_LAUNCH: return "HIP kernel launch failed";
         default: return "unknown status code";
     }

@@ -170,3 +170,23 @@ def test_packed_argument_codes(lib):
         assert call(B=0) == 0
     assert g(q=None) == -1
     assert g(d=96) == -2
+
+
+def test_work_item_limits(lib):
+    """One launch holds at most 2^32 - 1 work-items: the host rejects shapes
+    whose launch would not fit (nothing is dereferenced or launched)."""
+    v = lambda B, H: lib.ldv_verify_chain(B, 1, H, 16, 16, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                          None, None, None, None)
+    assert v(1 << 12, 1 << 11) == -2              # 2^23 heads x 512 work-items = 2^32
+    c = lambda B, H: lib.ldv_commit_state(B, 1, H, 16, 16, 0, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE,
+                                          None, None)
+    assert c(1 << 11, 1 << 11) == -2              # 2^22 heads x 1024 work-items = 2^32
+    g = lambda B, P, H: lib.ldv_gather_states(B, P, H, 16, 16, 1, 0, 0, FAKE, FAKE, None, None, FAKE,
+                                              None, None)
+    assert g(1 << 11, 4, 1 << 10) == -2           # 2^23 (sequence, position, head) units
+    r = lambda B, H, P, Qn: lib.ldv_read_block_states(B, 1, H, 16, 16, P, Qn, 0, FAKE, FAKE, FAKE, None,
+                                                      FAKE, FAKE, FAKE, FAKE, None, None)
+    assert r(1 << 12, 1 << 10, 8, 16) == -2       # 2^22 heads x 2 chunks = 2^23 units
+    s = lambda B, T: lib.ldv_select_accepted(B, T, 1, 1, FAKE, FAKE, None, FAKE, FAKE, None, None, None, None)
+    assert s((1 << 23) // 8, 7) == -2             # 2^23 rows
+
