@@ -55,7 +55,8 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
                                                  ip, vp]
     lib.ldv_select_accepted.argtypes = [i, i, i, i, vp, ip, ip, ip, ip, ip, ip, ip, vp]
     for f in ("ldv_verify_tree", "ldv_verify_chain", "ldv_verify_chain_long", "ldv_commit_state", "ldv_gather_states",
-              "ldv_read_block_states", "ldv_select_accepted", "ldv_version"):
+              "ldv_read_block_states", "ldv_gather_states_packed", "ldv_read_block_states_packed",
+              "ldv_select_accepted", "ldv_version"):
         getattr(lib, f).restype = ctypes.c_int
     lib.ldv_status_string.argtypes = [ctypes.c_int]
     lib.ldv_status_string.restype = ctypes.c_char_p
@@ -96,14 +97,34 @@ def _qkv_code(t: torch.Tensor) -> int:
     raise TypeError("q/k/v/queries must be bfloat16 or float32 (got %s)" % t.dtype)
 
 
-def _stream(stream) -> ctypes.c_void_p:
-    s = torch.cuda.current_stream() if stream is None else stream
-    return ctypes.c_void_p(s.cuda_stream)
+def _stream(stream, dev: torch.device) -> ctypes.c_void_p:
+    """The HIP stream to enqueue on: the given one, else torch's current
+    stream of the tensors' device."""
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    elif stream.device != dev:
+        raise ValueError("stream is on %s, the tensors on %s" % (stream.device, dev))
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _same_device(dev: torch.device, **tensors):
+    """One call works on one GPU: every tensor it is given must be there."""
+    for name, t in tensors.items():
+        if t is not None and t.device != dev:
+            raise ValueError("%s is on %s, the call's other tensors on %s" % (name, t.device, dev))
 
 
 def _check(fn: str, rc: int):
     if rc != LDV_OK:
         raise LdvError(fn, rc)
+
+
+def _invoke(fn: str, dev: torch.device, *args):
+    """Call the C entry point with ``dev`` current, so that the HIP runtime
+    and the stream agree on the device."""
+    with torch.cuda.device(dev):
+        rc = getattr(load(), fn)(*args)
+    _check(fn, rc)
 
 
 def _opt(t, name, dtype, shape, dev):
@@ -137,8 +158,9 @@ def _verify(fn, q, k, v, a, beta, S0, parent, o, u, logp, factors, status, strea
     if fn == "ldv_verify_tree":
         _dev(parent, "parent", torch.int32, (B, T))
         args.append(_ptr(parent))
-    args += [_ptr(o), _ptr(u), _ptr(logp), _ptr(status), _stream(stream)]
-    _check(fn, getattr(load(), fn)(*args))
+    _same_device(dev, k=k, v=v, a=a, beta=beta, S0=S0, parent=parent, o=o, u=u, logp=logp, status=status)
+    args += [_ptr(o), _ptr(u), _ptr(logp), _ptr(status), _stream(stream, dev)]
+    _invoke(fn, dev, *args)
     return o, u, logp
 
 
@@ -187,9 +209,10 @@ def verify_chain_long(q, k, v, a, beta, S0, o=None, u=None, logp=None, S_work=No
         _dev(S_work, "S_work", torch.float32, (B, H, dv, dk))
     if status is not None:
         _dev(status, "status", torch.int32)
-    _check("ldv_verify_chain_long", load().ldv_verify_chain_long(
-        B, T, H, dk, dv, code, _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(beta), _ptr(S0), _ptr(o), _ptr(u),
-        _ptr(logp), _ptr(S_work), _ptr(status), _stream(stream)))
+    _same_device(dev, k=k, v=v, a=a, beta=beta, S0=S0, o=o, u=u, logp=logp, S_work=S_work, status=status)
+    _invoke("ldv_verify_chain_long", dev,
+            B, T, H, dk, dv, code, _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(beta), _ptr(S0), _ptr(o), _ptr(u),
+            _ptr(logp), _ptr(S_work), _ptr(status), _stream(stream, dev))
     return o, u, logp
 
 
@@ -219,9 +242,11 @@ def commit_state(k, u, logp, accepted, S0, S_out=None, parent=None, status=None,
             raise ValueError("S_out overlaps S0 without being S0")
     if status is not None:
         _dev(status, "status", torch.int32)
-    _check("ldv_commit_state", load().ldv_commit_state(
-        B, T, H, dk, dv, code, _ptr(k), _ptr(u), _ptr(logp), _ptr(parent), _ptr(accepted),
-        _ptr(S0), _ptr(S_out), _ptr(status), _stream(stream)))
+    dev = k.device
+    _same_device(dev, u=u, logp=logp, accepted=accepted, S0=S0, parent=parent, S_out=S_out, status=status)
+    _invoke("ldv_commit_state", dev,
+            B, T, H, dk, dv, code, _ptr(k), _ptr(u), _ptr(logp), _ptr(parent), _ptr(accepted),
+            _ptr(S0), _ptr(S_out), _ptr(status), _stream(stream, dev))
     return S_out
 
 
@@ -253,9 +278,10 @@ def gather_states(pool, slot, queries=None, o=None, states_out=None, want_states
         _dev(states_out, "states_out", torch.float32, (B, P, H, dv, dk))
     if status is not None:
         _dev(status, "status", torch.int32)
-    _check("ldv_gather_states", load().ldv_gather_states(
-        B, P, H, dk, dv, num_slots, Qn, code, _ptr(pool), _ptr(slot), _ptr(queries), _ptr(o),
-        _ptr(states_out), _ptr(status), _stream(stream)))
+    _same_device(dev, slot=slot, queries=queries, o=o, states_out=states_out, status=status)
+    _invoke("ldv_gather_states", dev,
+            B, P, H, dk, dv, num_slots, Qn, code, _ptr(pool), _ptr(slot), _ptr(queries), _ptr(o),
+            _ptr(states_out), _ptr(status), _stream(stream, dev))
     return o, states_out
 
 
@@ -289,9 +315,11 @@ def read_block_states(k, u, logp, S0, pos, queries, parent=None, o=None, status=
     o = _opt(o, "o", torch.float32, (B, P, H, Qn, dv), k.device)
     if status is not None:
         _dev(status, "status", torch.int32)
-    _check("ldv_read_block_states", load().ldv_read_block_states(
-        B, T, H, dk, dv, P, Qn, code, _ptr(k), _ptr(u), _ptr(logp), _ptr(parent), _ptr(S0), _ptr(pos),
-        _ptr(queries), _ptr(o), _ptr(status), _stream(stream)))
+    dev = k.device
+    _same_device(dev, u=u, logp=logp, S0=S0, pos=pos, queries=queries, parent=parent, o=o, status=status)
+    _invoke("ldv_read_block_states", dev,
+            B, T, H, dk, dv, P, Qn, code, _ptr(k), _ptr(u), _ptr(logp), _ptr(parent), _ptr(S0), _ptr(pos),
+            _ptr(queries), _ptr(o), _ptr(status), _stream(stream, dev))
     return o
 
 
@@ -332,9 +360,11 @@ def gather_states_packed(pool, slot, queries, feat, col=0, status=None, stream=N
     fcode, W = _feat(feat, B, P, H * Qn * dv, col)
     if status is not None:
         _dev(status, "status", torch.int32)
-    _check("ldv_gather_states_packed", load().ldv_gather_states_packed(
-        B, P, H, dk, dv, num_slots, Qn, code, _ptr(pool), _ptr(slot), _ptr(queries), _ptr(feat), W, col, fcode,
-        _ptr(status), _stream(stream)))
+    dev = pool.device
+    _same_device(dev, slot=slot, queries=queries, feat=feat, status=status)
+    _invoke("ldv_gather_states_packed", dev,
+            B, P, H, dk, dv, num_slots, Qn, code, _ptr(pool), _ptr(slot), _ptr(queries), _ptr(feat), W, col,
+            fcode, _ptr(status), _stream(stream, dev))
     return feat
 
 
@@ -363,9 +393,11 @@ def read_block_states_packed(k, u, logp, S0, pos, queries, feat, col=0, parent=N
     fcode, W = _feat(feat, B, P, H * Qn * dv, col)
     if status is not None:
         _dev(status, "status", torch.int32)
-    _check("ldv_read_block_states_packed", load().ldv_read_block_states_packed(
-        B, T, H, dk, dv, P, Qn, code, _ptr(k), _ptr(u), _ptr(logp), _ptr(parent), _ptr(S0), _ptr(pos),
-        _ptr(queries), _ptr(feat), W, col, fcode, _ptr(status), _stream(stream)))
+    dev = k.device
+    _same_device(dev, u=u, logp=logp, S0=S0, pos=pos, queries=queries, parent=parent, feat=feat, status=status)
+    _invoke("ldv_read_block_states_packed", dev,
+            B, T, H, dk, dv, P, Qn, code, _ptr(k), _ptr(u), _ptr(logp), _ptr(parent), _ptr(S0), _ptr(pos),
+            _ptr(queries), _ptr(feat), W, col, fcode, _ptr(status), _stream(stream, dev))
     return feat
 
 
@@ -393,9 +425,11 @@ def select_accepted(logits, tokens, parent=None, target=None, accepted=None, acc
     bonus = _opt(bonus, "bonus", torch.int32, (B,), dev)
     if status is not None:
         _dev(status, "status", torch.int32)
-    _check("ldv_select_accepted", load().ldv_select_accepted(
-        B, T, V, code, _ptr(logits), _ptr(tokens), _ptr(parent), _ptr(target), _ptr(accepted),
-        _ptr(accepted_len), _ptr(bonus), _ptr(status), _stream(stream)))
+    _same_device(dev, tokens=tokens, parent=parent, target=target, accepted=accepted,
+                 accepted_len=accepted_len, bonus=bonus, status=status)
+    _invoke("ldv_select_accepted", dev,
+            B, T, V, code, _ptr(logits), _ptr(tokens), _ptr(parent), _ptr(target), _ptr(accepted),
+            _ptr(accepted_len), _ptr(bonus), _ptr(status), _stream(stream, dev))
     return target, accepted, accepted_len, bonus
 
 
