@@ -36,6 +36,7 @@ CASES = [
     (128, 8, "chain", "bf16", True), (128, 16, "chain", "bf16", False), (128, 37, "tree", "bf16", True),
     (128, 64, "tree", "bf16", False), (128, 64, "chain", "bf16", True), (64, 20, "tree", "bf16", False),
     (32, 9, "chain", "f32", False), (16, 4, "chain", "f32", True), (16, 50, "tree", "bf16", False),
+    (128, 64, "tree", "f32", True), (128, 30, "chain", "f32", False),
 ]
 
 

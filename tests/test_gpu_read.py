@@ -57,6 +57,7 @@ GRID = [  # D, T, topology, qkv, P, Qn
     (32, 48, "tree", "bf16", 3, 3),
     (16, 4, "chain", "f32", 3, 2),
     (16, 64, "tree", "bf16", 2, 40),
+    (128, 64, "tree", "f32", 3, 9), (128, 40, "chain", "f32", 2, 17),
 ]
 
 

@@ -50,6 +50,8 @@ GRID = [
     (128, 64, "chain", "bf16"), (128, 20, "tree", "f32"),
     (64, 5, "tree", "bf16"), (64, 33, "tree", "bf16"), (64, 64, "chain", "bf16"),
     (32, 12, "tree", "bf16"), (32, 40, "chain", "f32"), (16, 4, "chain", "f32"), (16, 29, "tree", "bf16"),
+    # fp32 q/k/v at every node-block count of d = 128 (hi and lo planes in LDS)
+    (128, 9, "chain", "f32"), (128, 33, "tree", "f32"), (128, 64, "tree", "f32"), (64, 64, "chain", "f32"),
 ]
 
 
