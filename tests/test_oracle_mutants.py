@@ -27,6 +27,14 @@ MUTANTS = {
     "argmax keeps the last maximum": ("if (best < 0 || t > bv) {", "if (best < 0 || t >= bv) {"),
     "walk takes the last matching child": ("next = c;\n                    break;", "next = c;"),
     "bonus read one row early": ("if (bonus) bonus[b] = tg[cur + 1];", "if (bonus) bonus[b] = tg[cur < 0 ? 0 : cur];"),
+    "commit at the node before the accepted one": (
+        "walk_to(c, b, h, c->accepted[b], S, x, path, NULL);",
+        "walk_to(c, b, h, c->accepted[b] > 0 ? c->accepted[b] - 1 : c->accepted[b], S, x, path, NULL);"),
+    "gather reads the state transposed": ("acc += (double)src[(size_t)r * c->dk + j] * (double)qv[j];",
+                                          "acc += (double)src[(size_t)j * c->dk + r] * (double)qv[j];"),
+    "gather pairs an output with the next query": (
+        "const float* qv = c->queries + (((size_t)bp * c->H + h) * c->Qn + i) * c->dk;",
+        "const float* qv = c->queries + (((size_t)bp * c->H + h) * c->Qn + (i + 1) % c->Qn) * c->dk;"),
 }
 
 
