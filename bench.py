@@ -323,7 +323,7 @@ def main():
                          "rocprofv3 FETCH_SIZE / WRITE_SIZE counters, and print its bandwidth")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+        print("bench.py runs on one GPU only: the library has no multi-GPU path "
               "(each (sequence, head) is independent, so the batch or the heads shard with no exchange).",
               file=sys.stderr)
         sys.exit(2)
