@@ -175,6 +175,20 @@ __device__ __forceinline__ unsigned xcd_remap(unsigned bid, unsigned nblocks) {
     return (x < rem) ? x * (per + 1) + t : rem * (per + 1) + (x - rem) * per + t;
 }
 
+// Block index remap for work whose cost varies from unit to unit (a unit =
+// `per` consecutive logical blocks, e.g. the row blocks of one head): the
+// blocks of a unit stay on one XCD (and share its L2), and consecutive units
+// go to different XCDs, so that uneven units (heads with nothing to commit
+// next to heads with long paths) spread over all eight XCDs.  Hardware block
+// 8 t + x runs on XCD x and becomes block (t % per) of unit
+// 8 (t / per) + x; the units past the last multiple of 8 keep their order.
+__host__ __device__ __forceinline__ unsigned xcd_spread(unsigned bid, unsigned units, unsigned per) {
+    const unsigned full = (units / kXcds) * kXcds * per;  // blocks of the first 8 * (units / 8) units
+    if (bid >= full) return bid;
+    const unsigned x = bid % kXcds, t = bid / kXcds;
+    return ((t / per) * kXcds + x) * per + t % per;
+}
+
 __device__ __forceinline__ int wave_max_i(int v) {
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) v = max(v, __shfl_xor(v, off, kWave));
