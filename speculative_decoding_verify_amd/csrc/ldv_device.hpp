@@ -166,20 +166,12 @@ __device__ __forceinline__ bf16x8 frag_row(const unsigned short* row, int s, int
     return join(c0, c1);
 }
 
-// Block index remap so that consecutive logical blocks share an XCD (and its
-// L2).  The dispatcher places hardware block i on XCD i % 8; logical blocks
-// [base(x), base(x) + count(x)) are given to the hardware blocks of XCD x.
-__device__ __forceinline__ unsigned xcd_remap(unsigned bid, unsigned nblocks) {
-    const unsigned x = bid % kXcds, t = bid / kXcds;
-    const unsigned per = nblocks / kXcds, rem = nblocks % kXcds;
-    return (x < rem) ? x * (per + 1) + t : rem * (per + 1) + (x - rem) * per + t;
-}
-
-// Block index remap for work whose cost varies from unit to unit (a unit =
-// `per` consecutive logical blocks, e.g. the row blocks of one head): the
-// blocks of a unit stay on one XCD (and share its L2), and consecutive units
-// go to different XCDs, so that uneven units (heads with nothing to commit
-// next to heads with long paths) spread over all eight XCDs.  Hardware block
+// Block index remap (the dispatcher places hardware block i on XCD i % 8,
+// and each XCD has its own L2).  A unit is `per` consecutive logical blocks,
+// e.g. the row blocks of one head: the blocks of a unit stay on one XCD (and
+// share its L2), and consecutive units go to different XCDs, so that uneven
+// units (heads with nothing to commit next to heads with long paths) spread
+// over all eight XCDs.  Hardware block
 // 8 t + x runs on XCD x and becomes block (t % per) of unit
 // 8 (t / per) + x; the units past the last multiple of 8 keep their order.
 __host__ __device__ __forceinline__ unsigned xcd_spread(unsigned bid, unsigned units, unsigned per) {

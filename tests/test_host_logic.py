@@ -1,0 +1,55 @@
+"""Host-side checks of device helpers that decide which data a block works
+on, compiled from the library's own header with hipcc and run on the CPU
+(no GPU call is made)."""
+import os
+import shutil
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+
+PROG = r"""
+#include <cstdio>
+#include <vector>
+#include "ldv_device.hpp"
+// Every hardware block maps to exactly one logical block, and below the tail
+// the blocks of one unit share the XCD (hardware block i runs on XCD i % 8).
+int main() {
+    long bad = 0, cases = 0;
+    for (unsigned units = 1; units <= 700; ++units)
+        for (unsigned per = 1; per <= 8; ++per) {
+            const unsigned n = units * per, full = (units / 8) * 8 * per;
+            std::vector<int> seen(n, 0);
+            std::vector<int> xcd(units, -1);
+            for (unsigned b = 0; b < n; ++b) {
+                const unsigned l = ldv::xcd_spread(b, units, per);
+                if (l >= n) { ++bad; continue; }
+                ++seen[l];
+                if (b < full) {
+                    const unsigned u = l / per;
+                    if (xcd[u] < 0) xcd[u] = (int)(b % 8);
+                    else if (xcd[u] != (int)(b % 8)) ++bad;
+                }
+            }
+            for (unsigned l = 0; l < n; ++l) bad += seen[l] != 1;
+            ++cases;
+        }
+    std::printf("%ld cases, %ld bad\n", cases, bad);
+    return bad != 0;
+}
+"""
+
+
+@pytest.mark.skipif(not os.path.exists(HIPCC), reason="hipcc not available")
+def test_xcd_spread_is_a_bijection(tmp_path):
+    src = tmp_path / "spread.hip"
+    src.write_text(PROG)
+    exe = tmp_path / "spread"
+    inc = os.path.join(ROOT, "speculative_decoding_verify_amd", "csrc")
+    subprocess.run([HIPCC, "--offload-arch=gfx950", "-O1", "-std=c++17", "-I", inc, "-I",
+                    os.path.join(ROOT, "include"), str(src), "-o", str(exe)], check=True, capture_output=True)
+    r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert r.stdout.strip().endswith(" 0 bad"), r.stdout
