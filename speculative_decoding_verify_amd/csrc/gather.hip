@@ -12,8 +12,10 @@
 // loads in flight per CU).  Each wave loads its 16-row block of the fp32
 // state straight into MFMA A-operand registers (64 contiguous bytes per row
 // per load), writes the copy from the same registers, and multiplies by the
-// queries on MFMA with the state split into bf16 hi + lo terms.  The read of
-// the 64 KiB state dominates: the kernel is bound by HBM.
+// queries on MFMA with the state split into bf16 hi + lo terms.  The o tile
+// of the block goes through LDS, so that every store instruction writes whole
+// rows of o (measured 5% faster for bf16 outputs, 1.5% for fp32).  The read
+// of the 64 KiB state dominates: the kernel is bound by HBM.
 #include "ldv_device.hpp"
 #include "ldv_kernels.hpp"
 
@@ -34,6 +36,8 @@ template <int D, bool F32Q>
 __global__ __launch_bounds__((GShape<D>::NWA * kWave)) void gather_kernel(const GatherArgs p) {
     using S = GShape<D>;
     constexpr int NWA = S::NWA, MBW = S::MBW, KS = S::KS;
+    constexpr int RB = NWA * MBW * 16;  // state rows per block
+    __shared__ __align__(16) float s_o[16][RB + 4];  // padded: the 16 query rows start on different banks
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int c = lane & 15, g = lane >> 4;
     const int H = p.H;
@@ -152,13 +156,21 @@ __global__ __launch_bounds__((GShape<D>::NWA * kWave)) void gather_kernel(const 
                 if constexpr (F32Q) acc[mi] = mfma16x16x32(ah, bql, acc[mi]);
             }
         }
-        if (cval) {
+        // the block's o tile (16 queries x RB rows) goes through LDS, so that
+        // each store instruction covers whole rows of o: 16 consecutive lanes
+        // write one query's RB values
+        __syncthreads();  // the previous query block's tile has been stored
 #pragma unroll
-            for (int mi = 0; mi < MBW; ++mi) {
-                const int row0 = ((part * NWA + wave) * MBW + mi) * 16 + 4 * g;
-                st_stream_out4(p.o.base, p.o.bf16, o_base + (size_t)col * D + row0,
-                               make_float4(acc[mi][0], acc[mi][1], acc[mi][2], acc[mi][3]));
-            }
+        for (int mi = 0; mi < MBW; ++mi) {
+            const int r0 = (wave * MBW + mi) * 16 + 4 * g;
+            *reinterpret_cast<float4*>(&s_o[c][r0]) = make_float4(acc[mi][0], acc[mi][1], acc[mi][2], acc[mi][3]);
+        }
+        __syncthreads();
+        for (int j = tid; j < 16 * (RB / 4); j += NWA * kWave) {
+            const int qi = j / (RB / 4), r4 = (j % (RB / 4)) * 4;
+            if (nb * 16 + qi < p.Qn)
+                st_stream_out4(p.o.base, p.o.bf16, o_base + (size_t)(nb * 16 + qi) * D + part * RB + r4,
+                               *reinterpret_cast<const float4*>(&s_o[qi][r4]));
         }
     }
 }
