@@ -173,7 +173,7 @@ int read_common(int B, int T, int H, int dk, int dv, int P, int Qn, int qk_dtype
         return LDV_ERR_ARG;
     if ((long long)P * Qn > 0x7fffffffLL || !grid_fits((long long)B * H * (((long long)P * Qn + 63) / 64), 512))
         return LDV_ERR_UNSUPPORTED;
-    ldv::ReadArgs args{B, T, H, dk, P, Qn, k, u, logp, parent, S0, pos, queries, o, status};
+    ldv::ReadArgs args{B, T, H, dk, P, Qn, k, u, logp, parent, S0, pos, queries, o, status, 0};
     hipError_t e = ldv::launch_read(args, qk_dtype == LDV_F32, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? LDV_OK : LDV_ERR_LAUNCH;
 }

@@ -73,6 +73,7 @@ struct ReadArgs {
     const void* queries;
     ReadOut o;
     int* status;  // may be NULL
+    int stage_o;  // set by the launch: 1 = the O tile goes through LDS before the stores
 };
 
 struct SelectArgs {

@@ -104,3 +104,39 @@ def test_packed_bad_slot_leaves_rows(ldv):
     torch.cuda.synchronize()
     assert int(st.item()) == ldv.STATUS_BAD_SLOT
     assert torch.all(f[1, 0] == SENT) and not torch.any(f[0, 0, 8:] == SENT)
+
+
+def test_read_staged_large_grid(ldv, orc):
+    """A grid of more than 2048 blocks: the in-block read stages its output
+    tile in LDS before storing it (plain o and packed features, fp32 and
+    bf16); a bad position leaves its row untouched on that path too."""
+    B, H, D, T, P, Qn, col = 24, 48, 128, 16, 4, 16, 8   # 24 * 48 heads x 2 value tiles = 2304 blocks
+    c, pos, qs = read_case(6300, B, T, H, D, "chain", "bf16", P, Qn)
+    k, u, logp, S0, par = gpu_verify(ldv, c, "bf16", "chain")
+    q = dev(qs, torch.bfloat16)
+    shape, W = layout(B, P, H * Qn * D, col, 4, True)
+    f32 = torch.full(shape, SENT, device="cuda")
+    fb = torch.full(shape, SENT, device="cuda", dtype=torch.bfloat16)
+    st = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ldv.read_block_states_packed(k, u, logp, S0, dev(pos), q, f32, col=col, parent=par, status=st)
+    ldv.read_block_states_packed(k, u, logp, S0, dev(pos), q, fb, col=col, parent=par, status=st)
+    o = ldv.read_block_states(k, u, logp, S0, dev(pos), q, parent=par, status=st)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+    ref, s = orc.read_states(c["k"], c["v"], c["a"], c["beta"], c["S0"], pos, qs, None)
+    assert s == 0
+    check_packed("read staged D%d T%d" % (D, T), f32, fb, ref, B, P, H, Qn, D, col)
+    n = H * Qn * D
+    assert torch.equal(f32.reshape(B * P, W)[:, col:col + n].reshape(o.shape), o)
+    # one bad position: its row keeps the sentinel, every other row is as before
+    bad = pos.copy()
+    bad[5, 2] = T + 3
+    f2 = torch.full(shape, SENT, device="cuda")
+    st.zero_()
+    ldv.read_block_states_packed(k, u, logp, S0, dev(bad), q, f2, col=col, parent=par, status=st)
+    torch.cuda.synchronize()
+    assert int(st.item()) == ldv.STATUS_BAD_POSITION
+    assert torch.all(f2[5, 2] == SENT)
+    keep = torch.ones((B, P), dtype=torch.bool, device="cuda")
+    keep[5, 2] = False
+    assert torch.equal(f2[keep], f32[keep])
