@@ -142,7 +142,7 @@ struct VShape {
     static constexpr int WPE = MBW == 2 ? 3 : 4;
 };
 
-template <int D, int TM, bool F32IN>
+template <int D, int TM, bool F32IN, bool STG>
 struct VLds {
     using S = VShape<D, TM>;
     static constexpr int NPLANE = F32IN ? 4 : 2;  // q, k (hi and lo planes for fp32 input)
@@ -151,18 +151,25 @@ struct VLds {
     static constexpr size_t off_anc = off_t + (size_t)S::NSLOT * kWave * 16;  // uint64 [TM]
     static constexpr size_t off_f = off_anc + 8 * TM;  // float logp, P, beta [TM] each
     static constexpr size_t off_i = off_f + 12 * TM;   // int: bad flag
-    static constexpr size_t total = off_i + 16;
+    // staged outputs (16-node drafts on large grids): the O^T and U^T tiles of
+    // the block as fp32 [node][value] rows of SLD, over everything above once
+    // the substitution is done
+    static constexpr int SLD = S::BV + 4;
+    static constexpr size_t stage = STG ? (size_t)2 * 16 * SLD * 4 : 0;
+    static constexpr size_t total = (off_i + 16 > stage) ? off_i + 16 : stage;
     // waves per SIMD that the registers must allow: the shape's target, or
     // fewer where this block's LDS (160 KiB per CU) already caps residency
     static constexpr int lds_waves = (int)(163840 / total) * S::NW / 4;
     static constexpr int WPE = lds_waves < 1 ? 1 : (lds_waves < S::WPE ? lds_waves : S::WPE);
 };
 
-template <int D, int TM, bool F32IN>
+// STG: outputs staged in LDS and stored as whole rows (16-node drafts only).
+template <int D, int TM, bool F32IN, bool STG>
 __global__ __launch_bounds__((VShape<D, TM>::NW * kWave))
-__attribute__((amdgpu_waves_per_eu(VLds<D, TM, F32IN>::WPE))) void verify_kernel(const VerifyArgs p) {
+__attribute__((amdgpu_waves_per_eu(VLds<D, TM, F32IN, STG>::WPE))) void verify_kernel(const VerifyArgs p) {
     using S = VShape<D, TM>;
-    using L = VLds<D, TM, F32IN>;
+    using L = VLds<D, TM, F32IN, STG>;
+    static_assert(!STG || S::NBM == 1, "staged outputs: one node block");
     constexpr int BV = S::BV, NW = S::NW, KS = S::KS, QKLD = S::QKLD, NBM = S::NBM, MBW = S::MBW;
     constexpr int NTHR = NW * kWave;
     constexpr int EPC = F32IN ? 4 : 8;                 // elements per 16-byte chunk
@@ -586,6 +593,7 @@ __attribute__((amdgpu_waves_per_eu(VLds<D, TM, F32IN>::WPE))) void verify_kernel
     const buf_t bu = make_buf(p.u_out ? p.u_out + hrow0 * D + vrow0 : nullptr, p.u_out ? obytes : 0u);
     const uint32_t ooff = ((uint32_t)c * HD + 4 * g) * 4;
     bf16x8 upr[MBW][NBM];  // U_i as pairs
+    floatx4 ukeep[MBW], okeep[MBW];  // STG: the finished U^T and O^T tiles
 #pragma unroll
     for (int i = 0; i < NBM; ++i) {
         if (i < NB) {
@@ -606,7 +614,9 @@ __attribute__((amdgpu_waves_per_eu(VLds<D, TM, F32IN>::WPE))) void verify_kernel
             for (int mi = 0; mi < MBW; ++mi) {
                 const bf16x8 ypr = pair16(y[mi]);
                 upr[mi][i] = pair16(mm16d(z, xdh, xdl, ypr));  // U_i = X_ii Y
-                if (p.u_out) {
+                if constexpr (STG) {
+                    ukeep[mi] = mm16f(z, ypr, xdh, xdl);  // U_i^T = Y^T X_ii^T
+                } else if (p.u_out) {
                     const floatx4 ut = mm16f(z, ypr, xdh, xdl);  // U_i^T = Y^T X_ii^T
                     buf_st_stream(bu, oo + 64u * mi, make_float4(ut[0], ut[1], ut[2], ut[3]));
                 }
@@ -618,7 +628,8 @@ __attribute__((amdgpu_waves_per_eu(VLds<D, TM, F32IN>::WPE))) void verify_kernel
 #pragma unroll
                 for (int mi = 0; mi < MBW; ++mi) {
                     const floatx4 ov = mm16f(acco[mi][i], upr[mi][i], cdh, cdl);
-                    buf_st_stream(bo, oo + 64u * mi, make_float4(ov[0], ov[1], ov[2], ov[3]));
+                    if constexpr (STG) okeep[mi] = ov;
+                    else buf_st_stream(bo, oo + 64u * mi, make_float4(ov[0], ov[1], ov[2], ov[3]));
                 }
             }
 #pragma unroll
@@ -632,22 +643,55 @@ __attribute__((amdgpu_waves_per_eu(VLds<D, TM, F32IN>::WPE))) void verify_kernel
             }
         }
     }
+    if constexpr (STG) {
+        // the block's O^T and U^T tiles through LDS, so that each store
+        // instruction writes whole rows (BV values of a node); nodes past T
+        // fall outside the views and are dropped
+        constexpr int SLD = L::SLD;
+        float* s_so = reinterpret_cast<float*>(smem);  // [16][SLD] O rows, then [16][SLD] U rows
+        __syncthreads();  // every wave is done with the factor tiles
+#pragma unroll
+        for (int mi = 0; mi < MBW; ++mi) {
+            const int v = (wave * MBW + mi) * 16 + 4 * g;
+            *reinterpret_cast<float4*>(s_so + c * SLD + v) = make_float4(okeep[mi][0], okeep[mi][1], okeep[mi][2], okeep[mi][3]);
+            *reinterpret_cast<float4*>(s_so + (16 + c) * SLD + v) =
+                make_float4(ukeep[mi][0], ukeep[mi][1], ukeep[mi][2], ukeep[mi][3]);
+        }
+        __syncthreads();
+        const uint32_t tbytes = (span + BV) * 4;
+        const buf_t to = make_buf(p.o + hrow0 * D + tile * BV, tbytes);
+        const buf_t tu = make_buf(p.u_out ? p.u_out + hrow0 * D + tile * BV : nullptr, p.u_out ? tbytes : 0u);
+        for (int k = tid; k < 16 * (BV / 4); k += NTHR) {
+            const int n = k / (BV / 4), v4 = 4 * (k % (BV / 4));
+            const uint32_t off = ((uint32_t)n * HD + v4) * 4;
+            buf_st_stream(to, off, *reinterpret_cast<const float4*>(s_so + n * SLD + v4));
+            buf_st_stream(tu, off, *reinterpret_cast<const float4*>(s_so + (16 + n) * SLD + v4));
+        }
+    }
 }
 
-template <int D, int TM, bool F32IN>
+// 16-node drafts on grids of at least this many blocks stage their outputs
+// in LDS and store whole rows; smaller grids (one round of blocks) are
+// latency-bound and store straight from the accumulators.
+constexpr long long kVerifyStageBlocks = 2048;
+
+template <int D, int TM, bool F32IN, bool STG>
 static hipError_t launch_t(const VerifyArgs& a, hipStream_t st) {
     using S = VShape<D, TM>;
     const long long nblk = (long long)a.B * a.H * S::NT;
     if (nblk <= 0) return hipSuccess;
-    hipLaunchKernelGGL((verify_kernel<D, TM, F32IN>), dim3((unsigned)nblk), dim3(S::NW * kWave), 0, st, a);
+    hipLaunchKernelGGL((verify_kernel<D, TM, F32IN, STG>), dim3((unsigned)nblk), dim3(S::NW * kWave), 0, st, a);
     return hipGetLastError();
 }
 
 template <int D, bool F32IN>
 static hipError_t launch_d(const VerifyArgs& a, hipStream_t st) {
-    if (a.T <= 16) return launch_t<D, 16, F32IN>(a, st);
-    if (a.T <= 32) return launch_t<D, 32, F32IN>(a, st);
-    return launch_t<D, 64, F32IN>(a, st);
+    if (a.T <= 16) {
+        if ((long long)a.B * a.H * VShape<D, 16>::NT >= kVerifyStageBlocks) return launch_t<D, 16, F32IN, true>(a, st);
+        return launch_t<D, 16, F32IN, false>(a, st);
+    }
+    if (a.T <= 32) return launch_t<D, 32, F32IN, false>(a, st);
+    return launch_t<D, 64, F32IN, false>(a, st);
 }
 
 template <bool F32IN>

@@ -166,3 +166,26 @@ def test_unsupported_sizes_raise(ldv):
     S0 = torch.zeros((1, 1, 96, 96), device="cuda")
     with pytest.raises(ldv.LdvError):
         ldv.verify_chain(q, q, q, a, a, S0)
+
+
+@pytest.mark.parametrize("T,topology,qkv", [(5, "chain", "bf16"), (13, "tree", "bf16"), (16, "tree", "f32"),
+                                            (1, "chain", "bf16")], ids=lambda v: str(v))
+def test_verify_staged_outputs(ldv, orc, T, topology, qkv):
+    """Drafts of up to 16 nodes on 2048 or more heads store o and u through
+    LDS as whole rows: ragged node counts drop the rows past T, and a call
+    without factors writes o alone."""
+    wl = WORKLOADS["tree64"].replace(B=32, H=64, D=128, T=T, topology=topology, qkv=qkv,
+                                     accept="uniform-node", seed=4400 + T)
+    x = make_inputs(wl, with_gather=False)
+    chain = topology == "chain"
+    compare_verify(ldv, orc, x, qkv, chain, "staged T%d %s %s" % (T, topology, qkv))
+    d = to_device(x, qkv)
+    if chain:
+        o, u, lp = ldv.verify_chain(d["q"], d["k"], d["v"], d["a"], d["beta"], d["S0"], factors=False)
+    else:
+        o, u, lp = ldv.verify_tree(d["q"], d["k"], d["v"], d["a"], d["beta"], d["S0"], d["parent"], factors=False)
+    torch.cuda.synchronize()
+    assert u is None and lp is None
+    ro, _, s = orc.verify(x["q"], x["k"], x["v"], x["a"], x["beta"], x["S0"], None if chain else x["parent"])
+    assert s == 0
+    check("staged T%d no factors o" % T, o, ro)
