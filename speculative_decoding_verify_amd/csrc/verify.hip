@@ -151,25 +151,26 @@ struct VLds {
     static constexpr size_t off_anc = off_t + (size_t)S::NSLOT * kWave * 16;  // uint64 [TM]
     static constexpr size_t off_f = off_anc + 8 * TM;  // float logp, P, beta [TM] each
     static constexpr size_t off_i = off_f + 12 * TM;   // int: bad flag
-    // staged outputs (16-node drafts on large grids): the O^T and U^T tiles of
-    // the block as fp32 [node][value] rows of SLD, over everything above once
-    // the substitution is done
+    // staged outputs (large grids): the O^T and U^T tiles of one node block
+    // as fp32 [node][value] rows of SLD.  With one node block they go over
+    // everything above once the substitution is done; with more, into an
+    // area of their own (the factor tiles are still in use).
     static constexpr int SLD = S::BV + 4;
     static constexpr size_t stage = STG ? (size_t)2 * 16 * SLD * 4 : 0;
-    static constexpr size_t total = (off_i + 16 > stage) ? off_i + 16 : stage;
+    static constexpr size_t off_stg = S::NBM > 1 ? (off_i + 16 + 15) / 16 * 16 : 0;
+    static constexpr size_t total = S::NBM > 1 ? off_stg + stage : ((off_i + 16 > stage) ? off_i + 16 : stage);
     // waves per SIMD that the registers must allow: the shape's target, or
     // fewer where this block's LDS (160 KiB per CU) already caps residency
     static constexpr int lds_waves = (int)(163840 / total) * S::NW / 4;
     static constexpr int WPE = lds_waves < 1 ? 1 : (lds_waves < S::WPE ? lds_waves : S::WPE);
 };
 
-// STG: outputs staged in LDS and stored as whole rows (16-node drafts only).
+// STG: outputs staged in LDS and stored as whole rows.
 template <int D, int TM, bool F32IN, bool STG>
 __global__ __launch_bounds__((VShape<D, TM>::NW * kWave))
 __attribute__((amdgpu_waves_per_eu(VLds<D, TM, F32IN, STG>::WPE))) void verify_kernel(const VerifyArgs p) {
     using S = VShape<D, TM>;
     using L = VLds<D, TM, F32IN, STG>;
-    static_assert(!STG || S::NBM == 1, "staged outputs: one node block");
     constexpr int BV = S::BV, NW = S::NW, KS = S::KS, QKLD = S::QKLD, NBM = S::NBM, MBW = S::MBW;
     constexpr int NTHR = NW * kWave;
     constexpr int EPC = F32IN ? 4 : 8;                 // elements per 16-byte chunk
@@ -197,7 +198,11 @@ __attribute__((amdgpu_waves_per_eu(VLds<D, TM, F32IN, STG>::WPE))) void verify_k
     const int bh = (int)(bid / S::NT);
     const int h = bh % H, b = bh / H;
     const size_t nb0 = (size_t)b * p.Ts + p.t0;  // node 0 of this sequence's (chunk of the) draft
-    const int NB = (T + 15) >> 4;  // 16-node blocks in use
+    // 16-node blocks in use.  The launch picks TM as the smallest of 16, 32
+    // and 64 that holds T, so at 16 and 32 every node block is in use; saying
+    // so at compile time also keeps the node-block branches out of those
+    // kernels.
+    const int NB = TM <= 32 ? NBM : (T + 15) >> 4;
     const int T16 = NB * 16;
     // first value row (of S0, o, u) of this wave; the wave index is read
     // into a scalar register so that every view base below is scalar
@@ -594,6 +599,30 @@ __attribute__((amdgpu_waves_per_eu(VLds<D, TM, F32IN, STG>::WPE))) void verify_k
     const uint32_t ooff = ((uint32_t)c * HD + 4 * g) * 4;
     bf16x8 upr[MBW][NBM];  // U_i as pairs
     floatx4 ukeep[MBW], okeep[MBW];  // STG: the finished U^T and O^T tiles
+    // STG with several node blocks: node block i's tiles through the staging
+    // area, then whole rows of its 16 nodes to o and u
+    auto stage_store = [&](int i) {
+        constexpr int SLD = L::SLD;
+        float* s_so = reinterpret_cast<float*>(smem + L::off_stg);  // [16][SLD] O rows, then [16][SLD] U rows
+        __syncthreads();  // the previous node block's rows have been read
+#pragma unroll
+        for (int mi = 0; mi < MBW; ++mi) {
+            const int v = (wave * MBW + mi) * 16 + 4 * g;
+            *reinterpret_cast<float4*>(s_so + c * SLD + v) = make_float4(okeep[mi][0], okeep[mi][1], okeep[mi][2], okeep[mi][3]);
+            *reinterpret_cast<float4*>(s_so + (16 + c) * SLD + v) =
+                make_float4(ukeep[mi][0], ukeep[mi][1], ukeep[mi][2], ukeep[mi][3]);
+        }
+        __syncthreads();
+        const uint32_t tbytes = (span + BV) * 4;
+        const buf_t to = make_buf(p.o + hrow0 * D + tile * BV, tbytes);
+        const buf_t tu = make_buf(p.u_out ? p.u_out + hrow0 * D + tile * BV : nullptr, p.u_out ? tbytes : 0u);
+        for (int k = tid; k < 16 * (BV / 4); k += NTHR) {
+            const int n = k / (BV / 4), v4 = 4 * (k % (BV / 4));
+            const uint32_t off = ((uint32_t)(16 * i + n) * HD + v4) * 4;
+            buf_st_stream(to, off, *reinterpret_cast<const float4*>(s_so + n * SLD + v4));
+            buf_st_stream(tu, off, *reinterpret_cast<const float4*>(s_so + (16 + n) * SLD + v4));
+        }
+    };
 #pragma unroll
     for (int i = 0; i < NBM; ++i) {
         if (i < NB) {
@@ -641,9 +670,10 @@ __attribute__((amdgpu_waves_per_eu(VLds<D, TM, F32IN, STG>::WPE))) void verify_k
                     for (int mi = 0; mi < MBW; ++mi) acco[mi][j] = mm16f(acco[mi][j], upr[mi][i], cdh, cdl);
                 }
             }
+            if constexpr (STG && NBM > 1) stage_store(i);
         }
     }
-    if constexpr (STG) {
+    if constexpr (STG && NBM == 1) {
         // the block's O^T and U^T tiles through LDS, so that each store
         // instruction writes whole rows (BV values of a node); nodes past T
         // fall outside the views and are dropped
@@ -670,8 +700,8 @@ __attribute__((amdgpu_waves_per_eu(VLds<D, TM, F32IN, STG>::WPE))) void verify_k
     }
 }
 
-// 16-node drafts on grids of at least this many blocks stage their outputs
-// in LDS and store whole rows; smaller grids (one round of blocks) are
+// Drafts of up to 32 nodes on grids of at least this many blocks stage their
+// outputs in LDS and store whole rows; smaller grids (one round of blocks) are
 // latency-bound and store straight from the accumulators.
 constexpr long long kVerifyStageBlocks = 2048;
 
@@ -690,7 +720,12 @@ static hipError_t launch_d(const VerifyArgs& a, hipStream_t st) {
         if ((long long)a.B * a.H * VShape<D, 16>::NT >= kVerifyStageBlocks) return launch_t<D, 16, F32IN, true>(a, st);
         return launch_t<D, 16, F32IN, false>(a, st);
     }
-    if (a.T <= 32) return launch_t<D, 32, F32IN, false>(a, st);
+    if (a.T <= 32) {
+        // fp32 inputs stay unstaged: the staging area would cost them a block per CU
+        if (!F32IN && (long long)a.B * a.H * VShape<D, 32>::NT >= kVerifyStageBlocks)
+            return launch_t<D, 32, F32IN, true>(a, st);
+        return launch_t<D, 32, F32IN, false>(a, st);
+    }
     return launch_t<D, 64, F32IN, false>(a, st);
 }
 
