@@ -153,12 +153,16 @@ struct VLds {
     static constexpr size_t off_i = off_f + 12 * TM;   // int: bad flag
     // staged outputs (large grids): the O^T and U^T tiles of one node block
     // as fp32 [node][value] rows of SLD.  With one node block they go over
-    // everything above once the substitution is done; with more, into an
-    // area of their own (the factor tiles are still in use).
+    // everything above once the substitution is done.  With more, the
+    // factor tiles are still in use, and they go over the Q and K rows (dead
+    // once the state products are done) where those are large enough, else
+    // into an area of their own.
     static constexpr int SLD = S::BV + 4;
     static constexpr size_t stage = STG ? (size_t)2 * 16 * SLD * 4 : 0;
-    static constexpr size_t off_stg = S::NBM > 1 ? (off_i + 16 + 15) / 16 * 16 : 0;
-    static constexpr size_t total = S::NBM > 1 ? off_stg + stage : ((off_i + 16 > stage) ? off_i + 16 : stage);
+    static constexpr bool own = S::NBM > 1 && qk < stage;
+    static constexpr size_t off_stg = own ? (off_i + 16 + 15) / 16 * 16 : 0;
+    static constexpr size_t total =
+        own ? off_stg + stage : (S::NBM > 1 || off_i + 16 > stage ? off_i + 16 : stage);
     // waves per SIMD that the registers must allow: the shape's target, or
     // fewer where this block's LDS (160 KiB per CU) already caps residency
     static constexpr int lds_waves = (int)(163840 / total) * S::NW / 4;
@@ -199,10 +203,11 @@ __attribute__((amdgpu_waves_per_eu(VLds<D, TM, F32IN, STG>::WPE))) void verify_k
     const int h = bh % H, b = bh / H;
     const size_t nb0 = (size_t)b * p.Ts + p.t0;  // node 0 of this sequence's (chunk of the) draft
     // 16-node blocks in use.  The launch picks TM as the smallest of 16, 32
-    // and 64 that holds T, so at 16 and 32 every node block is in use; saying
-    // so at compile time also keeps the node-block branches out of those
-    // kernels.
-    const int NB = TM <= 32 ? NBM : (T + 15) >> 4;
+    // and 64 that holds T, so at 16 and 32 every node block is in use and at
+    // 64 all but possibly the last.  Saying so at compile time keeps those
+    // node-block branches out of the kernels (at 64 nodes only where the
+    // outputs are staged: it measured 2% slower on the one-round tree grid).
+    const int NB = TM <= 32 ? NBM : (STG ? max(NBM - 1, (T + 15) >> 4) : (T + 15) >> 4);
     const int T16 = NB * 16;
     // first value row (of S0, o, u) of this wave; the wave index is read
     // into a scalar register so that every view base below is scalar
@@ -700,9 +705,9 @@ __attribute__((amdgpu_waves_per_eu(VLds<D, TM, F32IN, STG>::WPE))) void verify_k
     }
 }
 
-// Drafts of up to 32 nodes on grids of at least this many blocks stage their
-// outputs in LDS and store whole rows; smaller grids (one round of blocks) are
-// latency-bound and store straight from the accumulators.
+// Grids of at least this many blocks stage their outputs in LDS and store
+// whole rows; smaller grids (one round of blocks) are latency-bound and store
+// straight from the accumulators.
 constexpr long long kVerifyStageBlocks = 2048;
 
 template <int D, int TM, bool F32IN, bool STG>
@@ -721,10 +726,14 @@ static hipError_t launch_d(const VerifyArgs& a, hipStream_t st) {
         return launch_t<D, 16, F32IN, false>(a, st);
     }
     if (a.T <= 32) {
-        // fp32 inputs stay unstaged: the staging area would cost them a block per CU
-        if (!F32IN && (long long)a.B * a.H * VShape<D, 32>::NT >= kVerifyStageBlocks)
-            return launch_t<D, 32, F32IN, true>(a, st);
+        if ((long long)a.B * a.H * VShape<D, 32>::NT >= kVerifyStageBlocks) return launch_t<D, 32, F32IN, true>(a, st);
         return launch_t<D, 32, F32IN, false>(a, st);
+    }
+    // 64-node staging at d = 128 only: at d = 64 the compiler's code for it
+    // leaves an MFMA result one wait state short of the others before its
+    // LDS write on one path, so that shape keeps the direct stores
+    if constexpr (D == 128) {
+        if ((long long)a.B * a.H * VShape<D, 64>::NT >= kVerifyStageBlocks) return launch_t<D, 64, F32IN, true>(a, st);
     }
     return launch_t<D, 64, F32IN, false>(a, st);
 }

@@ -42,6 +42,7 @@ GRID = [  # B, T, H, D, qkv
     (2, 200, 2, 32, "bf16"),
     (1, 150, 2, 16, "f32"),
     (2, 80, 2, 128, "f32"),
+    (32, 100, 64, 128, "bf16"),   # 2048 heads: both chunks store through LDS
 ]
 
 

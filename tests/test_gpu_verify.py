@@ -169,11 +169,12 @@ def test_unsupported_sizes_raise(ldv):
 
 
 @pytest.mark.parametrize("T,topology,qkv", [(5, "chain", "bf16"), (13, "tree", "bf16"), (16, "tree", "f32"),
-                                            (1, "chain", "bf16")], ids=lambda v: str(v))
+                                            (1, "chain", "bf16"), (21, "chain", "bf16"), (29, "tree", "f32"),
+                                            (40, "tree", "bf16"), (36, "tree", "f32")], ids=lambda v: str(v))
 def test_verify_staged_outputs(ldv, orc, T, topology, qkv):
-    """Drafts of up to 16 nodes on 2048 or more heads store o and u through
-    LDS as whole rows: ragged node counts drop the rows past T, and a call
-    without factors writes o alone."""
+    """On 2048 or more heads the outputs go through LDS and are stored as
+    whole rows (16-, 32- and 64-node blocks): ragged node counts drop the
+    rows past T, and a call without factors writes o alone."""
     wl = WORKLOADS["tree64"].replace(B=32, H=64, D=128, T=T, topology=topology, qkv=qkv,
                                      accept="uniform-node", seed=4400 + T)
     x = make_inputs(wl, with_gather=False)
