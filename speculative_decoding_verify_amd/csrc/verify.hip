@@ -706,9 +706,11 @@ __attribute__((amdgpu_waves_per_eu(VLds<D, TM, F32IN, STG>::WPE))) void verify_k
 }
 
 // Grids of at least this many blocks stage their outputs in LDS and store
-// whole rows; smaller grids (one round of blocks) are latency-bound and store
-// straight from the accumulators.
-constexpr long long kVerifyStageBlocks = 2048;
+// whole rows.  Measured: 27B-hybrid 38.3 -> 36.5 us (2048 blocks), tree-64
+// 23.5 -> 21.3 us (512), batch-256 191 -> 175 us (8192); the GDN-1.3B grid
+// (256 blocks) is the same either way and stores straight from the
+// accumulators.
+constexpr long long kVerifyStageBlocks = 512;
 
 template <int D, int TM, bool F32IN, bool STG>
 static hipError_t launch_t(const VerifyArgs& a, hipStream_t st) {
