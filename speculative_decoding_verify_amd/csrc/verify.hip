@@ -604,12 +604,16 @@ __attribute__((amdgpu_waves_per_eu(VLds<D, TM, F32IN, STG>::WPE))) void verify_k
     const uint32_t ooff = ((uint32_t)c * HD + 4 * g) * 4;
     bf16x8 upr[MBW][NBM];  // U_i as pairs
     floatx4 ukeep[MBW], okeep[MBW];  // STG: the finished U^T and O^T tiles
-    // STG with several node blocks: node block i's tiles through the staging
-    // area, then whole rows of its 16 nodes to o and u
+    // STG: node block i's finished tiles through the staging area, then whole
+    // rows of its 16 nodes (BV values each) to o and u, so that each store
+    // instruction writes whole rows; nodes past T fall outside the views and
+    // are dropped
     auto stage_store = [&](int i) {
         constexpr int SLD = L::SLD;
         float* s_so = reinterpret_cast<float*>(smem + L::off_stg);  // [16][SLD] O rows, then [16][SLD] U rows
-        __syncthreads();  // the previous node block's rows have been read
+        // what the staging area overlays is no longer read: the previous node
+        // block's rows (or, with one node block, every factor tile)
+        __syncthreads();
 #pragma unroll
         for (int mi = 0; mi < MBW; ++mi) {
             const int v = (wave * MBW + mi) * 16 + 4 * g;
@@ -675,32 +679,7 @@ __attribute__((amdgpu_waves_per_eu(VLds<D, TM, F32IN, STG>::WPE))) void verify_k
                     for (int mi = 0; mi < MBW; ++mi) acco[mi][j] = mm16f(acco[mi][j], upr[mi][i], cdh, cdl);
                 }
             }
-            if constexpr (STG && NBM > 1) stage_store(i);
-        }
-    }
-    if constexpr (STG && NBM == 1) {
-        // the block's O^T and U^T tiles through LDS, so that each store
-        // instruction writes whole rows (BV values of a node); nodes past T
-        // fall outside the views and are dropped
-        constexpr int SLD = L::SLD;
-        float* s_so = reinterpret_cast<float*>(smem);  // [16][SLD] O rows, then [16][SLD] U rows
-        __syncthreads();  // every wave is done with the factor tiles
-#pragma unroll
-        for (int mi = 0; mi < MBW; ++mi) {
-            const int v = (wave * MBW + mi) * 16 + 4 * g;
-            *reinterpret_cast<float4*>(s_so + c * SLD + v) = make_float4(okeep[mi][0], okeep[mi][1], okeep[mi][2], okeep[mi][3]);
-            *reinterpret_cast<float4*>(s_so + (16 + c) * SLD + v) =
-                make_float4(ukeep[mi][0], ukeep[mi][1], ukeep[mi][2], ukeep[mi][3]);
-        }
-        __syncthreads();
-        const uint32_t tbytes = (span + BV) * 4;
-        const buf_t to = make_buf(p.o + hrow0 * D + tile * BV, tbytes);
-        const buf_t tu = make_buf(p.u_out ? p.u_out + hrow0 * D + tile * BV : nullptr, p.u_out ? tbytes : 0u);
-        for (int k = tid; k < 16 * (BV / 4); k += NTHR) {
-            const int n = k / (BV / 4), v4 = 4 * (k % (BV / 4));
-            const uint32_t off = ((uint32_t)n * HD + v4) * 4;
-            buf_st_stream(to, off, *reinterpret_cast<const float4*>(s_so + n * SLD + v4));
-            buf_st_stream(tu, off, *reinterpret_cast<const float4*>(s_so + (16 + n) * SLD + v4));
+            if constexpr (STG) stage_store(i);
         }
     }
 }
