@@ -56,10 +56,10 @@ __global__ __launch_bounds__(256) void commit_kernel(const CommitArgs p) {
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int T = p.T, H = p.H;
-    // heads spread over the XCDs (a head's row blocks stay together): the
-    // heads that commit nothing cost nothing, so whole sequences per XCD
-    // would leave some XCDs with far more work than others
-    const unsigned bid = xcd_spread(blockIdx.x, gridDim.x / S::NRB, S::NRB);
+    // units of kSpreadHeads heads spread over the XCDs (a unit's row blocks
+    // stay together): the heads that commit nothing cost nothing, so whole
+    // sequences per XCD would leave some XCDs with far more work than others
+    const unsigned bid = xcd_spread(blockIdx.x, gridDim.x / (kSpreadHeads * S::NRB), kSpreadHeads * S::NRB);
     const int rb = (int)(bid % S::NRB);
     const int bh = (int)(bid / S::NRB);
     const int h = bh % H, b = bh / H;

@@ -174,12 +174,20 @@ __device__ __forceinline__ bf16x8 frag_row(const unsigned short* row, int s, int
 // over all eight XCDs.  Hardware block
 // 8 t + x runs on XCD x and becomes block (t % per) of unit
 // 8 (t / per) + x; the units past the last multiple of 8 keep their order.
+// Blocks past the last whole group of 8 units (any remainder of the grid
+// included) keep their order, so that the map is a bijection on the grid.
 __host__ __device__ __forceinline__ unsigned xcd_spread(unsigned bid, unsigned units, unsigned per) {
     const unsigned full = (units / kXcds) * kXcds * per;  // blocks of the first 8 * (units / 8) units
     if (bid >= full) return bid;
     const unsigned x = bid % kXcds, t = bid / kXcds;
     return ((t / per) * kXcds + x) * per + t % per;
 }
+
+// Heads per spread unit in the per-head kernels (verify, commit, in-block
+// read), which share one head-to-XCD map: units of two heads measured as
+// fast as single heads on the 27B-hybrid, tree-64 and GDN-1.3B shapes and 6%
+// faster for the batch-256 commit (longer contiguous runs of state per XCD).
+constexpr unsigned kSpreadHeads = 2;
 
 __device__ __forceinline__ int wave_max_i(int v) {
 #pragma unroll

@@ -110,9 +110,10 @@ __attribute__((amdgpu_waves_per_eu(RLds<D, TM, F32IN>::WPE))) void read_kernel(c
     const int T = p.T, H = p.H, P = p.P, Qn = p.Qn;
     const int NQT = P * Qn;  // queries per (sequence, head), flattened f = p Qn + i
     const int nch = (NQT + NQ - 1) / NQ;
-    // heads spread over the XCDs as in verify and commit (a head's blocks
-    // stay on one XCD)
-    const unsigned bid = xcd_spread(blockIdx.x, gridDim.x / (unsigned)(S::NT * nch), (unsigned)(S::NT * nch));
+    // units of kSpreadHeads heads spread over the XCDs as in verify and
+    // commit (a unit's blocks stay on one XCD)
+    const unsigned per = kSpreadHeads * (unsigned)(S::NT * nch);  // blocks of a unit of heads
+    const unsigned bid = xcd_spread(blockIdx.x, gridDim.x / per, per);
     const int ch = (int)(bid % (unsigned)nch);
     const unsigned r1 = bid / (unsigned)nch;
     const int tile = (int)(r1 % S::NT);

@@ -195,9 +195,10 @@ __attribute__((amdgpu_waves_per_eu(VLds<D, TM, F32IN, STG>::WPE))) void verify_k
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int c = lane & 15, g = lane >> 4;
     const int T = p.T, H = p.H;
-    // heads spread over the XCDs as in commit and the in-block read, so that a
-    // head's S0 is in the same L2 for the calls that follow
-    const unsigned bid = xcd_spread(blockIdx.x, gridDim.x / S::NT, S::NT);
+    // units of kSpreadHeads heads spread over the XCDs as in commit and the
+    // in-block read, so that a head's S0 is in the same L2 for the calls that
+    // follow
+    const unsigned bid = xcd_spread(blockIdx.x, gridDim.x / (kSpreadHeads * S::NT), kSpreadHeads * S::NT);
     const int tile = (int)(bid % S::NT);
     const int bh = (int)(bid / S::NT);
     const int h = bh % H, b = bh / H;

@@ -14,13 +14,16 @@ PROG = r"""
 #include <cstdio>
 #include <vector>
 #include "ldv_device.hpp"
-// Every hardware block maps to exactly one logical block, and below the tail
-// the blocks of one unit share the XCD (hardware block i runs on XCD i % 8).
+// Every hardware block maps to exactly one logical block, also when the
+// grid is not a whole number of units (the kernels pass units = grid / per),
+// and below the tail the blocks of one unit share the XCD (hardware block i
+// runs on XCD i % 8).
 int main() {
     long bad = 0, cases = 0;
-    for (unsigned units = 1; units <= 700; ++units)
-        for (unsigned per = 1; per <= 8; ++per) {
-            const unsigned n = units * per, full = (units / 8) * 8 * per;
+    for (unsigned units = 1; units <= 400; ++units)
+        for (unsigned per = 1; per <= 8; ++per)
+        for (unsigned rest = 0; rest < per; ++rest) {
+            const unsigned n = units * per + rest, full = (units / 8) * 8 * per;
             std::vector<int> seen(n, 0);
             std::vector<int> xcd(units, -1);
             for (unsigned b = 0; b < n; ++b) {
