@@ -26,7 +26,9 @@
 //      more than Q and K (four blocks per CU at 64 nodes) and step 4 splits
 //      nothing;
 //   4. O^T = (S0 Q^T) diag(P_j) + U^T W on MFMA (S0, U and W carried as
-//      bf16 hi + lo terms), float4 stores.
+//      bf16 hi + lo terms); on large grids the O tile goes through LDS so
+//      that every store writes whole rows of o, else float4 stores straight
+//      from the accumulators.
 #include <limits.h>
 
 #include "ldv_device.hpp"

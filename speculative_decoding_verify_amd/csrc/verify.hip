@@ -46,8 +46,11 @@
 //   5. per node block i: Y = R_i - sum_k G_ik U_k, then U_i = X_ii Y (kept
 //      for the later blocks) and U_i^T = Y^T X_ii^T (stored), and
 //      O_j^T += U_i^T C_ji^T for j >= i; O_i^T is then complete and stored,
-//      each lane writing four consecutive values of one node (float4).
-// Two workgroup barriers in all (after step 2 and after step 3).
+//      each lane writing four consecutive values of one node (float4), or,
+//      on large grids, node block i's U^T and O^T tiles go through LDS so
+//      that every store writes whole rows of one node.
+// Two workgroup barriers (after step 2 and after step 3), and two more per
+// node block when the outputs are staged.
 // P_n / P_m is exp(log P_n - log P_m), evaluated only for ancestor pairs
 // (exponent <= 0 for gates in [0, 1]); log a is clamped at -87 so that a
 // zero gate gives a finite log.
