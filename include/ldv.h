@@ -124,9 +124,9 @@ int ldv_verify_chain(int B, int T, int H, int dk, int dv, int qkv_dtype,
  * Verify a chain of any length up to LDV_MAX_LONG_T (a long draft block).
  * The chain is cut into chunks of LDV_MAX_T consecutive nodes; chunk c is
  * verified with the closed form from the state at the end of chunk c - 1,
- * which is formed in S_work by the commit of that chunk's last node (the
- * chunk form: the Bole page's Eq. (2) per chunk, Eq. (9) to pass the state
- * on).  Results are those of ldv_verify_chain on the whole chain: o, the node
+ * which the verify of chunk c - 1 also forms, in S_work, from its own
+ * factors (the chunk form: the Bole page's Eq. (2) per chunk, Eq. (9) at the
+ * chunk's last node to pass the state on).  One kernel per chunk.  Results are those of ldv_verify_chain on the whole chain: o, the node
  * corrections u_n = beta_n (v_n - a_n S_{n-1} k_n) and log P_n counted from
  * S0, so ldv_commit_state (no parent array) commits any node from S0.
  *

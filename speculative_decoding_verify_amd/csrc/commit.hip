@@ -10,9 +10,9 @@
 // trees, T for a chain).
 //
 // A chain (no parent array) may be longer than 64 nodes: its path is
-// n, n-1, ..., 0 and is generated instead of walked.  The same kernel forms
-// the state at the end of each 64-node chunk of a long chain (the chunk
-// view: the base state is the previous chunk's end, log P relative to it).
+// n, n-1, ..., 0 and is generated instead of walked.  (The state at the end
+// of each 64-node chunk of a long chain is formed by the verify kernel of
+// that chunk, from the factors it already holds.)
 //
 // The work is a streaming read of S0 and write of S_out (64 KiB each per head
 // at d = 128), so it is bound by HBM.  One block of 256 threads per

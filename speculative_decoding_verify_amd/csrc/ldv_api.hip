@@ -46,7 +46,7 @@ int check_verify(int B, int T, int H, int dk, int dv, int dt, const void* q, con
 int verify_common(int B, int T, int H, int d, int dt, const void* q, const void* k, const void* v, const float* a,
                   const float* beta, const float* S0, const int32_t* parent, float* o, float* u_out,
                   float* logp_out, int* status, void* stream) {
-    ldv::VerifyArgs args{B, T, H, d, T, 0, q, k, v, a, beta, S0, parent, o, u_out, logp_out, status};
+    ldv::VerifyArgs args{B, T, H, d, T, 0, q, k, v, a, beta, S0, parent, o, u_out, logp_out, status, nullptr};
     hipError_t e = ldv::launch_verify(args, dt == LDV_F32, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? LDV_OK : LDV_ERR_LAUNCH;
 }
@@ -98,13 +98,11 @@ LDV_EXPORT int ldv_verify_chain_long(int B, int T, int H, int dk, int dv, int qk
     for (int t0 = 0; t0 < T; t0 += LDV_MAX_T) {
         const int len = T - t0 < LDV_MAX_T ? T - t0 : LDV_MAX_T;
         const float* base = t0 == 0 ? S0 : S_work;
-        ldv::VerifyArgs va{B, len, H, dk, T, t0, q, k, v, a, beta, base, nullptr, o, u_out, logp_out, status};
+        // every chunk but the last also forms the state at its last node, the
+        // next chunk's base, in S_work (in place from the second chunk on)
+        float* next = t0 + len < T ? S_work : nullptr;
+        ldv::VerifyArgs va{B, len, H, dk, T, t0, q, k, v, a, beta, base, nullptr, o, u_out, logp_out, status, next};
         if (ldv::launch_verify(va, f32, st) != hipSuccess) return LDV_ERR_LAUNCH;
-        if (t0 + len < T) {  // the state at the chunk's last node is the next chunk's base
-            ldv::CommitArgs ca{B, len, H, dk, T, t0, len - 1, k, u_out, logp_out, nullptr, nullptr, base, S_work,
-                               status};
-            if (ldv::launch_commit(ca, f32, st) != hipSuccess) return LDV_ERR_LAUNCH;
-        }
     }
     return LDV_OK;
 }

@@ -26,6 +26,10 @@ struct VerifyArgs {
     float* u_out;     // may be NULL (together with logp_out)
     float* logp_out;  // may be NULL
     int* status;      // may be NULL
+    // may be NULL; else T = 64 and the kernel also forms the state at node
+    // T - 1 into S_next (may equal S0: each wave reads its rows of S0 before
+    // it writes the same rows of S_next)
+    float* S_next;
 };
 
 struct CommitArgs {

@@ -49,8 +49,14 @@
 //      each lane writing four consecutive values of one node (float4), or,
 //      on large grids, node block i's U^T and O^T tiles go through LDS so
 //      that every store writes whole rows of one node.
+//   6. (a full 64-node chunk of a long chain only) the state at node T - 1,
+//        S = P S0 + sum_{m on its path} (P / P_m) u_m k_m^T   (Eq. (9)),
+//      from the U blocks still in registers: K goes transposed into the
+//      factor-tile area, and each wave forms its 16 value rows of S on MFMA,
+//      so the next chunk's base costs one read and one write of the state
+//      instead of a commit kernel's second pass over S0, u and k.
 // Two workgroup barriers (after step 2 and after step 3), and two more per
-// node block when the outputs are staged.
+// node block when the outputs are staged (two more for step 6).
 // P_n / P_m is exp(log P_n - log P_m), evaluated only for ancestor pairs
 // (exponent <= 0 for gates in [0, 1]); log a is clamped at -87 so that a
 // zero gate gives a finite log.
@@ -172,8 +178,9 @@ struct VLds {
     static constexpr int WPE = lds_waves < 1 ? 1 : (lds_waves < S::WPE ? lds_waves : S::WPE);
 };
 
-// STG: outputs staged in LDS and stored as whole rows.
-template <int D, int TM, bool F32IN, bool STG>
+// STG: outputs staged in LDS and stored as whole rows.  CMT: step 6 (64
+// nodes, all in use).
+template <int D, int TM, bool F32IN, bool STG, bool CMT>
 __global__ __launch_bounds__((VShape<D, TM>::NW * kWave))
 __attribute__((amdgpu_waves_per_eu(VLds<D, TM, F32IN, STG>::WPE))) void verify_kernel(const VerifyArgs p) {
     using S = VShape<D, TM>;
@@ -211,7 +218,9 @@ __attribute__((amdgpu_waves_per_eu(VLds<D, TM, F32IN, STG>::WPE))) void verify_k
     // 64 all but possibly the last.  Saying so at compile time keeps those
     // node-block branches out of the kernels (at 64 nodes only where the
     // outputs are staged: it measured 2% slower on the one-round tree grid).
-    const int NB = TM <= 32 ? NBM : (STG ? max(NBM - 1, (T + 15) >> 4) : (T + 15) >> 4);
+    // A chunk of a long chain that forms its end state is always full.
+    static_assert(!CMT || (TM == 64 && MBW == 1), "step 6 is written for full 64-node chunks");
+    const int NB = (TM <= 32 || CMT) ? NBM : (STG ? max(NBM - 1, (T + 15) >> 4) : (T + 15) >> 4);
     const int T16 = NB * 16;
     // first value row (of S0, o, u) of this wave; the wave index is read
     // into a scalar register so that every view base below is scalar
@@ -686,6 +695,61 @@ __attribute__((amdgpu_waves_per_eu(VLds<D, TM, F32IN, STG>::WPE))) void verify_k
             if constexpr (STG) stage_store(i);
         }
     }
+
+    // 6. the state at node T - 1 into S_next.  Per key tile kt the wave forms
+    //    M = (K^T)_kt U_w for its 16 value rows: A = the k column 16 kt + c at
+    //    four nodes, doubled like a factor tile (the nodes of U's k-slots), B
+    //    = U_i weighted by w_m = P / P_m as a pair; M[key 16 kt + 4 g + r]
+    //    [value c] is then S - P S0 at four consecutive keys of one value row.
+    if constexpr (CMT) {
+        if (p.S_next) {
+            constexpr int KTLD = TM + 8;        // bf16 row stride of K^T (rows are keys)
+            constexpr int NPK = F32IN ? 2 : 1;  // K planes (hi, lo)
+            static_assert((size_t)NPK * D * KTLD * 2 <= (size_t)S::NSLOT * kWave * 16, "K^T fits the factor tiles' area");
+            unsigned short* s_kt = reinterpret_cast<unsigned short*>(smem + L::off_t);
+            __syncthreads();  // every factor tile has been read
+            for (int e = tid; e < NPK * D * (TM / 4); e += NTHR) {
+                const int pl = e / (D * (TM / 4)), r = e % (D * (TM / 4));
+                const int x = r % D, n4 = 4 * (r / D);
+                const unsigned short* kr = s_k + pl * LO + n4 * QKLD + x;
+                const u16x4 w4 = {kr[0], kr[QKLD], kr[2 * QKLD], kr[3 * QKLD]};
+                *reinterpret_cast<u16x4*>(s_kt + (pl * D + x) * KTLD + n4) = w4;
+            }
+            __syncthreads();
+            const int last = T - 1;
+            const uint64_t path = s_anc[last] | (1ull << last);
+            const float lpl = s_logp[last], Pl = s_P[last];
+            bf16x8 uw[NBM];
+#pragma unroll
+            for (int i = 0; i < NBM; ++i) {
+                const u16x8 ub = __builtin_bit_cast(u16x8, upr[0][i]);  // [hi | lo] of nodes 16 i + 4 g + r
+                float x[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int m = 16 * i + 4 * g + r;
+                    const float w = ((path >> m) & 1ull) ? expf(lpl - s_logp[m]) : 0.f;
+                    x[r] = w * (bf16_val(ub[r]) + bf16_val(ub[4 + r]));
+                }
+                uw[i] = pair16(floatx4{x[0], x[1], x[2], x[3]});
+            }
+            const size_t srow = (((size_t)b * H + h) * D + vrow0 + c) * D + 4 * g;
+#pragma unroll
+            for (int kt = 0; kt < D / 16; ++kt) {
+                const float4 s4 = ld_stream(p.S0 + srow + 16 * kt);
+                floatx4 acc = {Pl * s4.x, Pl * s4.y, Pl * s4.z, Pl * s4.w};
+#pragma unroll
+                for (int i = 0; i < NBM; ++i) {
+                    const u16x4 k4 = load_u16x4(s_kt + (16 * kt + c) * KTLD + 16 * i + 4 * g);
+                    acc = mfma16x16x32(join(k4, k4), uw[i], acc);
+                    if constexpr (F32IN) {
+                        const u16x4 kl4 = load_u16x4(s_kt + (D + 16 * kt + c) * KTLD + 16 * i + 4 * g);
+                        acc = mfma16x16x32(join(kl4, kl4), uw[i], acc);
+                    }
+                }
+                st_stream(p.S_next + srow + 16 * kt, make_float4(acc[0], acc[1], acc[2], acc[3]));
+            }
+        }
+    }
 }
 
 // Grids of at least this many blocks stage their outputs in LDS and store
@@ -695,17 +759,25 @@ __attribute__((amdgpu_waves_per_eu(VLds<D, TM, F32IN, STG>::WPE))) void verify_k
 // accumulators.
 constexpr long long kVerifyStageBlocks = 512;
 
-template <int D, int TM, bool F32IN, bool STG>
+template <int D, int TM, bool F32IN, bool STG, bool CMT = false>
 static hipError_t launch_t(const VerifyArgs& a, hipStream_t st) {
     using S = VShape<D, TM>;
     const long long nblk = (long long)a.B * a.H * S::NT;
     if (nblk <= 0) return hipSuccess;
-    hipLaunchKernelGGL((verify_kernel<D, TM, F32IN, STG>), dim3((unsigned)nblk), dim3(S::NW * kWave), 0, st, a);
+    hipLaunchKernelGGL((verify_kernel<D, TM, F32IN, STG, CMT>), dim3((unsigned)nblk), dim3(S::NW * kWave), 0, st, a);
     return hipGetLastError();
 }
 
 template <int D, bool F32IN>
 static hipError_t launch_d(const VerifyArgs& a, hipStream_t st) {
+    if (a.S_next) {  // a full chunk of a long chain that also forms its end state
+        if (a.T != 64) return hipErrorInvalidValue;
+        if constexpr (D == 128) {
+            if ((long long)a.B * a.H * VShape<D, 64>::NT >= kVerifyStageBlocks)
+                return launch_t<D, 64, F32IN, true, true>(a, st);
+        }
+        return launch_t<D, 64, F32IN, false, true>(a, st);
+    }
     if (a.T <= 16) {
         if ((long long)a.B * a.H * VShape<D, 16>::NT >= kVerifyStageBlocks) return launch_t<D, 16, F32IN, true>(a, st);
         return launch_t<D, 16, F32IN, false>(a, st);

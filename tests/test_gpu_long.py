@@ -43,6 +43,10 @@ GRID = [  # B, T, H, D, qkv
     (1, 150, 2, 16, "f32"),
     (2, 80, 2, 128, "f32"),
     (32, 100, 64, 128, "bf16"),   # 2048 heads: both chunks store through LDS
+    (16, 130, 32, 128, "f32"),    # 512 heads, fp32 inputs: staged stores, two in-place chunk ends
+    (2, 140, 2, 64, "bf16"),
+    (2, 90, 2, 32, "f32"),
+    (2, 70, 3, 16, "bf16"),
 ]
 
 
@@ -87,3 +91,24 @@ def test_long_chain_gdn_shape(ldv, orc):
     torch.cuda.synchronize()
     ref = orc.chain_decode(x["q"], x["k"], x["v"], x["a"], x["beta"], x["S0"])
     check("long chain GDN shape T256", o, ref)
+
+
+@pytest.mark.parametrize("B,H,D,qkv", [(2, 3, 128, "bf16"), (16, 32, 128, "bf16"), (2, 2, 64, "f32"),
+                                       (1, 2, 16, "bf16")], ids=lambda v: str(v))
+def test_chunk_end_state(ldv, orc, B, H, D, qkv):
+    """Each full chunk but the last also forms the state at its last node, the
+    next chunk's base; with two chunks that state (node 63) is what the call
+    leaves in S_work.  Checked against the oracle's commit of node 63."""
+    c = case(8200 + B + D, B, 100, H, D, qkv)
+    dt = qkv_torch_dtype(qkv)
+    t = {key: dev(c[key], dt) for key in ("q", "k", "v")}
+    S0 = dev(c["S0"])
+    work = torch.full_like(S0, 7.0)
+    st = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ldv.verify_chain_long(t["q"], t["k"], t["v"], dev(c["a"]), dev(c["beta"]), S0, S_work=work, status=st)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+    want, s = orc.commit(c["k"], c["v"], c["a"], c["beta"], c["S0"], np.full(B, 63, dtype=np.int32))
+    assert s == 0
+    check("chunk end state B%d H%d D%d %s" % (B, H, D, qkv), work, want)
+    assert np.array_equal(host(S0), c["S0"])  # the committed state is only read
