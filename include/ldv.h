@@ -126,9 +126,10 @@ int ldv_verify_chain(int B, int T, int H, int dk, int dv, int qkv_dtype,
  * verified with the closed form from the state at the end of chunk c - 1,
  * which the verify of chunk c - 1 also forms, in S_work, from its own
  * factors (the chunk form: the Bole page's Eq. (2) per chunk, Eq. (9) at the
- * chunk's last node to pass the state on).  One kernel per chunk.  Results are those of ldv_verify_chain on the whole chain: o, the node
- * corrections u_n = beta_n (v_n - a_n S_{n-1} k_n) and log P_n counted from
- * S0, so ldv_commit_state (no parent array) commits any node from S0.
+ * chunk's last node to pass the state on).  One kernel per chunk.  Results
+ * are those of ldv_verify_chain on the whole chain: o, the node corrections
+ * u_n = beta_n (v_n - a_n S_{n-1} k_n) and log P_n counted from S0, so
+ * ldv_commit_state (no parent array) commits any node from S0.
  *
  *   q, k, v, a, beta, S0, o: as for ldv_verify_chain; u_out and logp_out are
  *             required
