@@ -258,6 +258,30 @@ def pin_chain_equals_decode(orc, seed=17, B=2, T=9, H=3, d=8):
     assert np.array_equal(o_chain, o_dec)
 
 
+def pin_chunk_form(orc, seed=25, B=2, T=23, H=2, dk=6, dv=5, L=8, tol=1e-10):
+    """The chunk form of long chains: verifying a chain chunk by chunk with
+    Eq. (2) (numpy, library solve), each chunk from the state that Eq. (9)
+    forms at the previous chunk's last node, gives the outputs of sequential
+    decode, and the state after the last chunk is the oracle's commit of the
+    chain's last node."""
+    c = random_case(seed, B, T, H, dk, dv, "chain")
+    o_dec = orc.chain_decode(c["q"], c["k"], c["v"], c["a"], c["beta"], c["S0"])
+    S_last, status = orc.commit(c["k"], c["v"], c["a"], c["beta"], c["S0"], np.full(B, T - 1, np.int32))
+    assert status == 0
+    for b in range(B):
+        for h in range(H):
+            S = c["S0"][b, h].astype(np.float64)
+            for t0 in range(0, T, L):
+                n = min(L, T - t0)
+                sl = slice(t0, t0 + n)
+                kc = c["k"][b, sl, h].astype(np.float64)
+                O, U, P, _ = closed_form_head(c["q"][b, sl, h], kc, c["v"][b, sl, h], c["a"][b, sl, h],
+                                              c["beta"][b, sl, h], S, np.arange(-1, n - 1))
+                assert rel_err(O, o_dec[b, sl, h]) <= tol, ("chunk o", b, h, t0)
+                S = P[n - 1] * S + sum((P[n - 1] / P[m]) * np.outer(U[m], kc[m]) for m in range(n))
+            assert rel_err(S, S_last[b, h]) <= tol, ("chunk end state", b, h)
+
+
 def pin_tree_equals_dfs(orc, seed=18, B=3, T=40, H=2, d=8):
     """Path walk per node equals branch-by-branch DFS traversal, bit for bit."""
     c = random_case(seed, B, T, H, d, d, "tree")
@@ -431,6 +455,6 @@ def pin_select_chain(orc, seed=24, B=16, T=10, V=50):
 
 
 ALL_PINS = [pin_golden, pin_closed_form, pin_commit_from_factors, pin_brute_force, pin_pure_decay,
-            pin_pure_read, pin_overwrite, pin_chain_equals_decode, pin_tree_equals_dfs, pin_gather,
+            pin_pure_read, pin_overwrite, pin_chain_equals_decode, pin_chunk_form, pin_tree_equals_dfs, pin_gather,
             pin_read_golden, pin_read_from_factors, pin_read_brute_force, pin_select_golden,
             pin_select_sets, pin_select_chain]
