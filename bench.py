@@ -213,6 +213,9 @@ class Runner:
                 del sel
                 self.sel_out = [torch.empty((wl.B, wl.T + 1), dtype=torch.int32, device="cuda")] + \
                                [torch.empty((wl.B,), dtype=torch.int32, device="cuda") for _ in range(3)]
+                # the selection's workspace (rows split over workgroups when they are few)
+                nws = self.ldv.select_workspace_bytes(wl.B, wl.T, wl.V)
+                self.sel_ws = torch.empty(nws, dtype=torch.uint8, device="cuda") if nws > 0 else None
 
     def verify(self, i):
         s = self.sets[i % len(self.sets)]
@@ -244,7 +247,7 @@ class Runner:
         t, a, l, b = self.sel_out
         self.ldv.select_accepted(self.logits[i % len(self.logits)], self.tokens,
                                  None if self.chain else s["parent"], target=t, accepted=a, accepted_len=l,
-                                 bonus=b, status=self.status)
+                                 bonus=b, status=self.status, workspace=self.sel_ws)
 
     def step_fns(self):
         return [self.verify, self.commit] + ([self.gather] if self.wl.P > 0 else [])

@@ -53,6 +53,7 @@
 #ifndef LDV_H
 #define LDV_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -270,6 +271,16 @@ int ldv_read_block_states_packed(int B, int T, int H, int dk, int dv, int P, int
  *   target        [B, T+1] int32 (written: every row's argmax)
  *   accepted      [B] int32 in [-1, T-1] (written), ready for ldv_commit_state
  *   accepted_len, bonus  [B] int32 or NULL
+ *   workspace     NULL, or device memory of at least
+ *                 ldv_select_workspace_bytes(B, T, V) bytes, 8-byte aligned,
+ *                 owned by the caller; its contents on entry and return do
+ *                 not matter.  With it, when there are few rows, each row is
+ *                 split over several workgroups (their partial results go
+ *                 through the workspace), which keeps every CU busy; the
+ *                 results are the same either way.  Calls that share a
+ *                 workspace must not overlap.
+ *   workspace_bytes  its size; a non-NULL workspace smaller than needed
+ *                 returns LDV_ERR_ARG
  * The logits need element alignment only.  A sequence with an invalid parent
  * row -> LDV_STATUS_BAD_PARENT; its target row is written, its accepted,
  * accepted_len and bonus are not.  V must be >= 1; T <= 64.
@@ -277,7 +288,14 @@ int ldv_read_block_states_packed(int B, int T, int H, int dk, int dv, int P, int
 int ldv_select_accepted(int B, int T, int V, int logits_dtype, const void* logits,
                         const int32_t* tokens, const int32_t* parent, int32_t* target,
                         int32_t* accepted, int32_t* accepted_len, int32_t* bonus,
-                        int* status, void* stream);
+                        int* status, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Bytes of workspace ldv_select_accepted uses for B sequences of T nodes and
+ * rows of V logits: 0 when it would not split the rows (then the workspace
+ * may be NULL at no cost), and 0 for sizes the call rejects.
+ */
+size_t ldv_select_workspace_bytes(int B, int T, int V);
 
 /* Text for an LDV_OK / LDV_ERR_* return code (static storage). */
 const char* ldv_status_string(int code);

@@ -7,6 +7,6 @@ fails if it has not been built.
 from .ldv import (LDV_BF16, LDV_F32, MAX_LONG_T, MAX_T, STATUS_BAD_ACCEPTED, STATUS_BAD_PARENT,  # noqa: F401
                   STATUS_BAD_POSITION, STATUS_BAD_SLOT, LdvError, commit_state, gather_states,
                   gather_states_packed, load, read_block_states, read_block_states_packed, select_accepted,
-                  status_string, verify_chain, verify_chain_long, verify_tree, version)
+                  select_workspace_bytes, status_string, verify_chain, verify_chain_long, verify_tree, version)
 
 load()

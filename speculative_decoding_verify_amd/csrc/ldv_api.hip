@@ -217,10 +217,17 @@ LDV_EXPORT int ldv_read_block_states_packed(int B, int T, int H, int dk, int dv,
     return read_common(B, T, H, dk, dv, P, Qn, qk_dtype, k, u, logp, parent, S0, pos, queries, out, status, stream);
 }
 
+LDV_EXPORT size_t ldv_select_workspace_bytes(int B, int T, int V) {
+    if (B <= 0 || T <= 0 || V <= 0 || T > LDV_MAX_T) return 0;
+    const long long rows = (long long)B * (T + 1);
+    const int np = ldv::select_parts(rows, V);
+    return np > 1 ? (size_t)rows * np * sizeof(ldv::ArgPart) : 0;
+}
+
 LDV_EXPORT int ldv_select_accepted(int B, int T, int V, int logits_dtype, const void* logits,
                                    const int32_t* tokens, const int32_t* parent, int32_t* target,
                                    int32_t* accepted, int32_t* accepted_len, int32_t* bonus, int* status,
-                                   void* stream) {
+                                   void* workspace, size_t workspace_bytes, void* stream) {
     if (B < 0 || T < 0 || V <= 0) return LDV_ERR_ARG;
     if (logits_dtype != LDV_BF16 && logits_dtype != LDV_F32) return LDV_ERR_ARG;
     if (T > LDV_MAX_T) return LDV_ERR_UNSUPPORTED;
@@ -231,7 +238,20 @@ LDV_EXPORT int ldv_select_accepted(int B, int T, int V, int logits_dtype, const 
         !aligned(status, 4))
         return LDV_ERR_ARG;
     if (!grid_fits((long long)B * (T + 1), 512)) return LDV_ERR_UNSUPPORTED;
-    ldv::SelectArgs args{B, T, V, logits, tokens, parent, target, accepted, accepted_len, bonus, status};
+    // with a workspace, rows may be split over several workgroups
+    const long long rows = (long long)B * (T + 1);
+    int np = 1;
+    if (workspace) {
+        if (!aligned(workspace, 8)) return LDV_ERR_ARG;
+        const int want = ldv::select_parts(rows, V);
+        if (want > 1) {
+            if (workspace_bytes < (size_t)rows * want * sizeof(ldv::ArgPart)) return LDV_ERR_ARG;
+            np = want;
+        }
+    }
+    if (!grid_fits(rows * np, 512)) return LDV_ERR_UNSUPPORTED;
+    ldv::SelectArgs args{B, T, V, logits, tokens, parent, target, accepted, accepted_len, bonus, status, np,
+                         static_cast<ldv::ArgPart*>(workspace)};
     hipError_t e = ldv::launch_select(args, logits_dtype == LDV_F32, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? LDV_OK : LDV_ERR_LAUNCH;
 }

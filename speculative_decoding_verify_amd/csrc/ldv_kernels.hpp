@@ -80,6 +80,14 @@ struct ReadArgs {
     int stage_o;  // set by the launch: 1 = the O tile goes through LDS before the stores
 };
 
+// The argmax of one part of a logits row: the largest value and its index
+// in the row (INT_MAX: no element of the part is a number above -inf, or the
+// part is empty).
+struct ArgPart {
+    float v;
+    int i;
+};
+
 struct SelectArgs {
     int B, T, V;
     const void* logits;      // [B, T+1, V]
@@ -90,7 +98,13 @@ struct SelectArgs {
     int32_t* accepted_len;   // may be NULL
     int32_t* bonus;          // may be NULL
     int* status;             // may be NULL
+    int np;                  // workgroups per logits row (1: the row's argmax goes straight to target)
+    ArgPart* part;           // np > 1: [B, T+1, np] partial results, combined by the walk
 };
+
+// Workgroups per logits row for B * (T + 1) = rows rows of V elements when
+// the caller provides the workspace for the partial results (1 otherwise).
+int select_parts(long long rows, int V);
 
 // Each launcher assumes arguments already validated by the C ABI layer and
 // returns the HIP launch status.

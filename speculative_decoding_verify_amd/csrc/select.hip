@@ -12,7 +12,10 @@
 // Two launches on the caller's stream:
 //   1. argmax_kernel: one workgroup per logits row (B x (T+1) rows of V
 //      values; 256 threads, or 512 when there are few rows), 16-byte loads
-//      with eight in flight per thread.  The rule,
+//      with eight in flight per thread; or, when the caller gives a
+//      workspace and the rows are few, np workgroups per row, each over one
+//      part of it (whole 16-byte chunks), writing its part's (maximum,
+//      index) to the workspace.  The rule,
 //      identical everywhere: the larger value wins, equal values go to the
 //      lower index, NaN never wins (+0 == -0), an all-NaN row gives 0.
 //      Each thread visits its 16-byte chunks in increasing index order and
@@ -28,7 +31,8 @@
 //      logits are read once.
 //   2. walk_kernel: one wave per sequence; lane n holds node n's parent and
 //      token and lane r the target of row r, so each step of the walk is a
-//      shuffle and a ballot (at most T steps).
+//      shuffle and a ballot (at most T steps).  With split rows, lane r first
+//      combines row r's parts under the same rule and writes target.
 #include <limits.h>
 
 #include "ldv_device.hpp"
@@ -46,6 +50,25 @@ constexpr int kArgThreadsWide = 512;
 constexpr int kArgThreadsNarrow = 256;
 constexpr int kArgFillRows = 1024;
 constexpr int kArgUnroll = 8;  // 16-byte loads in flight per thread
+
+// With one workgroup per row, a grid that is not a large multiple of the CU
+// count leaves CUs idle at its end (measured, rows of 151936 bf16 values:
+// 1024 rows 57.9 us, 1088 rows 66.1 us, 544 rows 37.4 us).  Given a
+// workspace, fewer rows than kArgSplitRows are split so that the grid holds
+// about kArgSplitBlocks workgroups, each part at least kArgMinPart values
+// (1088 rows: 61.9 us in four parts each; 544 rows: 34.9 us).  Shorter parts
+// measured slower: 144 rows of 32000 values take 6.5 us whole, 7.2 us in
+// three parts and 11.2 us in fifteen.
+constexpr long long kArgSplitRows = 2048;
+constexpr long long kArgSplitBlocks = 4096;
+constexpr int kArgMinPart = 32768;
+
+int select_parts(long long rows, int V) {
+    if (rows <= 0 || rows >= kArgSplitRows) return 1;
+    long long np = (kArgSplitBlocks + rows - 1) / rows;
+    if (np > V / kArgMinPart) np = V / kArgMinPart;
+    return np < 1 ? 1 : (int)np;
+}
 
 // (v, i) replaces (bv, bi) when v is larger, or equal with a lower index;
 // NaN compares false both ways and never replaces.
@@ -121,9 +144,15 @@ __global__ __launch_bounds__(NTHR) void argmax_kernel(const SelectArgs p) {
     __shared__ int s_i[NTHR / kWave];
 
     const int tid = threadIdx.x;
-    const int V = p.V;
-    const size_t row = blockIdx.x;
-    const unsigned char* base = static_cast<const unsigned char*>(p.logits) + row * (size_t)V * ES;
+    const int np = p.np;
+    const size_t row = blockIdx.x / np;
+    // this workgroup's part of the row, elements [lo, lo + V): parts of whole
+    // 16-byte chunks (each the same distance from a chunk boundary as the
+    // row), the last one shorter or empty
+    const int seg = ((p.V + np - 1) / np + EPC - 1) / EPC * EPC;
+    const int lo = min((int)(blockIdx.x % np) * seg, p.V);
+    const int V = min(lo + seg, p.V) - lo;
+    const unsigned char* base = static_cast<const unsigned char*>(p.logits) + (row * (size_t)p.V + lo) * ES;
     // elements up to the first 16-byte boundary of the row, 16-byte chunks,
     // then the elements past the last whole chunk
     const int mis = (int)((reinterpret_cast<uintptr_t>(base) & 15) / ES);
@@ -187,7 +216,27 @@ __global__ __launch_bounds__(NTHR) void argmax_kernel(const SelectArgs p) {
         for (int i = tid; i < V; i += NTHR) take_max(elem<F32>(base, i), i, bv, bi);
         block_take_max<NTHR>(bv, bi, s_v, s_i, tid);
     }
-    if (tid == 0) p.target[row] = bi == INT_MAX ? 0 : bi;  // a row of NaN: 0
+    if (tid == 0) {
+        if (np == 1) p.target[row] = bi == INT_MAX ? 0 : bi;  // a row of NaN: 0
+        else p.part[blockIdx.x] = ArgPart{bv, bi == INT_MAX ? INT_MAX : lo + bi};
+    }
+}
+
+// The argmax of a split row from its parts (same rule; no number: 0).  The
+// parts are loaded eight at a time (a repeated part, from the clamp, changes
+// nothing), so that the loads are in flight together.
+__device__ __forceinline__ int combine_row(const SelectArgs& p, size_t row) {
+    const ArgPart* pp = p.part + row * p.np;
+    float bv = -__builtin_inff();
+    int bi = INT_MAX;
+    for (int q0 = 0; q0 < p.np; q0 += 8) {
+        ArgPart e[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) e[j] = pp[min(q0 + j, p.np - 1)];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) take_max(e[j].v, e[j].i, bv, bi);
+    }
+    return bi == INT_MAX ? 0 : bi;
 }
 
 __global__ __launch_bounds__(256) void walk_kernel(const SelectArgs p) {
@@ -200,9 +249,21 @@ __global__ __launch_bounds__(256) void walk_kernel(const SelectArgs p) {
     const int nl = min(n, T - 1);
     const int par = p.parent ? p.parent[(size_t)b * T + nl] : n - 1;
     const int tok = p.tokens[(size_t)b * T + nl];
-    const int32_t* trow = p.target + (size_t)b * (T + 1);
-    const int tgt = trow[min(n, T)];  // target of row n (rows 0 .. 63)
-    const int tgt_last = trow[T];     // row T (the only row past 63 when T = 64)
+    const size_t rb = (size_t)b * (T + 1);
+    int tgt, tgt_last;  // target of row n (rows 0 .. 63), and of row T (the only row past 63 when T = 64)
+    if (p.np > 1) {  // split rows: combine the parts and write target (every row, as the argmax does)
+        tgt = combine_row(p, rb + min(n, T));
+        if (n <= T) p.target[rb + n] = tgt;
+        if (T == 64) {
+            tgt_last = combine_row(p, rb + 64);
+            if (lane == 0) p.target[rb + 64] = tgt_last;
+        } else {
+            tgt_last = __shfl(tgt, T, kWave);
+        }
+    } else {
+        tgt = p.target[rb + min(n, T)];
+        tgt_last = p.target[rb + T];
+    }
     if (__ballot(valid && (par < -1 || par >= n)) != 0ull) {
         if (lane == 0 && p.status) atomicOr(p.status, LDV_STATUS_BAD_PARENT);
         return;  // outputs of the sequence left unwritten
@@ -230,8 +291,8 @@ __global__ __launch_bounds__(256) void walk_kernel(const SelectArgs p) {
 hipError_t launch_select(const SelectArgs& a, bool f32_logits, hipStream_t stream) {
     const long long rows = (long long)a.B * (a.T + 1);
     if (rows <= 0) return hipSuccess;
-    const dim3 grid((unsigned)rows);
-    if (rows >= kArgFillRows) {
+    const dim3 grid((unsigned)(rows * a.np));
+    if (rows >= kArgFillRows || a.np > 1) {
         if (f32_logits)
             hipLaunchKernelGGL((argmax_kernel<true, kArgThreadsNarrow>), grid, dim3(kArgThreadsNarrow), 0, stream, a);
         else

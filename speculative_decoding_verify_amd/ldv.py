@@ -53,7 +53,9 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.ldv_gather_states_packed.argtypes = [i, i, i, i, i, i, i, i, fp, ip, vp, vp, ll, ll, i, ip, vp]
     lib.ldv_read_block_states_packed.argtypes = [i, i, i, i, i, i, i, i, vp, fp, fp, ip, fp, ip, vp, vp, ll, ll, i,
                                                  ip, vp]
-    lib.ldv_select_accepted.argtypes = [i, i, i, i, vp, ip, ip, ip, ip, ip, ip, ip, vp]
+    lib.ldv_select_accepted.argtypes = [i, i, i, i, vp, ip, ip, ip, ip, ip, ip, ip, vp, ctypes.c_size_t, vp]
+    lib.ldv_select_workspace_bytes.argtypes = [i, i, i]
+    lib.ldv_select_workspace_bytes.restype = ctypes.c_size_t
     for f in ("ldv_verify_tree", "ldv_verify_chain", "ldv_verify_chain_long", "ldv_commit_state", "ldv_gather_states",
               "ldv_read_block_states", "ldv_gather_states_packed", "ldv_read_block_states_packed",
               "ldv_select_accepted", "ldv_version"):
@@ -402,11 +404,14 @@ def read_block_states_packed(k, u, logp, S0, pos, queries, feat, col=0, parent=N
 
 
 def select_accepted(logits, tokens, parent=None, target=None, accepted=None, accepted_len=None,
-                    bonus=None, status=None, stream=None):
+                    bonus=None, status=None, workspace=None, split=True, stream=None):
     """Greedy accepted-node selection on the device.
 
     logits [B, T+1, V] bf16/fp32 (row 0: the committed position, row n+1:
     after node n); tokens [B, T] int32; parent [B, T] int32 or None (chain).
+    With split=True the library may split few, long rows over several
+    workgroups, through a workspace (uint8 device tensor of at least
+    select_workspace_bytes(B, T, V) bytes; allocated here when not given).
     Returns (target [B, T+1], accepted [B], accepted_len [B], bonus [B]),
     all int32."""
     _dev(logits, "logits")
@@ -425,12 +430,28 @@ def select_accepted(logits, tokens, parent=None, target=None, accepted=None, acc
     bonus = _opt(bonus, "bonus", torch.int32, (B,), dev)
     if status is not None:
         _dev(status, "status", torch.int32)
+    ws_bytes = 0
+    if split:
+        need = select_workspace_bytes(B, T, V)
+        if workspace is None and need > 0:
+            workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+        if workspace is not None:
+            _dev(workspace, "workspace", torch.uint8)
+            ws_bytes = workspace.numel()
+    else:
+        workspace = None
     _same_device(dev, tokens=tokens, parent=parent, target=target, accepted=accepted,
-                 accepted_len=accepted_len, bonus=bonus, status=status)
+                 accepted_len=accepted_len, bonus=bonus, status=status, workspace=workspace)
     _invoke("ldv_select_accepted", dev,
             B, T, V, code, _ptr(logits), _ptr(tokens), _ptr(parent), _ptr(target), _ptr(accepted),
-            _ptr(accepted_len), _ptr(bonus), _ptr(status), _stream(stream, dev))
+            _ptr(accepted_len), _ptr(bonus), _ptr(status), _ptr(workspace), ctypes.c_size_t(ws_bytes),
+            _stream(stream, dev))
     return target, accepted, accepted_len, bonus
+
+
+def select_workspace_bytes(B: int, T: int, V: int) -> int:
+    """Workspace bytes select_accepted uses for these sizes (0: none)."""
+    return int(load().ldv_select_workspace_bytes(int(B), int(T), int(V)))
 
 
 def version() -> int:

@@ -116,7 +116,8 @@ def test_read_block_argument_codes(lib):
 def test_select_argument_codes(lib):
     s = lambda **kw: lib.ldv_select_accepted(
         kw.get("B", 2), kw.get("T", 4), kw.get("V", 100), kw.get("dt", 0), kw.get("lg", FAKE),
-        kw.get("tok", FAKE), None, kw.get("tg", FAKE), kw.get("acc", FAKE), None, None, None, None)
+        kw.get("tok", FAKE), None, kw.get("tg", FAKE), kw.get("acc", FAKE), None, None, None,
+        kw.get("ws", None), kw.get("wsb", 0), None)
     assert s(V=0) == -1
     assert s(dt=9) == -1
     assert s(lg=None) == -1 and s(tok=None) == -1 and s(tg=None) == -1 and s(acc=None) == -1
@@ -124,6 +125,26 @@ def test_select_argument_codes(lib):
     assert s(dt=1, lg=ctypes.c_void_p(0x10002)) == -1
     assert s(T=65) == -2
     assert s(B=0) == 0 and s(T=0) == 0
+    # the workspace: 8-byte aligned and at least the queried size when the rows are split
+    need = lib.ldv_select_workspace_bytes(2, 4, 151936)
+    assert need > 0 and need % 8 == 0
+    assert s(V=151936, ws=ctypes.c_void_p(0x10004), wsb=need) == -1
+    assert s(V=151936, ws=FAKE, wsb=need - 8) == -1
+    assert s(V=151936, ws=FAKE, wsb=need, B=0) == 0
+
+
+def test_select_workspace_sizes(lib):
+    """Rows are split only when there are few of them and they are long
+    enough; the size covers one 8-byte partial result per part."""
+    ws = lib.ldv_select_workspace_bytes
+    assert ws(0, 4, 100) == 0 and ws(2, 0, 100) == 0 and ws(2, 65, 100) == 0 and ws(2, 4, 0) == 0
+    assert ws(2, 4, 100) == 0 and ws(2, 4, 32767) == 0  # rows too short to split
+    assert ws(256, 32, 151936) == 0           # 8448 rows fill the GPU by themselves
+    rows = 64 * 17                            # 27B-hybrid-shaped selection: 1088 rows of 151936
+    assert ws(64, 16, 151936) == rows * 4 * 8
+    assert ws(16, 8, 32000) == 0                  # GDN-1.3B shape: rows too short to split
+    assert ws(16, 8, 100003) == 16 * 9 * 3 * 8    # 144 longer rows: parts of >= 32768 values
+    assert ws(32, 64, 151936) == 0                # 2080 rows: enough to fill the GPU
 
 
 def test_verify_chain_long_argument_codes(lib):
@@ -187,6 +208,6 @@ def test_work_item_limits(lib):
     r = lambda B, H, P, Qn: lib.ldv_read_block_states(B, 1, H, 16, 16, P, Qn, 0, FAKE, FAKE, FAKE, None,
                                                       FAKE, FAKE, FAKE, FAKE, None, None)
     assert r(1 << 12, 1 << 10, 8, 16) == -2       # 2^22 heads x 2 chunks = 2^23 units
-    s = lambda B, T: lib.ldv_select_accepted(B, T, 1, 1, FAKE, FAKE, None, FAKE, FAKE, None, None, None, None)
+    s = lambda B, T: lib.ldv_select_accepted(B, T, 1, 1, FAKE, FAKE, None, FAKE, FAKE, None, None, None, None, 0, None)
     assert s((1 << 23) // 8, 7) == -2             # 2^23 rows
 

@@ -21,16 +21,16 @@ def ldv():
     return m
 
 
-def run(ldv, logits, tokens, parent, dtype):
+def run(ldv, logits, tokens, parent, dtype, split=True):
     st = torch.zeros(1, dtype=torch.int32, device="cuda")
     lg = dev(logits).to(torch.bfloat16 if dtype == "bf16" else torch.float32)
-    out = ldv.select_accepted(lg, dev(tokens), None if parent is None else dev(parent), status=st)
+    out = ldv.select_accepted(lg, dev(tokens), None if parent is None else dev(parent), status=st, split=split)
     torch.cuda.synchronize()
     return [t.cpu().numpy() for t in out], int(st.item())
 
 
-def compare(orc, ldv, logits, tokens, parent, dtype, name):
-    (tg, acc, alen, bonus), st = run(ldv, logits, tokens, parent, dtype)
+def compare(orc, ldv, logits, tokens, parent, dtype, name, split=True):
+    (tg, acc, alen, bonus), st = run(ldv, logits, tokens, parent, dtype, split)
     rt, racc, ralen, rbonus, rs = orc.select(logits, tokens, parent)
     assert st == rs == 0
     assert np.array_equal(tg, rt), name + ": target"
@@ -105,8 +105,53 @@ def test_select_workload_full_size(ldv, orc, key):
     wl = WORKLOADS[key]
     x = make_inputs(wl, with_gather=False)
     s = make_select_inputs(wl, x["parent"], x["accepted"])
-    compare(orc, ldv, s["logits"], s["tokens"], x["parent"] if wl.topology == "tree" else None, wl.qkv,
-            "select " + key)
+    for split in (True, False):
+        compare(orc, ldv, s["logits"], s["tokens"], x["parent"] if wl.topology == "tree" else None, wl.qkv,
+                "select %s split=%s" % (key, split), split=split)
+
+
+SPLIT = [  # B, T, V, dtype, value kind
+    (2, 64, 151936, "bf16", "ties"),     # 130 rows in 4 parts each; the walk also combines row 64
+    (16, 8, 100003, "bf16", "normal"),   # 144 rows in 3 parts; odd V
+    (3, 5, 70000, "f32", "ties"),        # 2 parts; equal maxima in both
+    (2, 7, 65579, "f32", "specials"),    # 2 parts; odd V puts rows off 16-byte boundaries
+    (1, 3, 98339, "bf16", "ties"),       # 3 parts, the last one shorter
+]
+
+
+@pytest.mark.parametrize("B,T,V,dtype,kind", SPLIT, ids=lambda v: str(v))
+def test_select_split_rows(ldv, orc, B, T, V, dtype, kind):
+    """Few long rows split over several workgroups (through the workspace)
+    give the oracle's result, and the same as one workgroup per row: equal
+    maxima in different parts go to the lower index, NaN never wins."""
+    assert ldv.select_workspace_bytes(B, T, V) > 0  # the split path runs
+    rng = np.random.default_rng(7200 + B * T + V)
+    par = make_tree(rng, B, T, 6, 3)
+    tokens = rng.integers(0, V, size=(B, T)).astype(np.int32)
+    if kind == "ties":
+        logits = rng.integers(-2, 3, size=(B, T + 1, V)).astype(np.float32)
+    else:
+        logits = rng.standard_normal((B, T + 1, V)).astype(np.float32)
+    for b in range(B):  # agree along a path so that walks go deep
+        n = int(rng.integers(0, T))
+        while n >= 0:
+            logits[b, int(par[b, n]) + 1, tokens[b, n]] = 9.0
+            n = int(par[b, n])
+    if kind == "specials":  # (after the path: these rows stay as set here)
+        m = rng.random(logits.shape)
+        logits[m < 0.05] = np.nan
+        logits[(m >= 0.05) & (m < 0.07)] = -np.inf
+        logits[(m >= 0.08) & (m < 0.1)] = -0.0
+        logits[0, 1] = np.nan                        # a row of NaN
+        logits[0, 2] = -np.inf                       # a row of -inf
+        logits[0, 3] = -np.inf
+        logits[0, 3, V - 5:] = np.nan                # -inf, then NaN in the last part only
+        logits[1, 0, :] = -1.0
+        logits[1, 0, [V // 2 - 10, V - 1]] = 7.0    # one maximum in each of the two parts
+    if dtype == "bf16":
+        logits = bf16_round(logits)
+    compare(orc, ldv, logits, tokens, par, dtype, "select split B%d T%d V%d %s" % (B, T, V, kind))
+    compare(orc, ldv, logits, tokens, par, dtype, "select unsplit B%d T%d V%d %s" % (B, T, V, kind), split=False)
 
 
 def test_select_bad_parent(ldv, orc):
@@ -179,8 +224,9 @@ def _special_rows(rng, R, V):
     return x, snan_rows
 
 
+@pytest.mark.parametrize("split", [True, False])
 @pytest.mark.parametrize("V,dtype", [(50003, "f32"), (151936, "bf16"), (32005, "bf16")])
-def test_select_specials_long_rows(ldv, orc, V, dtype):
+def test_select_specials_long_rows(ldv, orc, V, dtype, split):
     """Argmax edge cases on rows long enough for full eight-chunk steps:
     NaN (quiet and signalling) never wins, equal values go to the lower
     index across chunks and threads, +0 == -0, rows whose largest value is
@@ -211,7 +257,8 @@ def test_select_specials_long_rows(ldv, orc, V, dtype):
     ref = ref.reshape(B, T + 1, V)
     tokens = rng.integers(0, V, size=(B, T)).astype(np.int32)
     st = torch.zeros(1, dtype=torch.int32, device="cuda")
-    tg, acc, alen, bonus = (t.cpu().numpy() for t in ldv.select_accepted(lg, dev(tokens), None, status=st))
+    tg, acc, alen, bonus = (t.cpu().numpy() for t in ldv.select_accepted(lg, dev(tokens), None, status=st,
+                                                                          split=split))
     rt, racc, ralen, rbonus, rs = orc.select(ref, tokens, None)
     assert int(st.item()) == rs == 0
     assert np.array_equal(tg, rt), "targets %s vs %s" % (tg.ravel()[:16], rt.ravel()[:16])
