@@ -149,9 +149,9 @@ __global__ __launch_bounds__(NTHR) void argmax_kernel(const SelectArgs p) {
     // this workgroup's part of the row, elements [lo, lo + V): parts of whole
     // 16-byte chunks (each the same distance from a chunk boundary as the
     // row), the last one shorter or empty
-    const int seg = ((p.V + np - 1) / np + EPC - 1) / EPC * EPC;
-    const int lo = min((int)(blockIdx.x % np) * seg, p.V);
-    const int V = min(lo + seg, p.V) - lo;
+    const long long seg = (((long long)p.V + np - 1) / np + EPC - 1) / EPC * EPC;
+    const int lo = (int)min((long long)(blockIdx.x % np) * seg, (long long)p.V);
+    const int V = (int)(min(lo + seg, (long long)p.V) - lo);
     const unsigned char* base = static_cast<const unsigned char*>(p.logits) + (row * (size_t)p.V + lo) * ES;
     // elements up to the first 16-byte boundary of the row, 16-byte chunks,
     // then the elements past the last whole chunk
