@@ -1,9 +1,10 @@
 """Throughput of the verify -> commit -> gather path on one MI355X.
 
 One step = ldv_verify_chain / ldv_verify_tree over every draft node of the
-batch, ldv_commit_state of the accepted node (in place), and, for workloads
-with drafter reads, ldv_gather_states (o = S q for every query) - one pass of
-the whole path over one batch of seeded synthetic inputs already resident in
+batch (ldv_verify_chain_long for the chains longer than 64 nodes),
+ldv_commit_state of the accepted node (in place), and, for workloads with
+drafter reads, ldv_gather_states (o = S q for every query) - one pass of the
+whole path over one batch of seeded synthetic inputs already resident in
 HBM.  Buffer sets are rotated (at least 4, at least 1 GB in all) so that the
 256 MB Infinity Cache cannot hold a step's working set.
 
@@ -35,7 +36,7 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-from workloads import (WORKLOADS, make_block_read_inputs, make_inputs, make_select_inputs,  # noqa: E402
+from workloads import (LONG_WORKLOADS, WORKLOADS, make_block_read_inputs, make_inputs, make_select_inputs,  # noqa: E402
                        tree_depths)
 
 METRIC = "verified draft nodes/sec (B*H*N) on MFMA; commit+gather HBM GB/s vs peak"
@@ -51,9 +52,17 @@ def algorithmic(wl, x):
     esz = 2 if wl.qkv == "bf16" else 4
     depth = np.stack([tree_depths(r) for r in x["parent"]])         # [B, T]
     A = depth.sum(axis=1)                                           # sum of depths per sequence
-    per_head = D * D * 4 + T * (3 * D * esz + 8 + 2 * D * 4 + 4)    # S0, q k v, a beta, o u, logp
+    # a chain longer than 64 nodes is verified in 64-node chunks: each reads
+    # its base state, and all but the last write the next one; the ancestor
+    # pairs the closed form evaluates are those inside a chunk, and each
+    # chunk end state costs 2 * 64 * d^2 flops
+    nch = -(-T // 64)
+    per_head = (2 * nch - 1) * D * D * 4 + T * (3 * D * esz + 8 + 2 * D * 4 + 4)  # states, q k v, a beta, o u, logp
     verify_bytes = B * H * per_head + (B * T * 4 if wl.topology == "tree" else 0)
-    verify_flops = float(np.sum(H * (4 * T * D * D + 2 * D * (4 * A - 2 * T))))
+    if nch > 1:
+        lens = [min(64, T - 64 * c) for c in range(nch)]
+        A = np.full(B, sum(n * (n + 1) // 2 for n in lens))
+    verify_flops = float(np.sum(H * (4 * T * D * D + 2 * D * (4 * A - 2 * T)))) + B * H * (nch - 1) * 2 * 64 * D * D
     acc = x["accepted"]
     L = np.where(acc >= 0, depth[np.arange(B), np.maximum(acc, 0)], 0)
     committing = int(np.sum(acc >= 0))
@@ -82,14 +91,19 @@ def cpu_baseline(wl, x, seconds_min=10.0, seconds_cap=30.0):
     import oracle
     threads = min(16, os.cpu_count() or 1)
     chain = wl.topology == "chain"
+    long_chain = chain and wl.T > 64  # sequential decode: walking every path would be O(T^2) per head
     done, t_total = 0, 0.0
     step = max(1, wl.B // 16)
     while (t_total < seconds_min or done % wl.B) and t_total < seconds_cap:
         b0 = done % wl.B
         sl = slice(b0, min(wl.B, b0 + step))
         t0 = time.perf_counter()
-        oracle.verify(x["q"][sl], x["k"][sl], x["v"][sl], x["a"][sl], x["beta"][sl], x["S0"][sl],
-                      None if chain else x["parent"][sl], nthreads=threads)
+        if long_chain:
+            oracle.chain_decode(x["q"][sl], x["k"][sl], x["v"][sl], x["a"][sl], x["beta"][sl], x["S0"][sl],
+                                nthreads=threads)
+        else:
+            oracle.verify(x["q"][sl], x["k"][sl], x["v"][sl], x["a"][sl], x["beta"][sl], x["S0"][sl],
+                          None if chain else x["parent"][sl], nthreads=threads)
         oracle.commit(x["k"][sl], x["v"][sl], x["a"][sl], x["beta"][sl], x["S0"][sl], x["accepted"][sl],
                       None if chain else x["parent"][sl], nthreads=threads)
         if wl.P > 0:
@@ -98,10 +112,10 @@ def cpu_baseline(wl, x, seconds_min=10.0, seconds_cap=30.0):
         done += sl.stop - sl.start
     nodes = done * wl.H * wl.T
     return {"value": nodes / t_total, "unit": "nodes/s", "cores": threads, "kind": "oracle",
-            "sample": "%d sequence passes over the %d sequences (all %d heads; every node verified by its "
-                      "path walk, the accepted node committed%s), %.1f s" % (
-                          done, wl.B, wl.H, ", 4 positions x 16 queries read per sequence" if wl.P else "",
-                          t_total)}
+            "sample": "%d sequence passes over the %d sequences (all %d heads; every node verified by %s, "
+                      "the accepted node committed%s), %.1f s" % (
+                          done, wl.B, wl.H, "sequential decode" if long_chain else "its path walk",
+                          ", 4 positions x 16 queries read per sequence" if wl.P else "", t_total)}
 
 
 class HipEvents:
@@ -144,9 +158,9 @@ class HipEvents:
         self.lib.hipEventDestroy(e)
 
 
-def traffic_from_profiles(kernel_name, src_files):
+def traffic_from_profiles(kernel_name, src_files, workload):
     """HBM bytes per launch measured by rocprofv3 counters, if they were taken
-    on the kernel source as it is now (else None)."""
+    on this workload and on the kernel source as it is now (else None)."""
     import hashlib
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
@@ -158,7 +172,7 @@ def traffic_from_profiles(kernel_name, src_files):
         with open(os.path.join(ROOT, s), "rb") as f:
             h.update(f.read())
     ent = rec.get(kernel_name)
-    if not ent or ent.get("source_sha256") != h.hexdigest():
+    if not ent or ent.get("source_sha256") != h.hexdigest() or ent.get("workload") != workload:
         return None
     return ent.get("bytes_per_launch")
 
@@ -187,6 +201,8 @@ class Runner:
             st["o"] = torch.empty((wl.B, wl.T, wl.H, wl.D), device="cuda")
             st["u"] = torch.empty((wl.B, wl.T, wl.H, wl.D), device="cuda")
             st["logp"] = torch.empty((wl.B, wl.T, wl.H), device="cuda")
+            if wl.T > 64:  # the work state of a long chain
+                st["S_work"] = torch.empty_like(st["S0"])
             self.sets.append(st)
         del base
         self.status = torch.zeros(1, dtype=torch.int32, device="cuda")
@@ -219,7 +235,10 @@ class Runner:
 
     def verify(self, i):
         s = self.sets[i % len(self.sets)]
-        if self.chain:
+        if self.chain and self.wl.T > 64:
+            self.ldv.verify_chain_long(s["q"], s["k"], s["v"], s["a"], s["beta"], s["S0"], o=s["o"], u=s["u"],
+                                       logp=s["logp"], S_work=s["S_work"], status=self.status)
+        elif self.chain:
             self.ldv.verify_chain(s["q"], s["k"], s["v"], s["a"], s["beta"], s["S0"], o=s["o"], u=s["u"],
                                   logp=s["logp"], status=self.status)
         else:
@@ -313,7 +332,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(WORKLOADS))
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted({**WORKLOADS, **LONG_WORKLOADS}))
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-next", action="store_true", help="skip timing the in-block read and the selection")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum CPU-oracle time")
@@ -349,7 +368,9 @@ def main():
         return
     import speculative_decoding_verify_amd as ldv
 
-    wl = WORKLOADS[args.workload]
+    wl = {**WORKLOADS, **LONG_WORKLOADS}[args.workload]
+    if wl.T > 64:  # the in-block reads and the selection take drafts of at most 64 nodes
+        args.no_next = True
     K = args.steps
     nsets = int(min(64, max(4, -(-1_000_000_000 // set_bytes(wl)))))
     print("[bench] generating %s inputs (%d rotated buffer sets)" % (wl.key, nsets), file=sys.stderr, flush=True)
@@ -450,7 +471,8 @@ def main():
             "gather": "speculative_decoding_verify_amd/csrc/gather.hip"}
     roof = {"kernel": dom, "bound": "hbm", "achieved": kern[dom]["GB_s"], "peak": HBM_PEAK_GBS,
             "unit": "GB/s", "frac": kern[dom]["hbm_frac"],
-            "traffic": traffic_from_profiles(dom, [srcs[dom], "speculative_decoding_verify_amd/csrc/ldv_device.hpp"])}
+            "traffic": traffic_from_profiles(dom, [srcs[dom], "speculative_decoding_verify_amd/csrc/ldv_device.hpp"],
+                                             wl.key)}
     if peaks:
         roof["measured_peaks"] = peaks
         roof["frac_of_measured_copy"] = kern[dom]["GB_s"] / peaks["copy_GB_s"]

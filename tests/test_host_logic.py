@@ -56,3 +56,17 @@ def test_xcd_spread_is_a_bijection(tmp_path):
     r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
     assert r.returncode == 0, r.stdout + r.stderr
     assert r.stdout.strip().endswith(" 0 bad"), r.stdout
+
+
+def test_bench_algorithmic_bytes():
+    """bench.py's algorithmic verify bytes: per head the state (64 KiB at
+    d = 128) and, per node, bf16 q/k/v (768), the gates (8), fp32 o and u
+    (1024) and log P (4): 79,968 bytes per head for a chain of 8.  A chain
+    longer than 64 nodes reads one base state per chunk and writes one per
+    chunk but the last."""
+    import bench
+    from workloads import LONG_WORKLOADS, WORKLOADS, make_inputs
+    wl = WORKLOADS["gdn1.3b-chain"].replace(B=2, H=3)
+    assert bench.algorithmic(wl, make_inputs(wl, with_gather=False))["verify"] == 2 * 3 * 79968
+    wl = LONG_WORKLOADS["gdn1.3b-chain1024"].replace(B=1, H=2, T=130)  # three chunks
+    assert bench.algorithmic(wl, make_inputs(wl, with_gather=False))["verify"] == 2 * (5 * 65536 + 130 * 1804)

@@ -100,6 +100,21 @@ WORKLOADS = {
 }
 
 
+# Chains longer than one 64-node chunk (ldv_verify_chain_long): the
+# 27B-hybrid- and GDN-1.3B-shaped layers with long draft blocks.  Kept apart
+# from WORKLOADS, every entry of which the per-call tests run at full size.
+LONG_WORKLOADS = {
+    "hybrid27b-chain256": Workload(
+        "hybrid27b-chain256", "27B-hybrid-shaped layer, long chain: B64 H32 d128, chain of 256 (4 chunks)",
+        B=64, H=32, D=128, T=256, topology="chain", qkv="bf16", s0_std=0.05,
+        accept="geometric", seed=6),
+    "gdn1.3b-chain1024": Workload(
+        "gdn1.3b-chain1024", "GDN-1.3B-shaped layer, long chain: B16 H16 d128, chain of 1024 (16 chunks)",
+        B=16, H=16, D=128, T=1024, topology="chain", qkv="bf16", s0_std=0.05,
+        accept="geometric", seed=7),
+}
+
+
 def bf16_round(x: np.ndarray) -> np.ndarray:
     """Round fp32 values to the nearest bf16 (ties to even); return fp32.
 
