@@ -6,6 +6,8 @@
 
 namespace ldv {
 
+constexpr int kCus = 256;  // MI355X: compute units
+
 // Node arrays ([B, T, H, ...] and [B, T, H]) are addressed as node
 // b * Ts + t0 + n for n < T: a call on a whole draft has Ts = T and t0 = 0;
 // a chunk of a longer chain views nodes [t0, t0 + T) of arrays with Ts nodes
@@ -26,10 +28,12 @@ struct VerifyArgs {
     float* u_out;     // may be NULL (together with logp_out)
     float* logp_out;  // may be NULL
     int* status;      // may be NULL
-    // may be NULL; else T = 64 and the kernel also forms the state at node
-    // T - 1 into S_next (may equal S0: each wave reads its rows of S0 before
-    // it writes the same rows of S_next)
+    // may be NULL; else the call verifies `chunks` 64-node chunks of a chain
+    // of Ts > 64 nodes from node t0, each from the state at the end of the
+    // one before (S0 for the chunk at node 0, else S_next, the work state),
+    // and forms each chunk's end state in S_next unless it ends the chain
     float* S_next;
+    int chunks;
 };
 
 struct CommitArgs {
