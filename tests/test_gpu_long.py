@@ -35,7 +35,7 @@ def run(ldv, c, qkv):
     return t, a, beta, S0, o, u, logp, st
 
 
-GRID = [  # B, T, H, D, qkv
+GRID = [  # B, T, H, D, qkv (up to 256 heads: one launch for all chunks; more: a launch per chunk)
     (2, 65, 2, 128, "bf16"),
     (2, 100, 3, 128, "bf16"),
     (3, 129, 2, 64, "f32"),
@@ -44,6 +44,8 @@ GRID = [  # B, T, H, D, qkv
     (2, 80, 2, 128, "f32"),
     (32, 100, 64, 128, "bf16"),   # 2048 heads: both chunks store through LDS
     (16, 130, 32, 128, "f32"),    # 512 heads, fp32 inputs: staged stores, two in-place chunk ends
+    (12, 150, 32, 128, "bf16"),   # 384 heads: a launch per chunk, outputs stored straight
+    (8, 200, 32, 64, "bf16"),     # 256 heads at d = 64: all four chunks in one launch
     (2, 140, 2, 64, "bf16"),
     (2, 90, 2, 32, "f32"),
     (2, 70, 3, 16, "bf16"),
