@@ -76,8 +76,15 @@ extern "C" {
 #define LDV_F32 1
 
 #define LDV_MAX_T 64
-/* Longest chain ldv_verify_chain_long and ldv_commit_state (chain) accept. */
-#define LDV_MAX_LONG_T (1 << 20)
+/* Longest chain ldv_verify_chain_long and ldv_commit_state (chain) accept.
+ * log P is an fp32 sum counted from S0, and commit forms its weights as
+ * exp(log P_n - log P_m): each weight carries a relative error of about one
+ * fp32 ulp of |log P|, which grows with the chain.  At 8192 nodes, with
+ * decay gates a = exp(-softplus(x)), x ~ N(0, 1) or N(2, 1), a simulation of
+ * these fp32 sums keeps the committed state within 2.3e-4 of the exact one;
+ * at 16384 nodes it reached 1.4e-3 and at 65536 nodes 1.3e-3 to 8e-4, near
+ * the 2e-3 bound, so longer chains are not accepted. */
+#define LDV_MAX_LONG_T 8192
 
 /*
  * Verify a draft tree: for every node n of every (sequence b, head h),
@@ -127,18 +134,20 @@ int ldv_verify_chain(int B, int T, int H, int dk, int dv, int qkv_dtype,
  * verified with the closed form from the state at the end of chunk c - 1,
  * which the verify of chunk c - 1 also forms, in S_work, from its own
  * factors (the chunk form: the Bole page's Eq. (2) per chunk, Eq. (9) at the
- * chunk's last node to pass the state on).  One kernel per chunk.  Results
- * are those of ldv_verify_chain on the whole chain: o, the node corrections
- * u_n = beta_n (v_n - a_n S_{n-1} k_n) and log P_n counted from S0, so
- * ldv_commit_state (no parent array) commits any node from S0.
+ * chunk's last node to pass the state on).  When B * H is at most the CU
+ * count (256) one kernel launch verifies every chunk, each workgroup taking
+ * its head's chunks in order; larger grids get one launch per chunk, in
+ * order on `stream`.  Results are those of ldv_verify_chain on the whole
+ * chain: o, the node corrections u_n = beta_n (v_n - a_n S_{n-1} k_n) and
+ * log P_n counted from S0, so ldv_commit_state (no parent array) commits any
+ * node from S0 (see LDV_MAX_LONG_T for the precision of log P).
  *
  *   q, k, v, a, beta, S0, o: as for ldv_verify_chain; u_out and logp_out are
  *             required
  *   S_work    [B, H, dv, dk] fp32 scratch owned by the caller, not
  *             overlapping S0; needed when T > LDV_MAX_T (may be NULL
  *             otherwise); its contents on return are unspecified
- * The chunks are enqueued in order on `stream`.  T <= LDV_MAX_T is the same
- * as ldv_verify_chain.
+ * T <= LDV_MAX_T is the same as ldv_verify_chain.
  */
 int ldv_verify_chain_long(int B, int T, int H, int dk, int dv, int qkv_dtype,
                           const void* q, const void* k, const void* v,
@@ -283,7 +292,9 @@ int ldv_read_block_states_packed(int B, int T, int H, int dk, int dv, int P, int
  *                 returns LDV_ERR_ARG
  * The logits need element alignment only.  A sequence with an invalid parent
  * row -> LDV_STATUS_BAD_PARENT; its target row is written, its accepted,
- * accepted_len and bonus are not.  V must be >= 1; T <= 64.
+ * accepted_len and bonus are not.  V must be >= 1; 0 <= T <= 64.  With T = 0
+ * (no draft nodes) tokens may be NULL: target row 0 is written, accepted is
+ * -1, accepted_len 0 and bonus row 0's argmax.
  */
 int ldv_select_accepted(int B, int T, int V, int logits_dtype, const void* logits,
                         const int32_t* tokens, const int32_t* parent, int32_t* target,

@@ -20,7 +20,7 @@ import numpy as np
 
 from . import build as _build
 
-__all__ = ["Oracle", "default", "verify", "commit", "chain_decode", "verify_dfs",
+__all__ = ["Oracle", "default", "verify", "commit", "chain_decode", "log_decay", "verify_dfs",
            "gather", "read_states", "select", "BAD_PARENT", "BAD_ACCEPTED", "BAD_SLOT",
            "BAD_POSITION"]
 
@@ -69,7 +69,8 @@ class Oracle:
                                            _i32p, _i32p, _f32p, _f64p, i]
         lib.oracle_select.argtypes = [i, i, ctypes.c_long, _f32p, _i32p, _i32p, _i32p, _i32p,
                                       _i32p, _i32p, i]
-        for f in ("oracle_verify", "oracle_commit", "oracle_chain_decode",
+        lib.oracle_log_decay.argtypes = [i, i, i, _f32p, _i32p, _f64p]
+        for f in ("oracle_verify", "oracle_commit", "oracle_chain_decode", "oracle_log_decay",
                   "oracle_verify_dfs", "oracle_gather", "oracle_read_states", "oracle_select"):
             getattr(lib, f).restype = ctypes.c_int
         self.lib = lib
@@ -108,6 +109,17 @@ class Oracle:
                                         _p(beta, _f32p), _p(S0, _f32p), _p(par, _i32p),
                                         _p(acc, _i32p), _p(S_out, _f64p), _threads(nthreads))
         return S_out, status
+
+    def log_decay(self, a, parent=None):
+        """log P_n per (b, n, h): the log of the product of the decay gates on
+        the root-to-n path, multiplied in fp64 along the walk.  parent=None
+        means a chain.  Returns (logp fp64 [B, T, H], status)."""
+        a = _f32(a)
+        B, T, H = a.shape
+        par = None if parent is None else _i32(parent)
+        logp = np.zeros((B, T, H), dtype=np.float64)
+        status = self.lib.oracle_log_decay(B, T, H, _p(a, _f32p), _p(par, _i32p), _p(logp, _f64p))
+        return logp, status
 
     def chain_decode(self, q, k, v, a, beta, S0, nthreads=None):
         """Sequential decode with one running state: o_n read after token n."""
@@ -208,6 +220,10 @@ def commit(*args, **kw):
 
 def chain_decode(*args, **kw):
     return default().chain_decode(*args, **kw)
+
+
+def log_decay(*args, **kw):
+    return default().log_decay(*args, **kw)
 
 
 def verify_dfs(*args, **kw):

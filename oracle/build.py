@@ -17,7 +17,7 @@ def build(verbose: bool = False, src: str = SRC, out: str = LIB) -> str:
     """Compile ``src`` (default oracle.c) into the shared library ``out``."""
     tmp = out + ".tmp%d" % os.getpid()
     cmd = ["gcc", "-O2", "-std=c11", "-Wall", "-Wextra", "-fPIC", "-shared",
-           "-pthread", "-fno-fast-math", "-ffp-contract=off", src, "-o", tmp]
+           "-pthread", "-fno-fast-math", "-ffp-contract=off", src, "-o", tmp, "-lm"]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)

@@ -41,6 +41,7 @@
  * [0, num_slots), 8 = a read position outside [-1, T-1].  The outputs of an
  * affected sequence (or position) are left untouched.
  */
+#include <math.h>
 #include <pthread.h>
 #include <stdint.h>
 #include <stdlib.h>
@@ -235,6 +236,46 @@ int oracle_verify(int B, int T, int H, int dk, int dv, const float* q, const flo
     walk_ctx c = {B, T, H, dk, dv, q, k, v, a, beta, S0, parent, NULL, o, u, states, NULL, ok};
     run_items(verify_item, &c, (long)B * H, walk_work(T, dk, dv), nthreads);
     free(ok);
+    return status;
+}
+
+/*
+ * Log decay of every node: logp[b, n, h] = log P_n, where P_n is the product
+ * of the decay gates a_m over the root-to-n path (m = n included), multiplied
+ * in fp64 node by node along the walk (a zero gate gives -inf).  This is the
+ * gate product that multiplies S0 in the unrolled recurrence (with b = 0 the
+ * walk gives S_n = P_n S0), the factor P of the Bole page's Eq. (2) / Eq. (9).
+ * The running product is kept as m * 2^e with m in [1/2, 1) (frexp after
+ * every factor), so that long paths, whose product is far below the fp64
+ * range, keep full precision: log P = log m + e log 2.
+ *   a: [B, T, H]; parent: [B, T] or NULL (chain); logp: [B, T, H] fp64
+ * Returns status bits (OR_BAD_PARENT; the rows of such a sequence are left
+ * untouched).
+ */
+int oracle_log_decay(int B, int T, int H, const float* a, const int32_t* parent, double* logp) {
+    if (B <= 0 || T <= 0 || H <= 0) return 0;
+    int status = 0;
+    int* path = (int*)malloc(sizeof(int) * (size_t)T);
+    for (int b = 0; b < B; ++b) {
+        if (!parents_valid(parent, T, b)) {
+            status |= OR_BAD_PARENT;
+            continue;
+        }
+        for (int n = 0; n < T; ++n) {
+            int len = root_path(parent, T, b, n, path);
+            for (int h = 0; h < H; ++h) {
+                double P = 1.0;
+                long e2 = 0;
+                for (int i = 0; i < len; ++i) {
+                    int e;
+                    P = frexp(P * (double)a[((size_t)b * T + path[i]) * H + h], &e);
+                    e2 += e;
+                }
+                logp[((size_t)b * T + n) * H + h] = log(P) + (double)e2 * log(2.0);
+            }
+        }
+    }
+    free(path);
     return status;
 }
 

@@ -19,7 +19,8 @@
 // (sequence, head, row block of up to 16 KiB; small blocks keep more of them
 // in flight per CU, measured 2-3 % faster than 32 KiB); each thread owns
 // float4 chunks of consecutive columns so that every wave reads and writes
-// contiguous 1 KiB runs.  The block loads the parent row, then its S0 rows; walks the parent
+// contiguous 1 KiB runs, so the state is read with non-temporal loads
+// (whole lines, used once).  The block loads the parent row, then its S0 rows; walks the parent
 // row in LDS from the accepted node to the root while the state is in
 // flight; issues the loads of u, k and log P on the path; stages w_m u_m (its
 // rows) and k_m (all columns) for up to 16 path nodes at a time in LDS; and
@@ -86,7 +87,7 @@ __global__ __launch_bounds__(256) void commit_kernel(const CommitArgs p) {
 #pragma unroll
     for (int i = 0; i < F4; ++i) {
         const int f = tid + NTHR * i;
-        if (F4 * NTHR == E4 || f < E4) sv[i] = ld_stream(src + 4 * f);
+        if (F4 * NTHR == E4 || f < E4) sv[i] = ld_nt(src + 4 * f);
     }
     asm volatile("" ::: "memory");  // keep the loads above ahead of any use of them
     if (nacc < 0) {  // nothing accepted, out of place: copy the committed state

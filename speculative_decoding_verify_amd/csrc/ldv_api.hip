@@ -229,7 +229,7 @@ LDV_EXPORT int ldv_read_block_states_packed(int B, int T, int H, int dk, int dv,
 }
 
 LDV_EXPORT size_t ldv_select_workspace_bytes(int B, int T, int V) {
-    if (B <= 0 || T <= 0 || V <= 0 || T > LDV_MAX_T) return 0;
+    if (B <= 0 || T < 0 || V <= 0 || T > LDV_MAX_T) return 0;
     const long long rows = (long long)B * (T + 1);
     const int np = ldv::select_parts(rows, V);
     return np > 1 ? (size_t)rows * np * sizeof(ldv::ArgPart) : 0;
@@ -242,8 +242,10 @@ LDV_EXPORT int ldv_select_accepted(int B, int T, int V, int logits_dtype, const 
     if (B < 0 || T < 0 || V <= 0) return LDV_ERR_ARG;
     if (logits_dtype != LDV_BF16 && logits_dtype != LDV_F32) return LDV_ERR_ARG;
     if (T > LDV_MAX_T) return LDV_ERR_UNSUPPORTED;
-    if (B == 0 || T == 0) return LDV_OK;
-    if (!logits || !tokens || !target || !accepted) return LDV_ERR_ARG;
+    if (B == 0) return LDV_OK;
+    // T = 0 (no draft nodes): row 0 is still read, nothing is accepted and
+    // the bonus token is row 0's argmax; tokens may then be NULL
+    if (!logits || (T > 0 && !tokens) || !target || !accepted) return LDV_ERR_ARG;
     if (!aligned(logits, logits_dtype == LDV_F32 ? 4 : 2) || !aligned(tokens, 4) || !aligned(parent, 4) ||
         !aligned(target, 4) || !aligned(accepted, 4) || !aligned(accepted_len, 4) || !aligned(bonus, 4) ||
         !aligned(status, 4))

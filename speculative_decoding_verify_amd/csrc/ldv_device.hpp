@@ -95,12 +95,24 @@ __device__ __forceinline__ floatx4 mma3(floatx4 acc, bf16x8 ah, bf16x8 al, bf16x
 
 // Streaming accesses: data read or written exactly once per call (states,
 // outputs).  Outputs go through non-temporal stores, which let HBM mix the
-// write stream with the read stream at less loss; the state reads stay
-// ordinary loads (non-temporal loads measured slower on MI355X for this
-// path).
+// write stream with the read stream at less loss.  Reads depend on their
+// pattern:
+//   - ld_nt, a non-temporal load, where each wave load covers whole
+//     contiguous 128-byte lines (commit's state rows, the logits): measured
+//     7-13% faster than ordinary loads on MI355X (commit 36.2 -> 33.7 us on
+//     the 27B-hybrid shape, 197.9 -> 175.3 us on batch-256);
+//   - ld_stream, an ordinary load, where each load instruction covers 64-byte
+//     halves of lines (state rows loaded straight into MFMA operand
+//     registers): non-temporal loads measured 12% slower there in the gather
+//     and no faster in verify and the in-block read.
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float4 ld_stream(const float* p) { return *reinterpret_cast<const float4*>(p); }
+
+__device__ __forceinline__ float4 ld_nt(const float* p) {
+    const f32x4 v = __builtin_nontemporal_load(reinterpret_cast<global_ptr<const f32x4>>((global_ptr<const float>)p));
+    return make_float4(v[0], v[1], v[2], v[3]);
+}
 
 __device__ __forceinline__ void st_stream(float* p, const float4 v) {
     const f32x4 w = {v.x, v.y, v.z, v.w};

@@ -1,14 +1,22 @@
-// Achievable MFMA rate on this GPU, for the measurement harness only (not
-// part of the ldv ABI; built into its own library, libldv_peaks.so).
+// Achievable rates on this GPU, for the measurement harness only (not part of
+// the ldv ABI; built into its own library, libldv_peaks.so).
 //
-// Every wave runs kIters rounds of eight independent accumulation chains of
-// v_mfma_f32_16x16x32_bf16 (the instruction every kernel of the library
-// uses), so the matrix pipe never waits on a result.  Each lane then writes
-// one value derived from all eight accumulators, so nothing is dead code.
-// The round count is a compile-time constant: with a run-time count the
-// compiler rotates the accumulators through copies every round.
+// MFMA: every wave runs kIters rounds of eight independent accumulation
+// chains of v_mfma_f32_16x16x32_bf16 (the instruction every kernel of the
+// library uses), so the matrix pipe never waits on a result.  Each lane then
+// writes one value derived from all eight accumulators, so nothing is dead
+// code.  The round count is a compile-time constant: with a run-time count
+// the compiler rotates the accumulators through copies every round.
 // Flops per launch: blocks * 4 waves * kIters * 8 * (2 * 16 * 16 * 32).
+//
+// HBM streams: grid-stride kernels over a buffer of float4 in the read/write
+// mixes of the library's kernels: reads only (the selection's logits), one
+// write per read (commit: a state in, a state out, in place or not), and one
+// write per two, four or eight reads (verify, the gathers and the in-block
+// reads write less than they read).  Each kernel of the library is graded against
+// the probe nearest its own mix.
 #include <hip/hip_runtime.h>
+#include <stdint.h>
 
 namespace {
 
@@ -39,11 +47,52 @@ __global__ __launch_bounds__(kThreads) void mfma_peak_kernel(float seed, float* 
     out[(size_t)blockIdx.x * kThreads + threadIdx.x] = s;
 }
 
+// Stream probes: each thread keeps L = max(4, R) 16-byte non-temporal loads
+// in flight per step (four measured fastest on MI355X: 7.1-7.2 TB/s for
+// reads alone against about 6.0 TB/s with ordinary loads) and writes, with
+// non-temporal stores, one float4 per R float4 read (their sum, so the loads
+// are live); R = 0 reads only and writes one float4 per thread at the end.
+// A block step covers L * 256 consecutive float4, each wave load 1 KiB of
+// consecutive bytes.  Step w writes its sums at float4 w * (L / R) * 256 + ...,
+// so with R = 1 and dst == src every float4 is rewritten in place right after
+// it is read.
+constexpr int kMaxLoads = 8;
+
+template <int R>
+__global__ __launch_bounds__(kThreads) void stream_kernel(const floatx4* src, floatx4* dst, size_t n) {
+    constexpr int kLoads = R > 4 ? R : 4;
+    constexpr int W = R > 0 ? kLoads / R : 0;  // float4 written per thread and step
+    const size_t per_block = (size_t)kLoads * kThreads;
+    const size_t nsteps = n / per_block;
+    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (size_t w = blockIdx.x; w < nsteps; w += gridDim.x) {
+        const size_t base = w * per_block + threadIdx.x;
+        floatx4 v[kLoads];
+#pragma unroll
+        for (int i = 0; i < kLoads; ++i) v[i] = __builtin_nontemporal_load(src + base + (size_t)i * kThreads);
+        if constexpr (R == 0) {
+#pragma unroll
+            for (int i = 0; i < kLoads; ++i) acc += v[i];
+        } else {
+#pragma unroll
+            for (int j = 0; j < W; ++j) {
+                floatx4 s = v[j * R];
+#pragma unroll
+                for (int i = 1; i < R; ++i) s += v[j * R + i];
+                __builtin_nontemporal_store(s, dst + w * (size_t)W * kThreads + (size_t)j * kThreads + threadIdx.x);
+            }
+        }
+    }
+    if constexpr (R == 0) dst[(size_t)blockIdx.x * kThreads + threadIdx.x] = acc;
+}
+
 }  // namespace
+
+#define PEAKS_EXPORT extern "C" __attribute__((visibility("default")))
 
 // Enqueue one launch of `blocks` workgroups (out: blocks * 256 floats).
 // Returns 0, or the HIP error code of the launch.
-extern "C" __attribute__((visibility("default"))) int ldv_peak_mfma(int blocks, float* out, void* stream) {
+PEAKS_EXPORT int ldv_peak_mfma(int blocks, float* out, void* stream) {
     if (blocks <= 0 || out == nullptr) return (int)hipErrorInvalidValue;
     hipLaunchKernelGGL(mfma_peak_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, static_cast<hipStream_t>(stream),
                        1e-3f, out);
@@ -51,6 +100,31 @@ extern "C" __attribute__((visibility("default"))) int ldv_peak_mfma(int blocks, 
 }
 
 // Floating-point operations of one launch.
-extern "C" __attribute__((visibility("default"))) double ldv_peak_mfma_flops(int blocks) {
+PEAKS_EXPORT double ldv_peak_mfma_flops(int blocks) {
     return (double)blocks * (kThreads / 64) * kIters * kChains * (2.0 * 16 * 16 * 32);
+}
+
+// Float4 granule of the stream probes: n4 must be a multiple of it.
+PEAKS_EXPORT long long ldv_peak_stream_granule(void) { return (long long)kMaxLoads * kThreads; }
+
+// One launch of the stream probe reading n4 float4 of src and writing one
+// float4 per `ratio` read (ratio 1, 2, 4 or 8; 0 = reads only).  dst holds at
+// least n4 / ratio float4 (ratio 0: blocks * 256 float4); dst == src with
+// ratio 1 rewrites src in place.  Returns 0 or a HIP error code (an invalid
+// size, ratio or pointer gives hipErrorInvalidValue before any launch).
+PEAKS_EXPORT int ldv_peak_stream(int ratio, const void* src, void* dst, long long n4, int blocks, void* stream) {
+    if (!src || !dst || blocks <= 0 || n4 <= 0 || n4 % ldv_peak_stream_granule() != 0) return (int)hipErrorInvalidValue;
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    const floatx4* s = static_cast<const floatx4*>(src);
+    floatx4* d = static_cast<floatx4*>(dst);
+    const dim3 g((unsigned)blocks), b(kThreads);
+    switch (ratio) {
+        case 0: hipLaunchKernelGGL(stream_kernel<0>, g, b, 0, st, s, d, (size_t)n4); break;
+        case 1: hipLaunchKernelGGL(stream_kernel<1>, g, b, 0, st, s, d, (size_t)n4); break;
+        case 2: hipLaunchKernelGGL(stream_kernel<2>, g, b, 0, st, s, d, (size_t)n4); break;
+        case 4: hipLaunchKernelGGL(stream_kernel<4>, g, b, 0, st, s, d, (size_t)n4); break;
+        case 8: hipLaunchKernelGGL(stream_kernel<8>, g, b, 0, st, s, d, (size_t)n4); break;
+        default: return (int)hipErrorInvalidValue;
+    }
+    return (int)hipGetLastError();
 }

@@ -21,7 +21,7 @@ LDV_OK, LDV_ERR_ARG, LDV_ERR_UNSUPPORTED, LDV_ERR_LAUNCH = 0, -1, -2, -3
 LDV_BF16, LDV_F32 = 0, 1
 STATUS_BAD_PARENT, STATUS_BAD_ACCEPTED, STATUS_BAD_SLOT, STATUS_BAD_POSITION = 1, 2, 4, 8
 MAX_T = 64
-MAX_LONG_T = 1 << 20
+MAX_LONG_T = 8192
 
 _lib = None
 
@@ -129,9 +129,22 @@ def _invoke(fn: str, dev: torch.device, *args):
     _check(fn, rc)
 
 
-def _opt(t, name, dtype, shape, dev):
+def _alloc(shape, dtype, dev, stream):
+    """A new device tensor for an output or scratch buffer of a call that
+    enqueues on ``stream``.  torch's caching allocator ties a block to the
+    stream current at allocation; when the call runs on another stream, the
+    block is also recorded on that one, so that it is not handed out again
+    (for instance once a dropped scratch tensor is freed) before the call's
+    kernels are done with it."""
+    t = torch.empty(shape, dtype=dtype, device=dev)
+    if stream is not None and stream != torch.cuda.current_stream(dev):
+        t.record_stream(stream)
+    return t
+
+
+def _opt(t, name, dtype, shape, dev, stream=None):
     if t is None:
-        return torch.empty(shape, dtype=dtype, device=dev)
+        return _alloc(shape, dtype, dev, stream)
     return _dev(t, name, dtype, shape)
 
 
@@ -148,10 +161,10 @@ def _verify(fn, q, k, v, a, beta, S0, parent, o, u, logp, factors, status, strea
     _dev(beta, "beta", torch.float32, (B, T, H))
     _dev(S0, "S0", torch.float32, (B, H, dv, dk))
     dev = q.device
-    o = _opt(o, "o", torch.float32, (B, T, H, dv), dev)
+    o = _opt(o, "o", torch.float32, (B, T, H, dv), dev, stream)
     if factors:
-        u = _opt(u, "u", torch.float32, (B, T, H, dv), dev)
-        logp = _opt(logp, "logp", torch.float32, (B, T, H), dev)
+        u = _opt(u, "u", torch.float32, (B, T, H, dv), dev, stream)
+        logp = _opt(logp, "logp", torch.float32, (B, T, H), dev, stream)
     else:
         u = logp = None
     if status is not None:
@@ -202,11 +215,11 @@ def verify_chain_long(q, k, v, a, beta, S0, o=None, u=None, logp=None, S_work=No
     _dev(beta, "beta", torch.float32, (B, T, H))
     _dev(S0, "S0", torch.float32, (B, H, dv, dk))
     dev = q.device
-    o = _opt(o, "o", torch.float32, (B, T, H, dv), dev)
-    u = _opt(u, "u", torch.float32, (B, T, H, dv), dev)
-    logp = _opt(logp, "logp", torch.float32, (B, T, H), dev)
+    o = _opt(o, "o", torch.float32, (B, T, H, dv), dev, stream)
+    u = _opt(u, "u", torch.float32, (B, T, H, dv), dev, stream)
+    logp = _opt(logp, "logp", torch.float32, (B, T, H), dev, stream)
     if S_work is None and T > MAX_T:
-        S_work = torch.empty((B, H, dv, dk), dtype=torch.float32, device=dev)
+        S_work = _alloc((B, H, dv, dk), torch.float32, dev, stream)
     elif S_work is not None:
         _dev(S_work, "S_work", torch.float32, (B, H, dv, dk))
     if status is not None:
@@ -236,7 +249,7 @@ def commit_state(k, u, logp, accepted, S0, S_out=None, parent=None, status=None,
     _dev(S0, "S0", torch.float32, (B, H, dv, dk))
     if parent is not None:
         _dev(parent, "parent", torch.int32, (B, T))
-    S_out = _opt(S_out, "S_out", torch.float32, (B, H, dv, dk), k.device)
+    S_out = _opt(S_out, "S_out", torch.float32, (B, H, dv, dk), k.device, stream)
     if S_out.data_ptr() != S0.data_ptr():
         lo0, hi0 = S0.data_ptr(), S0.data_ptr() + S0.numel() * 4
         lo1, hi1 = S_out.data_ptr(), S_out.data_ptr() + S_out.numel() * 4
@@ -271,11 +284,11 @@ def gather_states(pool, slot, queries=None, o=None, states_out=None, want_states
         if queries.dim() != 5 or tuple(queries.shape[:3]) != (B, P, H) or queries.shape[4] != dk:
             raise ValueError("queries must have shape [B, P, H, Qn, dk]")
         Qn = queries.shape[3]
-        o = _opt(o, "o", torch.float32, (B, P, H, Qn, dv), dev)
+        o = _opt(o, "o", torch.float32, (B, P, H, Qn, dv), dev, stream)
     else:
         o = None
     if states_out is None and want_states:
-        states_out = torch.empty((B, P, H, dv, dk), dtype=torch.float32, device=dev)
+        states_out = _alloc((B, P, H, dv, dk), torch.float32, dev, stream)
     elif states_out is not None:
         _dev(states_out, "states_out", torch.float32, (B, P, H, dv, dk))
     if status is not None:
@@ -314,7 +327,7 @@ def read_block_states(k, u, logp, S0, pos, queries, parent=None, o=None, status=
     Qn = queries.shape[3]
     if parent is not None:
         _dev(parent, "parent", torch.int32, (B, T))
-    o = _opt(o, "o", torch.float32, (B, P, H, Qn, dv), k.device)
+    o = _opt(o, "o", torch.float32, (B, P, H, Qn, dv), k.device, stream)
     if status is not None:
         _dev(status, "status", torch.int32)
     dev = k.device
@@ -424,17 +437,17 @@ def select_accepted(logits, tokens, parent=None, target=None, accepted=None, acc
     if parent is not None:
         _dev(parent, "parent", torch.int32, (B, T))
     dev = logits.device
-    target = _opt(target, "target", torch.int32, (B, T1), dev)
-    accepted = _opt(accepted, "accepted", torch.int32, (B,), dev)
-    accepted_len = _opt(accepted_len, "accepted_len", torch.int32, (B,), dev)
-    bonus = _opt(bonus, "bonus", torch.int32, (B,), dev)
+    target = _opt(target, "target", torch.int32, (B, T1), dev, stream)
+    accepted = _opt(accepted, "accepted", torch.int32, (B,), dev, stream)
+    accepted_len = _opt(accepted_len, "accepted_len", torch.int32, (B,), dev, stream)
+    bonus = _opt(bonus, "bonus", torch.int32, (B,), dev, stream)
     if status is not None:
         _dev(status, "status", torch.int32)
     ws_bytes = 0
     if split:
         need = select_workspace_bytes(B, T, V)
         if workspace is None and need > 0:
-            workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+            workspace = _alloc((need,), torch.uint8, dev, stream)
         if workspace is not None:
             _dev(workspace, "workspace", torch.uint8)
             ws_bytes = workspace.numel()

@@ -148,6 +148,10 @@ def pin_golden(orc):
     assert status == 0
     assert np.array_equal(o[0, :, 0, :], fr(g["o"])), (o[0, :, 0, :], fr(g["o"]))
     assert np.array_equal(st[0, :, 0], fr(g["states"]))
+    # log P_n: the log of the hand-worked gate products
+    lp, status = orc.log_decay(a, par)
+    assert status == 0
+    assert np.max(np.abs(lp[0, :, 0] - np.log(fr(g["P"])))) <= 1e-15, (lp[0, :, 0], fr(g["P"]))
     for n in range(-1, T):
         S, status = orc.commit(k, v, a, beta, S0, np.array([n], np.int32), par)
         assert status == 0
@@ -220,6 +224,37 @@ def pin_pure_decay(orc, seed=14, B=2, T=24, H=3, d=8, tol=1e-14):
                     P *= float(c["a"][b, m, h])
                 assert rel_err(st[b, n, h], P * S0) <= tol
                 assert rel_err(o[b, n, h], P * (S0 @ c["q"][b, n, h].astype(np.float64))) <= tol
+
+
+def pin_log_decay(orc, seed=26, B=3, T=20, H=4, d=4):
+    """log P_n against closed forms: a chain with one gate value per head has
+    log P_n = (n + 1) log a; on a tree, b = 0 makes every node state the
+    decayed committed state, S_n = P_n S0, so exp(log P_n) S0 must equal the
+    walk's state; and each node's value minus its parent's is log a_n."""
+    c = random_case(seed, B, T, H, d, d, "chain")
+    gate = np.array([0.5, 0.9, 0.25, 0.999], np.float32)[:H]
+    c["a"] = np.broadcast_to(gate, (B, T, H)).copy()
+    lp, status = orc.log_decay(c["a"], None)
+    assert status == 0
+    want = (np.arange(1, T + 1)[:, None] * np.log(gate.astype(np.float64))[None, :])[None]
+    assert np.max(np.abs(lp - want)) <= 1e-13 * np.max(np.abs(want))
+    t = random_case(seed + 1, B, T, H, d, d, "tree", beta=0.0)
+    lp, status = orc.log_decay(t["a"], t["parent"])
+    assert status == 0
+    _, st, status = orc.verify(**t, want_states=True)
+    assert status == 0
+    S0 = t["S0"].astype(np.float64)
+    assert rel_err(st, np.exp(lp)[..., None, None] * S0[:, None]) <= 1e-14
+    # a chain far past the fp64 range of the plain product (|log P| ~ 1e4)
+    long = (np.full((1, 20000, 1), 0.5, np.float32), 20000 * np.log(0.5))
+    lpl, status = orc.log_decay(long[0], None)
+    assert status == 0 and abs(lpl[0, -1, 0] - long[1]) <= 1e-12 * abs(long[1])
+    la = np.log(t["a"].astype(np.float64))
+    for b in range(B):
+        for n in range(T):
+            p = int(t["parent"][b, n])
+            base = lp[b, p] if p >= 0 else 0.0
+            assert np.max(np.abs(lp[b, n] - base - la[b, n])) <= 1e-12
 
 
 def pin_pure_read(orc, seed=15, B=2, T=12, H=2, d=16):
@@ -454,7 +489,7 @@ def pin_select_chain(orc, seed=24, B=16, T=10, V=50):
         assert np.array_equal(bonus, am[np.arange(B), run])
 
 
-ALL_PINS = [pin_golden, pin_closed_form, pin_commit_from_factors, pin_brute_force, pin_pure_decay,
+ALL_PINS = [pin_golden, pin_closed_form, pin_commit_from_factors, pin_brute_force, pin_pure_decay, pin_log_decay,
             pin_pure_read, pin_overwrite, pin_chain_equals_decode, pin_chunk_form, pin_tree_equals_dfs, pin_gather,
             pin_read_golden, pin_read_from_factors, pin_read_brute_force, pin_select_golden,
             pin_select_sets, pin_select_chain]

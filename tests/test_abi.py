@@ -75,7 +75,7 @@ def test_commit_argument_codes(lib):
     assert c(acc=None) == -1
     assert c(out=None) == -1
     assert c(S0=MIS) == -1
-    assert c(T=(1 << 20) + 1) == -2   # a chain may be long, but not beyond the limit
+    assert c(T=8192 + 1) == -2         # a chain may be long, but not beyond LDV_MAX_LONG_T
     assert c(B=0) == 0
 
 
@@ -124,7 +124,11 @@ def test_select_argument_codes(lib):
     assert s(lg=ctypes.c_void_p(0x10001)) == -1       # not element aligned
     assert s(dt=1, lg=ctypes.c_void_p(0x10002)) == -1
     assert s(T=65) == -2
-    assert s(B=0) == 0 and s(T=0) == 0
+    assert s(B=0) == 0 and s(B=0, T=0) == 0
+    # with no draft nodes (T = 0) row 0 is still read: logits, target and
+    # accepted are required, tokens are not
+    assert s(T=0, lg=None, tok=None) == -1 and s(T=0, tg=None, tok=None) == -1
+    assert s(T=0, acc=None, tok=None) == -1
     # the workspace: 8-byte aligned and at least the queried size when the rows are split
     need = lib.ldv_select_workspace_bytes(2, 4, 151936)
     assert need > 0 and need % 8 == 0
@@ -156,7 +160,7 @@ def test_verify_chain_long_argument_codes(lib):
     assert c(w=None) == -1                    # T > 64 needs the work state
     assert c(w=FAKE) == -1                    # overlaps S0
     assert c(w=MIS) == -1
-    assert c(T=(1 << 20) + 1) == -2
+    assert c(T=8192 + 1) == -2
     assert c(d=48) == -2
     assert c(H=1 << 17) == -2                 # a 64-node chunk of 2^17 heads: 4 GiB per view
     assert c(B=0) == 0 and c(T=0) == 0

@@ -41,7 +41,7 @@ def test_gather_grid(ldv, orc, D, Qn, qkv):
     ro, rs, s = orc.gather(pool, slot, qs)
     assert s == 0
     assert np.array_equal(S.cpu().numpy(), rs)
-    check("gather D%d Qn%d %s" % (D, Qn, qkv), o, ro)
+    check("gather D%d Qn%d %s" % (D, Qn, qkv), o, ro, slices=(0, 1, 2))
 
 
 def test_gather_copy_only_and_read_only(ldv, orc):
@@ -82,4 +82,4 @@ def test_gather_workload_full_size(ldv, orc):
     ro, rs, s = orc.gather(x["pool"], x["slot"], x["queries"])
     assert s == 0
     assert np.array_equal(S.cpu().numpy(), rs)
-    check("hybrid27b gather o", o, ro)
+    check("hybrid27b gather o", o, ro, slices=(0, 1, 2))

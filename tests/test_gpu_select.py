@@ -264,3 +264,20 @@ def test_select_specials_long_rows(ldv, orc, V, dtype, split):
     assert np.array_equal(tg, rt), "targets %s vs %s" % (tg.ravel()[:16], rt.ravel()[:16])
     assert np.array_equal(acc, racc) and np.array_equal(alen, ralen) and np.array_equal(bonus, rbonus)
     print("select specials V%d %s targets %s" % (V, dtype, tg.ravel().tolist()), flush=True)
+
+
+@pytest.mark.parametrize("V,dtype", [(32000, "bf16"), (151936, "bf16"), (1000, "f32")], ids=lambda v: str(v))
+def test_select_no_draft_nodes(ldv, orc, V, dtype):
+    """T = 0: only the committed position's row is read; nothing is accepted
+    (accepted -1, length 0) and the bonus token is that row's argmax, as in
+    the oracle.  No token array is needed."""
+    rng = np.random.default_rng(7900 + V)
+    B = 6
+    logits = rng.standard_normal((B, 1, V)).astype(np.float32)
+    if dtype == "bf16":
+        logits = bf16_round(logits)
+    tokens = np.zeros((B, 0), np.int32)
+    for split in (True, False):
+        compare(orc, ldv, logits, tokens, None, dtype, "T=0 V%d split %s" % (V, split), split=split)
+    (tg, acc, alen, bonus), _ = run(ldv, logits, tokens, None, dtype)
+    assert np.all(acc == -1) and np.all(alen == 0) and np.array_equal(bonus, tg[:, 0])

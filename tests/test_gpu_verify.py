@@ -3,7 +3,7 @@ import numpy as np
 import pytest
 
 import pins
-from gpu_util import DESIGN_TOL, TOL, check, dev, host, log_p, qkv_torch_dtype, to_device
+from gpu_util import DESIGN_TOL, TOL, check, check_logp, dev, host, qkv_torch_dtype, to_device
 from workloads import WORKLOADS, bf16_round, make_inputs
 
 torch = pytest.importorskip("torch")
@@ -33,7 +33,9 @@ def compare_verify(ldv, orc, x, qkv, chain, name):
     assert s == 0
     check(name + " o", o, ro)
     check(name + " u", u, ru)
-    check(name + " logp", lp, log_p(x["a"], x["parent"]), design_tol=1e-5)
+    rlp, s = orc.log_decay(x["a"], None if chain else x["parent"])
+    assert s == 0
+    check_logp(name + " logp", lp, rlp)
     # per (sequence, head) slices, so that a small head cannot hide behind a large one
     go, gu = host(o), host(u)
     for b in range(x["q"].shape[0]):

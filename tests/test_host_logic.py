@@ -60,13 +60,37 @@ def test_xcd_spread_is_a_bijection(tmp_path):
 
 def test_bench_algorithmic_bytes():
     """bench.py's algorithmic verify bytes: per head the state (64 KiB at
-    d = 128) and, per node, bf16 q/k/v (768), the gates (8), fp32 o and u
-    (1024) and log P (4): 79,968 bytes per head for a chain of 8.  A chain
-    longer than 64 nodes reads one base state per chunk and writes one per
-    chunk but the last."""
+    d = 128) and, per node, bf16 q/k/v (768) and the gates (8) read, fp32 o
+    and u (1024) and log P (4) written: 79,968 bytes per head for a chain of
+    8.  A chain longer than 64 nodes reads one base state per chunk and
+    writes one per chunk but the last.  Commit reads and writes the state of
+    each committing head and reads the path's u, k and log P."""
+    import numpy as np
+
     import bench
     from workloads import LONG_WORKLOADS, WORKLOADS, make_inputs
     wl = WORKLOADS["gdn1.3b-chain"].replace(B=2, H=3)
-    assert bench.algorithmic(wl, make_inputs(wl, with_gather=False))["verify"] == 2 * 3 * 79968
+    x = make_inputs(wl, with_gather=False)
+    alg, _ = bench.algorithmic(wl, x)
+    rd, wr = alg["verify"]
+    assert (rd, wr) == (2 * 3 * (65536 + 8 * 776), 2 * 3 * 8 * 1028) and rd + wr == 2 * 3 * 79968
+    x["accepted"] = np.array([3, -1], np.int32)  # one sequence commits node 3 (a path of 4 nodes)
+    alg, _ = bench.algorithmic(wl, x)
+    assert alg["commit"] == (3 * (65536 + 4 * (512 + 256 + 4)) + 2 * 4, 3 * 65536)
     wl = LONG_WORKLOADS["gdn1.3b-chain1024"].replace(B=1, H=2, T=130)  # three chunks
-    assert bench.algorithmic(wl, make_inputs(wl, with_gather=False))["verify"] == 2 * (5 * 65536 + 130 * 1804)
+    rd, wr = bench.algorithmic(wl, make_inputs(wl, with_gather=False))[0]["verify"]
+    assert rd + wr == 2 * (5 * 65536 + 130 * 1804) and rd == 2 * (3 * 65536 + 130 * 776)
+
+
+def test_bench_ceiling_choice():
+    """Each kernel is graded against the stream probe nearest its mix."""
+    import bench
+    peaks = {"read_GB_s": 7.0, "copy_GB_s": 6.0, "rmw_GB_s": 6.2, "read2write1_GB_s": 6.1,
+             "read4write1_GB_s": 6.3, "read8write1_GB_s": 6.4}
+    assert bench.ceiling_for(10, 10, True, peaks) == ("rmw_GB_s", 6.2)
+    assert bench.ceiling_for(10, 10, False, peaks)[0] == "copy_GB_s"
+    assert bench.ceiling_for(77952, 16448, False, peaks)[0] == "read4write1_GB_s"   # 27B-hybrid verify
+    assert bench.ceiling_for(69632, 8192, False, peaks)[0] == "read8write1_GB_s"    # gather
+    assert bench.ceiling_for(1000, 1, False, peaks)[0] == "read_GB_s"               # selection
+    assert bench.ceiling_for(1000, 0, False, peaks)[0] == "read_GB_s"
+    assert bench.ceiling_for(1, 1, False, None) == (None, None)

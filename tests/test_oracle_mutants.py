@@ -32,6 +32,12 @@ MUTANTS = {
         "walk_to(c, b, h, c->accepted[b] > 0 ? c->accepted[b] - 1 : c->accepted[b], S, x, path, NULL);"),
     "gather reads the state transposed": ("acc += (double)src[(size_t)r * c->dk + j] * (double)qv[j];",
                                           "acc += (double)src[(size_t)j * c->dk + r] * (double)qv[j];"),
+    "log decay leaves out the node's own gate": ("for (int i = 0; i < len; ++i) {\n                    int e;",
+                                                 "for (int i = 0; i < len - 1; ++i) {\n                    int e;"),
+    "log decay drops the exponent": ("logp[((size_t)b * T + n) * H + h] = log(P) + (double)e2 * log(2.0);",
+                                     "logp[((size_t)b * T + n) * H + h] = log(P);"),
+    "log decay walks a chain instead of the tree": ("int len = root_path(parent, T, b, n, path);",
+                                                    "int len = root_path(NULL, T, b, n, path);"),
     "gather pairs an output with the next query": (
         "const float* qv = c->queries + (((size_t)bp * c->H + h) * c->Qn + i) * c->dk;",
         "const float* qv = c->queries + (((size_t)bp * c->H + h) * c->Qn + (i + 1) % c->Qn) * c->dk;"),
