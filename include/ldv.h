@@ -302,6 +302,27 @@ int ldv_select_accepted(int B, int T, int V, int logits_dtype, const void* logit
                         int* status, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * ldv_select_accepted without a workspace argument and without any
+ * allocation, for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc).  It
+ * splits few, long rows exactly as ldv_select_accepted does when given a
+ * workspace, with the partial results in an array of the library instead: a
+ * fixed 48 KiB (6144 entries) per GPU, reserved on each GPU the library runs
+ * on until the process ends, its address resolved on the first call on that
+ * GPU.  Every split the selection makes fits it; a larger one would return
+ * LDV_ERR_UNSUPPORTED.  Results are those of ldv_select_accepted.  Every call
+ * on a GPU shares that GPU's array: calls that overlap on one GPU (on
+ * different streams, or from different host threads) race and must be
+ * ordered by the caller.  Arguments, checks and status bits are those of
+ * ldv_select_accepted; LDV_ERR_LAUNCH also reports a failure to resolve the
+ * array's address.  The caller still passes every output.
+ */
+int ldv_select_accepted_noalloc(int B, int T, int V, int logits_dtype, const void* logits,
+                                const int32_t* tokens, const int32_t* parent, int32_t* target,
+                                int32_t* accepted, int32_t* accepted_len, int32_t* bonus,
+                                int* status, void* stream);
+
+/*
  * Bytes of workspace ldv_select_accepted uses for B sequences of T nodes and
  * rows of V logits: 0 when it would not split the rows (then the workspace
  * may be NULL at no cost), and 0 for sizes the call rejects.

@@ -235,22 +235,45 @@ LDV_EXPORT size_t ldv_select_workspace_bytes(int B, int T, int V) {
     return np > 1 ? (size_t)rows * np * sizeof(ldv::ArgPart) : 0;
 }
 
-LDV_EXPORT int ldv_select_accepted(int B, int T, int V, int logits_dtype, const void* logits,
-                                   const int32_t* tokens, const int32_t* parent, int32_t* target,
-                                   int32_t* accepted, int32_t* accepted_len, int32_t* bonus, int* status,
-                                   void* workspace, size_t workspace_bytes, void* stream) {
+namespace {
+
+// Shared checks of the selection calls: 1 = proceed.
+int check_select(int B, int T, int V, int dt, const void* logits, const int32_t* tokens, const int32_t* parent,
+                 const int32_t* target, const int32_t* accepted, const int32_t* accepted_len, const int32_t* bonus,
+                 const int* status) {
     if (B < 0 || T < 0 || V <= 0) return LDV_ERR_ARG;
-    if (logits_dtype != LDV_BF16 && logits_dtype != LDV_F32) return LDV_ERR_ARG;
+    if (dt != LDV_BF16 && dt != LDV_F32) return LDV_ERR_ARG;
     if (T > LDV_MAX_T) return LDV_ERR_UNSUPPORTED;
     if (B == 0) return LDV_OK;
     // T = 0 (no draft nodes): row 0 is still read, nothing is accepted and
     // the bonus token is row 0's argmax; tokens may then be NULL
     if (!logits || (T > 0 && !tokens) || !target || !accepted) return LDV_ERR_ARG;
-    if (!aligned(logits, logits_dtype == LDV_F32 ? 4 : 2) || !aligned(tokens, 4) || !aligned(parent, 4) ||
+    if (!aligned(logits, dt == LDV_F32 ? 4 : 2) || !aligned(tokens, 4) || !aligned(parent, 4) ||
         !aligned(target, 4) || !aligned(accepted, 4) || !aligned(accepted_len, 4) || !aligned(bonus, 4) ||
         !aligned(status, 4))
         return LDV_ERR_ARG;
     if (!grid_fits((long long)B * (T + 1), 512)) return LDV_ERR_UNSUPPORTED;
+    return 1;
+}
+
+int select_launch(int B, int T, int V, int dt, const void* logits, const int32_t* tokens, const int32_t* parent,
+                  int32_t* target, int32_t* accepted, int32_t* accepted_len, int32_t* bonus, int* status, int np,
+                  ldv::ArgPart* part, void* stream) {
+    if (!grid_fits((long long)B * (T + 1) * np, 512)) return LDV_ERR_UNSUPPORTED;
+    ldv::SelectArgs args{B, T, V, logits, tokens, parent, target, accepted, accepted_len, bonus, status, np, part};
+    hipError_t e = ldv::launch_select(args, dt == LDV_F32, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? LDV_OK : LDV_ERR_LAUNCH;
+}
+
+}  // namespace
+
+LDV_EXPORT int ldv_select_accepted(int B, int T, int V, int logits_dtype, const void* logits,
+                                   const int32_t* tokens, const int32_t* parent, int32_t* target,
+                                   int32_t* accepted, int32_t* accepted_len, int32_t* bonus, int* status,
+                                   void* workspace, size_t workspace_bytes, void* stream) {
+    const int rc = check_select(B, T, V, logits_dtype, logits, tokens, parent, target, accepted, accepted_len, bonus,
+                                status);
+    if (rc != 1) return rc;
     // with a workspace, rows may be split over several workgroups
     const long long rows = (long long)B * (T + 1);
     int np = 1;
@@ -262,11 +285,28 @@ LDV_EXPORT int ldv_select_accepted(int B, int T, int V, int logits_dtype, const 
             np = want;
         }
     }
-    if (!grid_fits(rows * np, 512)) return LDV_ERR_UNSUPPORTED;
-    ldv::SelectArgs args{B, T, V, logits, tokens, parent, target, accepted, accepted_len, bonus, status, np,
-                         static_cast<ldv::ArgPart*>(workspace)};
-    hipError_t e = ldv::launch_select(args, logits_dtype == LDV_F32, static_cast<hipStream_t>(stream));
-    return e == hipSuccess ? LDV_OK : LDV_ERR_LAUNCH;
+    return select_launch(B, T, V, logits_dtype, logits, tokens, parent, target, accepted, accepted_len, bonus, status,
+                         np, static_cast<ldv::ArgPart*>(workspace), stream);
+}
+
+LDV_EXPORT int ldv_select_accepted_noalloc(int B, int T, int V, int logits_dtype, const void* logits,
+                                           const int32_t* tokens, const int32_t* parent, int32_t* target,
+                                           int32_t* accepted, int32_t* accepted_len, int32_t* bonus, int* status,
+                                           void* stream) {
+    const int rc = check_select(B, T, V, logits_dtype, logits, tokens, parent, target, accepted, accepted_len, bonus,
+                                status);
+    if (rc != 1) return rc;
+    // rows split exactly as ldv_select_accepted splits them with a workspace,
+    // the partial results in the library's own array
+    const long long rows = (long long)B * (T + 1);
+    const int np = ldv::select_parts(rows, V);
+    ldv::ArgPart* part = nullptr;
+    if (np > 1) {
+        if (rows * np > ldv::kSelectScratchParts) return LDV_ERR_UNSUPPORTED;  // beyond the array (no valid split is)
+        if (ldv::select_scratch(&part) != hipSuccess) return LDV_ERR_LAUNCH;
+    }
+    return select_launch(B, T, V, logits_dtype, logits, tokens, parent, target, accepted, accepted_len, bonus, status,
+                         np, part, stream);
 }
 
 LDV_EXPORT const char* ldv_status_string(int code) {

@@ -110,6 +110,14 @@ struct SelectArgs {
 // the caller provides the workspace for the partial results (1 otherwise).
 int select_parts(long long rows, int V);
 
+// Entries of the library's own split-row workspace (ldv_select_accepted_noalloc):
+// every split select_parts makes fits (fewer than 2048 rows, at most
+// ceil(4096 / rows) parts each).
+constexpr long long kSelectScratchParts = 6144;
+
+// The current GPU's address of that workspace (resolved once per device).
+hipError_t select_scratch(ArgPart** out);
+
 // Each launcher assumes arguments already validated by the C ABI layer and
 // returns the HIP launch status.
 hipError_t launch_verify(const VerifyArgs& a, bool f32_inputs, hipStream_t stream);

@@ -36,6 +36,8 @@
 //      combines row r's parts under the same rule and writes target.
 #include <limits.h>
 
+#include <mutex>
+
 #include "ldv_device.hpp"
 #include "ldv_kernels.hpp"
 
@@ -69,6 +71,43 @@ int select_parts(long long rows, int V) {
     long long np = (kArgSplitBlocks + rows - 1) / rows;
     if (np > V / kArgMinPart) np = V / kArgMinPart;
     return np < 1 ? 1 : (int)np;
+}
+
+// The split-row partial results of ldv_select_accepted_noalloc, for callers
+// that cannot allocate: a fixed array of the library, one copy per GPU, held
+// until the process ends.  Rows are split only when there are fewer than
+// kArgSplitRows of them, into at most ceil(kArgSplitBlocks / rows) parts, so
+// a call never needs more than kSelectScratchParts entries (48 KiB).  Every
+// call on a GPU uses that GPU's array: calls that overlap on one GPU (on
+// different streams) race.  No entry needs to start at any value (each part
+// writes its entry before the walk kernel reads it), so nothing is cleared.
+static_assert(kSelectScratchParts >= kArgSplitBlocks + kArgSplitRows - 1, "scratch smaller than a split");
+static __device__ __align__(256) ArgPart scratch[kSelectScratchParts];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+ArgPart* g_scratch_ptr[kMaxDevices];  // the array's device address on each GPU (null: not resolved yet)
+}  // namespace
+
+// In host code `scratch` names a host-side handle, not device memory: its
+// device address on the current GPU is resolved once per device, with that
+// device current, and only that address is handed to kernels.
+hipError_t select_scratch(ArgPart** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        g_scratch_ptr[dev] = static_cast<ArgPart*>(p);
+    }
+    *out = g_scratch_ptr[dev];
+    return hipSuccess;
 }
 
 // (v, i) replaces (bv, bi) when v is larger, or equal with a lower index;

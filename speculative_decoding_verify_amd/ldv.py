@@ -54,11 +54,12 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.ldv_read_block_states_packed.argtypes = [i, i, i, i, i, i, i, i, vp, fp, fp, ip, fp, ip, vp, vp, ll, ll, i,
                                                  ip, vp]
     lib.ldv_select_accepted.argtypes = [i, i, i, i, vp, ip, ip, ip, ip, ip, ip, ip, vp, ctypes.c_size_t, vp]
+    lib.ldv_select_accepted_noalloc.argtypes = [i, i, i, i, vp, ip, ip, ip, ip, ip, ip, ip, vp]
     lib.ldv_select_workspace_bytes.argtypes = [i, i, i]
     lib.ldv_select_workspace_bytes.restype = ctypes.c_size_t
     for f in ("ldv_verify_tree", "ldv_verify_chain", "ldv_verify_chain_long", "ldv_commit_state", "ldv_gather_states",
               "ldv_read_block_states", "ldv_gather_states_packed", "ldv_read_block_states_packed",
-              "ldv_select_accepted", "ldv_version"):
+              "ldv_select_accepted", "ldv_select_accepted_noalloc", "ldv_version"):
         getattr(lib, f).restype = ctypes.c_int
     lib.ldv_status_string.argtypes = [ctypes.c_int]
     lib.ldv_status_string.restype = ctypes.c_char_p
@@ -459,6 +460,41 @@ def select_accepted(logits, tokens, parent=None, target=None, accepted=None, acc
             B, T, V, code, _ptr(logits), _ptr(tokens), _ptr(parent), _ptr(target), _ptr(accepted),
             _ptr(accepted_len), _ptr(bonus), _ptr(status), _ptr(workspace), ctypes.c_size_t(ws_bytes),
             _stream(stream, dev))
+    return target, accepted, accepted_len, bonus
+
+
+def select_accepted_noalloc(logits, tokens, target, accepted, parent=None, accepted_len=None, bonus=None,
+                            status=None, stream=None):
+    """select_accepted through the entry point that allocates nothing: rows
+    are split as select_accepted splits them with a workspace, the partial
+    results in the library's own per-GPU array.  Every output is the
+    caller's (target [B, T+1] and accepted [B] int32 required, accepted_len
+    and bonus [B] int32 optional), so that the call allocates nothing; calls
+    that overlap on one GPU race.  Returns (target, accepted, accepted_len,
+    bonus)."""
+    _dev(logits, "logits")
+    if logits.dim() != 3:
+        raise ValueError("logits must have shape [B, T+1, V]")
+    B, T1, V = logits.shape
+    T = T1 - 1
+    code = _qkv_code(logits)
+    _dev(tokens, "tokens", torch.int32, (B, T))
+    if parent is not None:
+        _dev(parent, "parent", torch.int32, (B, T))
+    _dev(target, "target", torch.int32, (B, T1))
+    _dev(accepted, "accepted", torch.int32, (B,))
+    if accepted_len is not None:
+        _dev(accepted_len, "accepted_len", torch.int32, (B,))
+    if bonus is not None:
+        _dev(bonus, "bonus", torch.int32, (B,))
+    if status is not None:
+        _dev(status, "status", torch.int32)
+    dev = logits.device
+    _same_device(dev, tokens=tokens, parent=parent, target=target, accepted=accepted,
+                 accepted_len=accepted_len, bonus=bonus, status=status)
+    _invoke("ldv_select_accepted_noalloc", dev,
+            B, T, V, code, _ptr(logits), _ptr(tokens), _ptr(parent), _ptr(target), _ptr(accepted),
+            _ptr(accepted_len), _ptr(bonus), _ptr(status), _stream(stream, dev))
     return target, accepted, accepted_len, bonus
 
 
