@@ -8,14 +8,19 @@
 //   states_out[b, p, h] = pool[s, h]  (optional bit copy).
 //
 // One block of four waves per 64 rows of a (sequence, position, head) state
-// (two blocks per state at d = 128: small blocks with few registers keep more
-// loads in flight per CU).  Each wave loads its 16-row block of the fp32
-// state straight into MFMA A-operand registers (64 contiguous bytes per row
-// per load), writes the copy from the same registers, and multiplies by the
-// queries on MFMA with the state split into bf16 hi + lo terms.  The o tile
-// of the block goes through LDS, so that every store instruction writes whole
-// rows of o (measured 5% faster for bf16 outputs, 1.5% for fp32).  The read
-// of the 64 KiB state dominates: the kernel is bound by HBM.
+// (two blocks per state at d = 128: small blocks keep more loads in flight
+// per CU).  Each wave's 16 rows of the fp32 state are 8 KiB of consecutive
+// bytes at d = 128; the wave reads them with non-temporal loads of which
+// each covers 1 KiB (whole 128-byte lines), writes the optional copy from the
+// same registers, and passes them through LDS into the MFMA operand layout
+// (lane (c, g) holds row c).  Loading the operands straight from memory, as
+// before, made every load instruction cover only 64-byte halves of lines:
+// measured 119.1 us against 103.1 us now on the 27B-hybrid shape (106.4 us
+// with ordinary loads in the new form).  o = S q is formed on MFMA with the
+// state split into bf16 hi + lo terms; the o tile of the block goes through
+// LDS, so that every store instruction writes whole rows of o (measured 5%
+// faster for bf16 outputs, 1.5% for fp32).  The read of the 64 KiB state
+// dominates: the kernel is bound by HBM.
 #include "ldv_device.hpp"
 #include "ldv_kernels.hpp"
 
@@ -35,9 +40,12 @@ struct GShape {
 template <int D, bool F32Q>
 __global__ __launch_bounds__((GShape<D>::NWA * kWave)) void gather_kernel(const GatherArgs p) {
     using S = GShape<D>;
-    constexpr int NWA = S::NWA, MBW = S::MBW, KS = S::KS;
-    constexpr int RB = NWA * MBW * 16;  // state rows per block
-    __shared__ __align__(16) float s_o[16][RB + 4];  // padded: the 16 query rows start on different banks
+    constexpr int NWA = S::NWA, KS = S::KS;
+    constexpr int RB = NWA * 16;        // state rows per block
+    constexpr int SP = D + 4;           // padded LDS row of the state tile (floats)
+    constexpr int NL = 16 * D / 4 / kWave > 0 ? 16 * D / 4 / kWave : 1;  // float4 per lane of a wave's 16 rows
+    __shared__ __align__(16) float s_st[NWA][16 * SP];  // each wave's 16 state rows
+    __shared__ __align__(16) float s_o[16][RB + 4];     // padded: the 16 query rows start on different banks
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int c = lane & 15, g = lane >> 4;
     const int H = p.H;
@@ -54,7 +62,8 @@ __global__ __launch_bounds__((GShape<D>::NWA * kWave)) void gather_kernel(const 
         if (tid == 0 && p.status && h == 0 && part == 0) atomicOr(p.status, LDV_STATUS_BAD_SLOT);
         return;
     }
-    const float* src = p.pool + ((size_t)s * H + h) * D * D;
+    const size_t row0 = (size_t)(part * NWA + wave) * 16;  // the wave's first state row
+    const float* src = p.pool + ((size_t)s * H + h) * D * D + row0 * D;
     const bool reads = p.queries && p.o.base && p.Qn > 0;
     const size_t qo_base = ((size_t)bp * H + h) * (size_t)p.Qn;           // queries row of query 0
     const size_t o_base = bp * p.o.ld + p.o.col + (size_t)h * p.Qn * D;  // o element of query 0
@@ -81,33 +90,40 @@ __global__ __launch_bounds__((GShape<D>::NWA * kWave)) void gather_kernel(const 
             }
         }
     }
-    float4 st[MBW][KS][2];
+    // the wave's 16 rows are 16 * D consecutive floats: each load instruction
+    // covers 1 KiB of them (whole lines), read non-temporally
+    float4 v[NL];
 #pragma unroll
-    for (int mi = 0; mi < MBW; ++mi) {
-        const int row = ((part * NWA + wave) * MBW + mi) * 16 + c;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            const int k0 = 32 * ks + 4 * g;
-            st[mi][ks][0] = (k0 < D) ? ld_stream(src + (size_t)row * D + k0) : make_float4(0.f, 0.f, 0.f, 0.f);
-            st[mi][ks][1] = (k0 + 16 < D) ? ld_stream(src + (size_t)row * D + k0 + 16)
-                                          : make_float4(0.f, 0.f, 0.f, 0.f);
-        }
+    for (int i = 0; i < NL; ++i) {
+        const int e = 4 * (lane + kWave * i);
+        if (16 * D >= 4 * kWave || e < 16 * D) v[i] = ld_nt(src + e);
     }
     asm volatile("" ::: "memory");  // keep the loads above ahead of any use of them
-    if (p.states_out) {
-        float* dst = p.states_out + ((size_t)bp * H + h) * D * D;
+    if (p.states_out) {  // the bit copy, from the same registers, whole lines per store
+        float* dst = p.states_out + ((size_t)bp * H + h) * D * D + row0 * D;
 #pragma unroll
-        for (int mi = 0; mi < MBW; ++mi) {
-            const int row = ((part * NWA + wave) * MBW + mi) * 16 + c;
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                const int k0 = 32 * ks + 4 * g;
-                if (k0 < D) st_stream(dst + (size_t)row * D + k0, st[mi][ks][0]);
-                if (k0 + 16 < D) st_stream(dst + (size_t)row * D + k0 + 16, st[mi][ks][1]);
-            }
+        for (int i = 0; i < NL; ++i) {
+            const int e = 4 * (lane + kWave * i);
+            if (16 * D >= 4 * kWave || e < 16 * D) st_stream(dst + e, v[i]);
         }
     }
     if (!reads) return;
+    // through LDS into the MFMA operand layout: lane (c, g) takes row c
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+        const int e = 4 * (lane + kWave * i);
+        if (16 * D >= 4 * kWave || e < 16 * D)
+            *reinterpret_cast<float4*>(&s_st[wave][(e / D) * SP + e % D]) = v[i];
+    }
+    __syncthreads();
+    float4 st[KS][2];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+        const int k0 = 32 * ks + 4 * g;
+        st[ks][0] = (k0 < D) ? *reinterpret_cast<const float4*>(&s_st[wave][c * SP + k0]) : make_float4(0.f, 0.f, 0.f, 0.f);
+        st[ks][1] = (k0 + 16 < D) ? *reinterpret_cast<const float4*>(&s_st[wave][c * SP + k0 + 16])
+                                  : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
 
     for (int nb = 0; nb * 16 < p.Qn; ++nb) {
         const int col = nb * 16 + c;  // query index held by this lane
@@ -128,9 +144,7 @@ __global__ __launch_bounds__((GShape<D>::NWA * kWave)) void gather_kernel(const 
                 }
             }
         }
-        floatx4 acc[MBW];
-#pragma unroll
-        for (int mi = 0; mi < MBW; ++mi) acc[mi] = floatx4{0.f, 0.f, 0.f, 0.f};
+        floatx4 acc = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             const int k0 = 32 * ks + 4 * g;
@@ -145,25 +159,21 @@ __global__ __launch_bounds__((GShape<D>::NWA * kWave)) void gather_kernel(const 
             } else {
                 bq = join((cval && k0 < D) ? qc[ks][0] : zero4(), (cval && k0 + 16 < D) ? qc[ks][1] : zero4());
             }
-#pragma unroll
-            for (int mi = 0; mi < MBW; ++mi) {
-                u16x4 h0, l0, h1, l1;
-                split4(st[mi][ks][0], h0, l0);
-                split4(st[mi][ks][1], h1, l1);
-                const bf16x8 ah = join(h0, h1), al = join(l0, l1);
-                acc[mi] = mfma16x16x32(ah, bq, acc[mi]);
-                acc[mi] = mfma16x16x32(al, bq, acc[mi]);
-                if constexpr (F32Q) acc[mi] = mfma16x16x32(ah, bql, acc[mi]);
-            }
+            u16x4 h0, l0, h1, l1;
+            split4(st[ks][0], h0, l0);
+            split4(st[ks][1], h1, l1);
+            const bf16x8 ah = join(h0, h1), al = join(l0, l1);
+            acc = mfma16x16x32(ah, bq, acc);
+            acc = mfma16x16x32(al, bq, acc);
+            if constexpr (F32Q) acc = mfma16x16x32(ah, bql, acc);
         }
         // the block's o tile (16 queries x RB rows) goes through LDS, so that
         // each store instruction covers whole rows of o: 16 consecutive lanes
         // write one query's RB values
         __syncthreads();  // the previous query block's tile has been stored
-#pragma unroll
-        for (int mi = 0; mi < MBW; ++mi) {
-            const int r0 = (wave * MBW + mi) * 16 + 4 * g;
-            *reinterpret_cast<float4*>(&s_o[c][r0]) = make_float4(acc[mi][0], acc[mi][1], acc[mi][2], acc[mi][3]);
+        {
+            const int r0 = wave * 16 + 4 * g;
+            *reinterpret_cast<float4*>(&s_o[c][r0]) = make_float4(acc[0], acc[1], acc[2], acc[3]);
         }
         __syncthreads();
         for (int j = tid; j < 16 * (RB / 4); j += NWA * kWave) {

@@ -98,13 +98,14 @@ __device__ __forceinline__ floatx4 mma3(floatx4 acc, bf16x8 ah, bf16x8 al, bf16x
 // write stream with the read stream at less loss.  Reads depend on their
 // pattern:
 //   - ld_nt, a non-temporal load, where each wave load covers whole
-//     contiguous 128-byte lines (commit's state rows, the logits): measured
-//     7-13% faster than ordinary loads on MI355X (commit 36.2 -> 33.7 us on
-//     the 27B-hybrid shape, 197.9 -> 175.3 us on batch-256);
+//     contiguous 128-byte lines (commit's state rows, the gather's state
+//     rows before their LDS transpose, the logits): measured 7-13% faster
+//     than ordinary loads on MI355X (commit 36.2 -> 33.7 us on the
+//     27B-hybrid shape, 197.9 -> 175.3 us on batch-256);
 //   - ld_stream, an ordinary load, where each load instruction covers 64-byte
 //     halves of lines (state rows loaded straight into MFMA operand
-//     registers): non-temporal loads measured 12% slower there in the gather
-//     and no faster in verify and the in-block read.
+//     registers): non-temporal loads measured no faster there in verify and
+//     the in-block read, and 12% slower in a gather of that form.
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float4 ld_stream(const float* p) { return *reinterpret_cast<const float4*>(p); }

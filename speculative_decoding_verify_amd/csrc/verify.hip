@@ -173,8 +173,17 @@ struct VLds {
     static constexpr size_t stage = STG ? (size_t)2 * 16 * SLD * 4 : 0;
     static constexpr bool own = S::NBM > 1 && qk < stage;
     static constexpr size_t off_stg = own ? (off_i + 16 + 15) / 16 * 16 : 0;
-    static constexpr size_t total =
-        own ? off_stg + stage : (S::NBM > 1 || off_i + 16 > stage ? off_i + 16 : stage);
+    // S0 rows through LDS (16- and 32-node kernels at d = 128, bf16 inputs): each wave's
+    // rows, S0C columns at a time (two passes with one row block per wave,
+    // four with two, so that three 32-node blocks still fit a CU); the
+    // staged outputs may overlay this area (S0 is used up by then)
+    static constexpr bool cs0 = D == 128 && !F32IN && (TM == 16 || TM == 32);
+    static constexpr int S0C = S::MBW == 1 ? 64 : 32;  // columns per pass
+    static constexpr int S0LD = S0C + 4;                // padded LDS row (floats)
+    static constexpr size_t end_i = own ? off_stg + stage : off_i + 16;
+    static constexpr size_t off_s0 = (end_i + 15) / 16 * 16;
+    static constexpr size_t end_s0 = cs0 ? off_s0 + (size_t)S::NW * 16 * S::MBW * S0LD * 4 : end_i;
+    static constexpr size_t total = (own || S::NBM > 1 || end_s0 > stage) ? end_s0 : stage;
     // waves per SIMD that the registers must allow: the shape's target, or
     // fewer where this block's LDS (160 KiB per CU) already caps residency
     static constexpr int lds_waves = (int)(163840 / total) * S::NW / 4;
@@ -315,7 +324,20 @@ __attribute__((amdgpu_waves_per_eu(VLds<D, TM, F32IN, STG>::WPE))) void verify_k
         // (one row block is written without the row-block loop: with it the
         // compiler's allocation of the 64-node kernel spills)
         float4 sreg[MBW][KS][2];
-        {
+        // 16 and 32 nodes at d = 128: the wave's 16 MBW rows are 8 MBW KiB of
+        // consecutive bytes, read with non-temporal loads that each cover 1 KiB
+        // (whole lines), and put into the operand layout through LDS before
+        // step 4 (verify 36.7 -> 33.6 us on the 27B-hybrid shape); loading the
+        // operand layout straight from memory covers 64-byte halves of lines
+        // per load
+        constexpr bool CS0 = L::cs0 && !CMT;
+        constexpr int NS0 = CS0 ? 8 * MBW : 1;
+        float4 s0c[NS0];  // float4 lane + 64 i of the wave's rows: row 2 i + lane / 32, columns 4 (lane % 32) ..
+        if constexpr (CS0) {
+            const float* wsrc = p.S0 + (((size_t)b * H + h) * D + vrow0) * D;
+    #pragma unroll
+            for (int i = 0; i < NS0; ++i) s0c[i] = ld_nt(wsrc + 4 * (lane + kWave * i));
+        } else {
             const buf_t bs = make_buf(p.S0 + (((size_t)b * H + h) * D + vrow0) * D, 16u * MBW * D * 4);
             const uint32_t soff = (uint32_t)(c * D + 4 * g) * 4;
             const float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -537,6 +559,37 @@ __attribute__((amdgpu_waves_per_eu(VLds<D, TM, F32IN, STG>::WPE))) void verify_k
         //    (and the registers to spare) each k-step splits its own S0
         //    registers, so the S0 loads are waited for one step at a time.  (The
         //    other orders make the compiler spill.)
+        if constexpr (CS0) {
+            // lane (c, g) takes row c of each row block, S0C columns per pass:
+            // the lanes holding the pass's columns write them, every lane
+            // reads its operands back (wave-local: the wave's own rows)
+            constexpr int S0C = L::S0C, S0LD = L::S0LD, LPP = S0C / 4;  // lanes (mod 32) per pass
+            float* s0t = reinterpret_cast<float*>(smem + L::off_s0) + wave * 16 * MBW * S0LD;
+    #pragma unroll
+            for (int ps = 0; ps < D / S0C; ++ps) {
+                if ((lane & 31) / LPP == ps) {
+    #pragma unroll
+                    for (int i = 0; i < NS0; ++i)
+                        *reinterpret_cast<float4*>(&s0t[(2 * i + (lane >> 5)) * S0LD + 4 * (lane & 31) - S0C * ps]) =
+                            s0c[i];
+                }
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                __builtin_amdgcn_wave_barrier();
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    #pragma unroll
+                for (int s = ps * S0C / 32; s < (ps + 1) * S0C / 32; ++s) {
+                    const int k = 32 * s + 4 * g - S0C * ps;
+    #pragma unroll
+                    for (int mi = 0; mi < MBW; ++mi) {
+                        sreg[mi][s][0] = *reinterpret_cast<const float4*>(&s0t[(16 * mi + c) * S0LD + k]);
+                        sreg[mi][s][1] = *reinterpret_cast<const float4*>(&s0t[(16 * mi + c) * S0LD + k + 16]);
+                    }
+                }
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                __builtin_amdgcn_wave_barrier();
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            }
+        }
         bf16x8 sh[MBW][KS], sl[MBW][KS];
         floatx4 acck[MBW][NBM];
         if constexpr (MBW > 1) {
