@@ -38,7 +38,8 @@
  *   - Supported sizes: d_k == d_v in {16, 32, 64, 128}; 1 <= T <= 64.
  *   - One launch holds at most 2^32 - 1 work-items (the dispatch grid size
  *     is 32 bits), so B * H <= 2^23 - 1 for verify, B * H <= 2^22 - 1 for
- *     commit and long chains, B * P * H <= 2^23 - 1 for the gathers,
+ *     long chains, B * H <= 2^21 - 1 for commit, B * P * H <= 2^23 - 1 for
+ *     the gathers,
  *     B * H * ceil(P * Qn / 64) <= 2^23 - 1 for the in-block reads and
  *     B * (T + 1) <= 2^23 - 1 for selection; larger shapes return
  *     LDV_ERR_UNSUPPORTED.

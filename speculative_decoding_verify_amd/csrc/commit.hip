@@ -16,8 +16,8 @@
 //
 // The work is a streaming read of S0 and write of S_out (64 KiB each per head
 // at d = 128), so it is bound by HBM.  One block of 256 threads per
-// (sequence, head, row block of up to 16 KiB; small blocks keep more of them
-// in flight per CU, measured 2-3 % faster than 32 KiB); each thread owns
+// (sequence, head, row block of 8 KiB, or 16 KiB where that alone makes the
+// grid one round of resident blocks; see launch_t); each thread owns
 // float4 chunks of consecutive columns so that every wave reads and writes
 // contiguous 1 KiB runs, so the state is read with non-temporal loads
 // (whole lines, used once).  The block loads the parent row, then its S0 rows; walks the parent
@@ -32,20 +32,21 @@
 
 namespace ldv {
 
-template <int D>
+// EMAX: float4 per block at most (512: 8 KiB row blocks, 1024: 16 KiB)
+template <int D, int EMAX>
 struct CShape {
     static constexpr int NTHR = 256;
     static constexpr int C4 = D / 4;                                  // float4 per state row (divides NTHR)
-    static constexpr int E4 = (D * D / 4 < 1024) ? D * D / 4 : 1024;  // float4 per block (<= 16 KiB)
+    static constexpr int E4 = (D * D / 4 < EMAX) ? D * D / 4 : EMAX;  // float4 per block
     static constexpr int RB = E4 / C4;                                // rows per block
     static constexpr int NRB = D / RB;                                // row blocks per head
     static constexpr int F4 = (E4 + NTHR - 1) / NTHR;                 // float4 per thread
     static constexpr int PCH = 16;                                    // path nodes staged per pass
 };
 
-template <int D, bool F32K>
+template <int D, bool F32K, int EMAX>
 __global__ __launch_bounds__(256) void commit_kernel(const CommitArgs p) {
-    using S = CShape<D>;
+    using S = CShape<D, EMAX>;
     constexpr int C4 = S::C4, E4 = S::E4, RB = S::RB, F4 = S::F4, NTHR = S::NTHR, PCH = S::PCH;
     constexpr int KI = (PCH * C4 + NTHR - 1) / NTHR;  // k chunks staged per thread and pass
     constexpr int UI = (PCH * RB + NTHR - 1) / NTHR;  // u values staged per thread and pass
@@ -189,12 +190,27 @@ __global__ __launch_bounds__(256) void commit_kernel(const CommitArgs p) {
     }
 }
 
+// Resident 256-thread commit blocks per CU (8 waves per SIMD).
+constexpr long long kCommitBlocksPerCu = 8;
+
+template <int D, bool F32K, int EMAX>
+static hipError_t launch_e(const CommitArgs& a, hipStream_t st) {
+    const long long nblk = (long long)a.B * a.H * CShape<D, EMAX>::NRB;
+    if (nblk <= 0) return hipSuccess;
+    hipLaunchKernelGGL((commit_kernel<D, F32K, EMAX>), dim3((unsigned)nblk), dim3(CShape<D, EMAX>::NTHR), 0, st, a);
+    return hipGetLastError();
+}
+
+// 8 KiB row blocks keep more loads in flight per CU than 16 KiB ones and
+// measured faster (27B-hybrid 33.6 -> 30.9 us, batch-256 175.3 -> 163.7 us,
+// GDN-1.3B 5.8 -> 5.3 us), except where the 16 KiB grid is one round of
+// resident blocks and the 8 KiB grid would need two (tree-64: 8.1 vs 9.5 us).
 template <int D, bool F32K>
 static hipError_t launch_t(const CommitArgs& a, hipStream_t st) {
-    const long long nblk = (long long)a.B * a.H * CShape<D>::NRB;
-    if (nblk <= 0) return hipSuccess;
-    hipLaunchKernelGGL((commit_kernel<D, F32K>), dim3((unsigned)nblk), dim3(CShape<D>::NTHR), 0, st, a);
-    return hipGetLastError();
+    const long long heads = (long long)a.B * a.H, round = kCommitBlocksPerCu * kCus;
+    if (heads * CShape<D, 512>::NRB > round && heads * CShape<D, 1024>::NRB <= round)
+        return launch_e<D, F32K, 1024>(a, st);
+    return launch_e<D, F32K, 512>(a, st);
 }
 
 template <bool F32K>

@@ -17,7 +17,7 @@ bool supported_d(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
 
 // A launch dispatches at most 2^32 - 1 work-items (the dispatch packet's grid
 // size is 32 bits).  `units` independent units of at most `per_unit`
-// work-items each must fit: verify 512 per (sequence, head), commit 1024 per
+// work-items each must fit: verify 512 per (sequence, head), commit 2048 per
 // (sequence, head), gather 512 per (sequence, position, head), the in-block
 // read 512 per (sequence, head, chunk of 64 queries), selection 512 per row.
 bool grid_fits(long long units, long long per_unit) { return units * per_unit <= 0xffffffffLL; }
@@ -132,7 +132,7 @@ LDV_EXPORT int ldv_commit_state(int B, int T, int H, int dk, int dv, int k_dtype
     if (!aligned(k, 16) || !aligned(u, 16) || !aligned(S0, 16) || !aligned(S_out, 16) || !aligned(logp, 4) ||
         !aligned(parent, 4) || !aligned(accepted, 4) || !aligned(status, 4))
         return LDV_ERR_ARG;
-    if (!grid_fits((long long)B * H, 1024) || (long long)B * T > 0x7fffffffLL) return LDV_ERR_UNSUPPORTED;
+    if (!grid_fits((long long)B * H, 2048) || (long long)B * T > 0x7fffffffLL) return LDV_ERR_UNSUPPORTED;
     ldv::CommitArgs args{B, T, H, dk, T, 0, -2, k, u, logp, parent, accepted, S0, S_out, status};
     hipError_t e = ldv::launch_commit(args, k_dtype == LDV_F32, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? LDV_OK : LDV_ERR_LAUNCH;

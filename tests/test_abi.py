@@ -205,7 +205,7 @@ def test_work_item_limits(lib):
     assert v(1 << 12, 1 << 11) == -2              # 2^23 heads x 512 work-items = 2^32
     c = lambda B, H: lib.ldv_commit_state(B, 1, H, 16, 16, 0, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE,
                                           None, None)
-    assert c(1 << 11, 1 << 11) == -2              # 2^22 heads x 1024 work-items = 2^32
+    assert c(1 << 11, 1 << 10) == -2              # 2^21 heads x 2048 work-items = 2^32
     g = lambda B, P, H: lib.ldv_gather_states(B, P, H, 16, 16, 1, 0, 0, FAKE, FAKE, None, None, FAKE,
                                               None, None)
     assert g(1 << 11, 4, 1 << 10) == -2           # 2^23 (sequence, position, head) units
