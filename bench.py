@@ -318,10 +318,12 @@ class Timer:
         self.hev.destroy(e1)
         return t
 
+    warm_s = WARM_S
+
     def warm(self, fn):
-        """Untimed runs of fn until WARM_S of GPU time has passed."""
+        """Untimed runs of fn until warm_s of GPU time has passed (at least one)."""
         t, n = 0.0, 0
-        while t < WARM_S or n < 1:
+        while t < self.warm_s or n < 1:
             t += self.once(fn)
             n += 1
         return n
@@ -345,8 +347,9 @@ def measure_peaks(torch):
     """Achievable rates on this GPU, each the best of 5 timed launches after a
     warm-up: stream probes over 1 GiB (libldv_peaks.so; non-temporal loads
     and stores) reading only, copying, rewriting in place, and writing one
-    float4 per 2, 4 or 8 read, each the best of grid-stride grids of 256 to
-    16384 blocks and a grid of one block per step of the stream; a loop of
+    float4 per 2, 4 or 8 read, each the best of 2, 4 or 8 loads in flight per
+    thread on grid-stride grids of 256 to 16384 blocks and on a grid of one
+    block per step of the stream; a loop of
     independent v_mfma_f32_16x16x32_bf16 chains on every SIMD; an 8192^3 bf16
     GEMM (hipBLASLt through torch.matmul)."""
     import ctypes
@@ -355,7 +358,7 @@ def measure_peaks(torch):
     plib.ldv_peak_mfma.argtypes = [ctypes.c_int, vp, vp]
     plib.ldv_peak_mfma_flops.argtypes = [ctypes.c_int]
     plib.ldv_peak_mfma_flops.restype = ctypes.c_double
-    plib.ldv_peak_stream.argtypes = [ctypes.c_int, vp, vp, ctypes.c_longlong, ctypes.c_int, vp]
+    plib.ldv_peak_stream.argtypes = [ctypes.c_int, ctypes.c_int, vp, vp, ctypes.c_longlong, ctypes.c_int, vp]
     plib.ldv_peak_stream_granule.restype = ctypes.c_longlong
     g = plib.ldv_peak_stream_granule()
     n4 = (1 << 30) // 16 // g * g
@@ -366,10 +369,10 @@ def measure_peaks(torch):
     nblk = 4 * torch.cuda.get_device_properties(0).multi_processor_count
     pout = torch.empty(nblk * 256, device="cuda")
 
-    def stream_call(ratio, blocks, in_place=False):
+    def stream_call(ratio, loads, blocks, in_place=False):
         def f():
-            rc = plib.ldv_peak_stream(ratio, vp(src.data_ptr()), vp((src if in_place else dst).data_ptr()), n4,
-                                      blocks, vp(torch.cuda.current_stream().cuda_stream))
+            rc = plib.ldv_peak_stream(ratio, loads, vp(src.data_ptr()), vp((src if in_place else dst).data_ptr()),
+                                      n4, blocks, vp(torch.cuda.current_stream().cuda_stream))
             assert rc == 0, "stream probe launch failed (%d)" % rc
         return f
 
@@ -397,9 +400,14 @@ def measure_peaks(torch):
                                   ("read2write1_GB_s", 2, False), ("read4write1_GB_s", 4, False),
                                   ("read8write1_GB_s", 8, False)):
         wr = nbytes // ratio if ratio else 0
-        one_shot = n4 // (max(4, ratio) * 256)  # one block per step of the stream: no grid-stride loop
-        out[name] = max(best_rate(stream_call(ratio, blk, in_place), (nbytes + wr) / 1e9)
-                        for blk in (256, 512, 1024, 2048, 4096, 16384, one_shot))
+        rates = []
+        for loads in (2, 4, 8):
+            if loads < ratio:
+                continue
+            one_shot = n4 // (loads * 256)  # one block per step of the stream: no grid-stride loop
+            rates += [best_rate(stream_call(ratio, loads, blk, in_place), (nbytes + wr) / 1e9)
+                      for blk in (256, 512, 1024, 2048, 4096, 16384, one_shot)]
+        out[name] = max(rates)
     out["bf16_mfma_loop_TFLOP_s"] = best_rate(mfma_loop, plib.ldv_peak_mfma_flops(nblk) / 1e12)
     out["bf16_gemm_TFLOP_s"] = best_rate(lambda: torch.matmul(a, b), 2 * 8192 ** 3 / 1e12)
     del src, dst, a, b, pout
@@ -408,19 +416,24 @@ def measure_peaks(torch):
 
 
 def ceiling_for(rd, wr, in_place, peaks):
-    """The measured stream probe nearest a kernel's read/write mix: the
-    in-place probe for an in-place commit, else the read:write ratio nearest
-    in log scale among 1, 2, 4, 8 and reads only (taken as 32:1)."""
+    """The achievable streaming rate for a kernel's read/write mix: the best
+    stream probe whose read:write ratio is at most the kernel's (a kernel
+    that reads more per byte written can stream at least as fast), the
+    reads-only probe counting as a 32:1 mix (kernels that write less than
+    that are graded as reading only).  The in-place probe counts as a 1:1
+    mix; an in-place commit is graded against it alone."""
     if not peaks:
         return None, None
     if in_place:
         return "rmw_GB_s", peaks["rmw_GB_s"]
     r = rd / wr if wr > 0 else float("inf")
-    cands = [(1, "copy_GB_s"), (2, "read2write1_GB_s"), (4, "read4write1_GB_s"), (8, "read8write1_GB_s"),
-             (32, "read_GB_s")]
-    lr = math.log2(min(r, 1e9))
-    name = min(cands, key=lambda c: abs(math.log2(c[0]) - lr))[1]
-    return name, peaks[name]
+    cands = [(1, "copy_GB_s"), (1, "rmw_GB_s"), (2, "read2write1_GB_s"), (4, "read4write1_GB_s"),
+             (8, "read8write1_GB_s"), (32, "read_GB_s")]
+    ok = [(peaks[n], n) for ratio, n in cands if ratio <= r * (1 + 1e-9)]
+    if not ok:
+        return "copy_GB_s", peaks["copy_GB_s"]
+    v, n = max(ok)
+    return n, v
 
 
 def host_threads():
@@ -603,6 +616,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU-oracle time on the headline workload")
     ap.add_argument("--cpu-seconds-other", type=float, default=3.0, help="CPU-oracle time on each other workload")
     ap.add_argument("--repeats", type=int, default=5, help="timed replays of each graph")
+    ap.add_argument("--warm-ms", type=float, default=WARM_S * 1e3,
+                    help="untimed GPU work before each timed graph (at least one replay; 0 for counter runs)")
     ap.add_argument("--no-peaks", action="store_true", help="skip measuring the stream, MFMA and GEMM rates")
     ap.add_argument("--eager", action="store_true",
                     help="launch from Python each step instead of replaying HIP graphs (for profilers)")
@@ -639,6 +654,7 @@ def main():
     allw = {**WORKLOADS, **LONG_WORKLOADS}
     hev = HipEvents()
     timer = Timer(torch, hev, torch.cuda.current_stream().cuda_stream)  # the stream the library launches on
+    timer.warm_s = args.warm_ms * 1e-3
     peaks = None if args.no_peaks else measure_peaks(torch)
     res = {}
     for key in keys:

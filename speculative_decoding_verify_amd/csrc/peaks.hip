@@ -13,8 +13,9 @@
 // mixes of the library's kernels: reads only (the selection's logits), one
 // write per read (commit: a state in, a state out, in place or not), and one
 // write per two, four or eight reads (verify, the gathers and the in-block
-// reads write less than they read).  Each kernel of the library is graded against
-// the probe nearest its own mix.
+// reads write less than they read), each with 2, 4 or 8 loads in flight per
+// thread.  Each kernel of the library is graded against the best rate
+// measured at its own read:write ratio or a more write-heavy one.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -47,32 +48,32 @@ __global__ __launch_bounds__(kThreads) void mfma_peak_kernel(float seed, float* 
     out[(size_t)blockIdx.x * kThreads + threadIdx.x] = s;
 }
 
-// Stream probes: each thread keeps L = max(4, R) 16-byte non-temporal loads
-// in flight per step (four measured fastest on MI355X: 7.1-7.2 TB/s for
-// reads alone against about 6.0 TB/s with ordinary loads) and writes, with
-// non-temporal stores, one float4 per R float4 read (their sum, so the loads
-// are live); R = 0 reads only and writes one float4 per thread at the end.
-// A block step covers L * 256 consecutive float4, each wave load 1 KiB of
-// consecutive bytes.  Step w writes its sums at float4 w * (L / R) * 256 + ...,
-// so with R = 1 and dst == src every float4 is rewritten in place right after
-// it is read.
+// Stream probes: each thread keeps L 16-byte non-temporal loads in flight
+// per step (2, 4 or 8; non-temporal loads measured fastest on MI355X: 7.1-7.2
+// TB/s for reads alone against about 6.0 TB/s with ordinary loads) and
+// writes, with non-temporal stores, one float4 per R float4 read (their sum,
+// so the loads are live); R = 0 reads only and writes one float4 per thread
+// at the end.  A block step covers L * 256 consecutive float4, each wave load
+// 1 KiB of consecutive bytes.  Step w writes its sums at float4
+// w * (L / R) * 256 + ..., so with R = 1 and dst == src every float4 is
+// rewritten in place right after it is read.
 constexpr int kMaxLoads = 8;
 
-template <int R>
+template <int R, int L>
 __global__ __launch_bounds__(kThreads) void stream_kernel(const floatx4* src, floatx4* dst, size_t n) {
-    constexpr int kLoads = R > 4 ? R : 4;
-    constexpr int W = R > 0 ? kLoads / R : 0;  // float4 written per thread and step
-    const size_t per_block = (size_t)kLoads * kThreads;
+    static_assert(R == 0 || L % R == 0, "R divides L");
+    constexpr int W = R > 0 ? L / R : 0;  // float4 written per thread and step
+    const size_t per_block = (size_t)L * kThreads;
     const size_t nsteps = n / per_block;
     floatx4 acc = {0.f, 0.f, 0.f, 0.f};
     for (size_t w = blockIdx.x; w < nsteps; w += gridDim.x) {
         const size_t base = w * per_block + threadIdx.x;
-        floatx4 v[kLoads];
+        floatx4 v[L];
 #pragma unroll
-        for (int i = 0; i < kLoads; ++i) v[i] = __builtin_nontemporal_load(src + base + (size_t)i * kThreads);
+        for (int i = 0; i < L; ++i) v[i] = __builtin_nontemporal_load(src + base + (size_t)i * kThreads);
         if constexpr (R == 0) {
 #pragma unroll
-            for (int i = 0; i < kLoads; ++i) acc += v[i];
+            for (int i = 0; i < L; ++i) acc += v[i];
         } else {
 #pragma unroll
             for (int j = 0; j < W; ++j) {
@@ -107,24 +108,30 @@ PEAKS_EXPORT double ldv_peak_mfma_flops(int blocks) {
 // Float4 granule of the stream probes: n4 must be a multiple of it.
 PEAKS_EXPORT long long ldv_peak_stream_granule(void) { return (long long)kMaxLoads * kThreads; }
 
-// One launch of the stream probe reading n4 float4 of src and writing one
-// float4 per `ratio` read (ratio 1, 2, 4 or 8; 0 = reads only).  dst holds at
+// One launch of the stream probe reading n4 float4 of src with `loads`
+// (2, 4 or 8) loads in flight per thread and writing one float4 per `ratio`
+// read (ratio 1, 2, 4 or 8, at most `loads`; 0 = reads only).  dst holds at
 // least n4 / ratio float4 (ratio 0: blocks * 256 float4); dst == src with
 // ratio 1 rewrites src in place.  Returns 0 or a HIP error code (an invalid
-// size, ratio or pointer gives hipErrorInvalidValue before any launch).
-PEAKS_EXPORT int ldv_peak_stream(int ratio, const void* src, void* dst, long long n4, int blocks, void* stream) {
+// size, ratio, load count or pointer gives hipErrorInvalidValue before any
+// launch).
+PEAKS_EXPORT int ldv_peak_stream(int ratio, int loads, const void* src, void* dst, long long n4, int blocks,
+                                 void* stream) {
     if (!src || !dst || blocks <= 0 || n4 <= 0 || n4 % ldv_peak_stream_granule() != 0) return (int)hipErrorInvalidValue;
     const hipStream_t st = static_cast<hipStream_t>(stream);
     const floatx4* s = static_cast<const floatx4*>(src);
     floatx4* d = static_cast<floatx4*>(dst);
     const dim3 g((unsigned)blocks), b(kThreads);
-    switch (ratio) {
-        case 0: hipLaunchKernelGGL(stream_kernel<0>, g, b, 0, st, s, d, (size_t)n4); break;
-        case 1: hipLaunchKernelGGL(stream_kernel<1>, g, b, 0, st, s, d, (size_t)n4); break;
-        case 2: hipLaunchKernelGGL(stream_kernel<2>, g, b, 0, st, s, d, (size_t)n4); break;
-        case 4: hipLaunchKernelGGL(stream_kernel<4>, g, b, 0, st, s, d, (size_t)n4); break;
-        case 8: hipLaunchKernelGGL(stream_kernel<8>, g, b, 0, st, s, d, (size_t)n4); break;
-        default: return (int)hipErrorInvalidValue;
+#define PEAKS_CASE(R, L) \
+    if (ratio == R && loads == L) { \
+        hipLaunchKernelGGL((stream_kernel<R, L>), g, b, 0, st, s, d, (size_t)n4); \
+        return (int)hipGetLastError(); \
     }
-    return (int)hipGetLastError();
+    PEAKS_CASE(0, 2) PEAKS_CASE(0, 4) PEAKS_CASE(0, 8)
+    PEAKS_CASE(1, 2) PEAKS_CASE(1, 4) PEAKS_CASE(1, 8)
+    PEAKS_CASE(2, 2) PEAKS_CASE(2, 4) PEAKS_CASE(2, 8)
+    PEAKS_CASE(4, 4) PEAKS_CASE(4, 8)
+    PEAKS_CASE(8, 8)
+#undef PEAKS_CASE
+    return (int)hipErrorInvalidValue;
 }

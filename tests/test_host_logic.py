@@ -83,14 +83,18 @@ def test_bench_algorithmic_bytes():
 
 
 def test_bench_ceiling_choice():
-    """Each kernel is graded against the stream probe nearest its mix."""
+    """Each kernel is graded against the best stream probe at its read:write
+    ratio or a more write-heavy one; an in-place commit against the in-place
+    probe."""
     import bench
     peaks = {"read_GB_s": 7.0, "copy_GB_s": 6.0, "rmw_GB_s": 6.2, "read2write1_GB_s": 6.1,
-             "read4write1_GB_s": 6.3, "read8write1_GB_s": 6.4}
+             "read4write1_GB_s": 6.5, "read8write1_GB_s": 6.3}
     assert bench.ceiling_for(10, 10, True, peaks) == ("rmw_GB_s", 6.2)
-    assert bench.ceiling_for(10, 10, False, peaks)[0] == "copy_GB_s"
-    assert bench.ceiling_for(77952, 16448, False, peaks)[0] == "read4write1_GB_s"   # 27B-hybrid verify
-    assert bench.ceiling_for(69632, 8192, False, peaks)[0] == "read8write1_GB_s"    # gather
-    assert bench.ceiling_for(1000, 1, False, peaks)[0] == "read_GB_s"               # selection
-    assert bench.ceiling_for(1000, 0, False, peaks)[0] == "read_GB_s"
+    assert bench.ceiling_for(10, 10, False, peaks) == ("rmw_GB_s", 6.2)
+    assert bench.ceiling_for(15, 10, False, peaks) == ("rmw_GB_s", 6.2)          # 1.5:1: the 1:1 probes only
+    assert bench.ceiling_for(77952, 16448, False, peaks) == ("read4write1_GB_s", 6.5)   # 27B-hybrid verify, 4.7:1
+    assert bench.ceiling_for(69632, 8192, False, peaks) == ("read4write1_GB_s", 6.5)    # gather, 8.5:1
+    assert bench.ceiling_for(1000, 1, False, peaks) == ("read_GB_s", 7.0)               # 1000:1: reads only
+    assert bench.ceiling_for(1000, 0, False, peaks) == ("read_GB_s", 7.0)
+    assert bench.ceiling_for(1, 2, False, peaks) == ("copy_GB_s", 6.0)                  # more writes than reads
     assert bench.ceiling_for(1, 1, False, None) == (None, None)
