@@ -349,7 +349,8 @@ def measure_peaks(torch):
     and stores) reading only, copying, rewriting in place, and writing one
     float4 per 2, 4 or 8 read, each the best of 2, 4 or 8 loads in flight per
     thread on grid-stride grids of 256 to 16384 blocks and on a grid of one
-    block per step of the stream; a loop of
+    block per step of the stream (steps in order, or 128 KiB units spread
+    over the XCDs as the library's per-head kernels spread heads); a loop of
     independent v_mfma_f32_16x16x32_bf16 chains on every SIMD; an 8192^3 bf16
     GEMM (hipBLASLt through torch.matmul)."""
     import ctypes
@@ -358,7 +359,8 @@ def measure_peaks(torch):
     plib.ldv_peak_mfma.argtypes = [ctypes.c_int, vp, vp]
     plib.ldv_peak_mfma_flops.argtypes = [ctypes.c_int]
     plib.ldv_peak_mfma_flops.restype = ctypes.c_double
-    plib.ldv_peak_stream.argtypes = [ctypes.c_int, ctypes.c_int, vp, vp, ctypes.c_longlong, ctypes.c_int, vp]
+    plib.ldv_peak_stream.argtypes = [ctypes.c_int, ctypes.c_int, vp, vp, ctypes.c_longlong, ctypes.c_int, ctypes.c_int,
+                                     vp]
     plib.ldv_peak_stream_granule.restype = ctypes.c_longlong
     g = plib.ldv_peak_stream_granule()
     n4 = (1 << 30) // 16 // g * g
@@ -369,10 +371,10 @@ def measure_peaks(torch):
     nblk = 4 * torch.cuda.get_device_properties(0).multi_processor_count
     pout = torch.empty(nblk * 256, device="cuda")
 
-    def stream_call(ratio, loads, blocks, in_place=False):
+    def stream_call(ratio, loads, blocks, in_place=False, spread=0):
         def f():
             rc = plib.ldv_peak_stream(ratio, loads, vp(src.data_ptr()), vp((src if in_place else dst).data_ptr()),
-                                      n4, blocks, vp(torch.cuda.current_stream().cuda_stream))
+                                      n4, blocks, spread, vp(torch.cuda.current_stream().cuda_stream))
             assert rc == 0, "stream probe launch failed (%d)" % rc
         return f
 
@@ -407,6 +409,7 @@ def measure_peaks(torch):
             one_shot = n4 // (loads * 256)  # one block per step of the stream: no grid-stride loop
             rates += [best_rate(stream_call(ratio, loads, blk, in_place), (nbytes + wr) / 1e9)
                       for blk in (256, 512, 1024, 2048, 4096, 16384, one_shot)]
+            rates.append(best_rate(stream_call(ratio, loads, one_shot, in_place, 1), (nbytes + wr) / 1e9))
         out[name] = max(rates)
     out["bf16_mfma_loop_TFLOP_s"] = best_rate(mfma_loop, plib.ldv_peak_mfma_flops(nblk) / 1e12)
     out["bf16_gemm_TFLOP_s"] = best_rate(lambda: torch.matmul(a, b), 2 * 8192 ** 3 / 1e12)

@@ -14,8 +14,8 @@
  * columns into independent tiles; Eq. (9) and its "Lemma 1" keep only the
  * node factors (gate products P, keys K, corrections U) plus the one
  * committed state, so that only the accepted node's state is ever formed
- * (the page's summary: "materializes only the post-sampling selected
- * state").  The ReaDy page (arXiv 2610.20503, Fig. 2a, 3, 4) reads committed
+ * (the page's summary makes the same point: of all proposal nodes, only
+ * the one kept after sampling gets its state built).  The ReaDy page (arXiv 2610.20503, Fig. 2a, 3, 4) reads committed
  * recurrent states at chosen positions for the drafter.
  *
  * Conventions shared by every call:

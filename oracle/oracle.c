@@ -19,8 +19,8 @@
  * uses the closed form: every node's state is rebuilt from S0 along the
  * node's root-to-node path.
  *
- * Commit (Bole page, summary: only the post-sampling selected state is
- * materialised) is the walk's state at the accepted node; gather (ReaDy page,
+ * Commit (Bole page, summary: of all proposal nodes only the one kept
+ * after sampling gets its state built) is the walk's state at the accepted node; gather (ReaDy page,
  * Fig. 2a-3: position-specific reads from committed recurrent states) is a
  * copy of a pool entry plus o = S q for each query.
  *

@@ -1,8 +1,8 @@
 // State commit: form only the accepted node's state from the committed state
 // and the node factors (gfx950).
 //
-// Bole page (arXiv 2608.01651): the summary says only the post-sampling
-// selected state is materialised; section IV, Eq. (9) and its "Lemma 1"
+// Bole page (arXiv 2608.01651): its summary has only the state of the node
+// kept after sampling built; section IV, Eq. (9) and its "Lemma 1"
 // keep the node factors P, K, U next to the single committed state.  Unrolling
 // the recurrence S_n = a_n S_p + u_n k_n^T gives, for the accepted node n,
 //   S_n = P_n S0 + sum_{m on root-to-n path} (P_n / P_m) u_m k_m^T,

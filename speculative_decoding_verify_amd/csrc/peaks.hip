@@ -59,14 +59,28 @@ __global__ __launch_bounds__(kThreads) void mfma_peak_kernel(float seed, float* 
 // rewritten in place right after it is read.
 constexpr int kMaxLoads = 8;
 
+// With `spread` (a grid of one block per step), the steps are grouped in
+// units of 128 KiB (two heads' states at d = 128) and consecutive units go to
+// different XCDs, the steps of a unit staying on one XCD (hardware block i
+// runs on XCD i % 8): the block-to-data map of the library's per-head
+// kernels.  Blocks past the last whole group of 8 units keep their step.
 template <int R, int L>
-__global__ __launch_bounds__(kThreads) void stream_kernel(const floatx4* src, floatx4* dst, size_t n) {
+__global__ __launch_bounds__(kThreads) void stream_kernel(const floatx4* src, floatx4* dst, size_t n, int spread) {
     static_assert(R == 0 || L % R == 0, "R divides L");
     constexpr int W = R > 0 ? L / R : 0;  // float4 written per thread and step
     const size_t per_block = (size_t)L * kThreads;
     const size_t nsteps = n / per_block;
     floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (size_t w = blockIdx.x; w < nsteps; w += gridDim.x) {
+    size_t w0 = blockIdx.x;
+    if (spread) {
+        constexpr size_t per = 32 / L;  // steps per 128 KiB unit
+        const size_t full = (nsteps / per / 8) * 8 * per;
+        if (w0 < full) {
+            const size_t x = w0 % 8, t = w0 / 8;
+            w0 = ((t / per) * 8 + x) * per + t % per;
+        }
+    }
+    for (size_t w = w0; w < nsteps; w += gridDim.x) {
         const size_t base = w * per_block + threadIdx.x;
         floatx4 v[L];
 #pragma unroll
@@ -112,19 +126,22 @@ PEAKS_EXPORT long long ldv_peak_stream_granule(void) { return (long long)kMaxLoa
 // (2, 4 or 8) loads in flight per thread and writing one float4 per `ratio`
 // read (ratio 1, 2, 4 or 8, at most `loads`; 0 = reads only).  dst holds at
 // least n4 / ratio float4 (ratio 0: blocks * 256 float4); dst == src with
-// ratio 1 rewrites src in place.  Returns 0 or a HIP error code (an invalid
+// ratio 1 rewrites src in place.  spread != 0 maps steps to XCDs as above
+// (only on a grid of one block per step).  Returns 0 or a HIP error code (an invalid
 // size, ratio, load count or pointer gives hipErrorInvalidValue before any
 // launch).
 PEAKS_EXPORT int ldv_peak_stream(int ratio, int loads, const void* src, void* dst, long long n4, int blocks,
-                                 void* stream) {
+                                 int spread, void* stream) {
     if (!src || !dst || blocks <= 0 || n4 <= 0 || n4 % ldv_peak_stream_granule() != 0) return (int)hipErrorInvalidValue;
+    // the spread map is meant for a grid of one block per step
+    if (spread && (loads <= 0 || n4 / ((long long)loads * kThreads) != blocks)) return (int)hipErrorInvalidValue;
     const hipStream_t st = static_cast<hipStream_t>(stream);
     const floatx4* s = static_cast<const floatx4*>(src);
     floatx4* d = static_cast<floatx4*>(dst);
     const dim3 g((unsigned)blocks), b(kThreads);
 #define PEAKS_CASE(R, L) \
     if (ratio == R && loads == L) { \
-        hipLaunchKernelGGL((stream_kernel<R, L>), g, b, 0, st, s, d, (size_t)n4); \
+        hipLaunchKernelGGL((stream_kernel<R, L>), g, b, 0, st, s, d, (size_t)n4, spread); \
         return (int)hipGetLastError(); \
     }
     PEAKS_CASE(0, 2) PEAKS_CASE(0, 4) PEAKS_CASE(0, 8)
