@@ -344,8 +344,8 @@ def capture(torch, fns, K):
 
 
 def measure_peaks(torch):
-    """Achievable rates on this GPU, each the best of 5 timed launches after a
-    warm-up: stream probes over 1 GiB (libldv_peaks.so; non-temporal loads
+    """Achievable rates on this GPU, each the best of 3 timed runs of 8
+    back-to-back launches after a warm-up: stream probes over 1 GiB (libldv_peaks.so; non-temporal loads
     and stores) reading only, copying, rewriting in place, and writing one
     float4 per 2, 4 or 8 read, each the best of 2, 4 or 8 loads in flight per
     thread on grid-stride grids of 256 to 16384 blocks and on a grid of one
@@ -382,17 +382,20 @@ def measure_peaks(torch):
         rc = plib.ldv_peak_mfma(nblk, vp(pout.data_ptr()), vp(torch.cuda.current_stream().cuda_stream))
         assert rc == 0, "MFMA probe launch failed (%d)" % rc
 
-    def best_rate(fn, work):
+    def best_rate(fn, work, launches=8, repeats=3):
+        """work per second of `launches` back-to-back launches (as the
+        library's kernels are timed), the best of `repeats`."""
         fn()
         torch.cuda.synchronize()
         best = None
-        for _ in range(5):
+        for _ in range(repeats):
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record()
-            fn()
+            for _ in range(launches):
+                fn()
             e1.record()
             torch.cuda.synchronize()
-            t = e0.elapsed_time(e1) * 1e-3
+            t = e0.elapsed_time(e1) * 1e-3 / launches
             best = t if best is None else min(best, t)
         return work / best
 

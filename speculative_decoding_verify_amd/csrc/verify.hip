@@ -192,9 +192,14 @@ struct VLds {
 
 // STG: outputs staged in LDS and stored as whole rows.  CMT: a 64-node chunk
 // of a long chain of pa.Ts nodes, with step 6; with LOOP, pa.chunks chunks.
+// The looping form runs one block per CU, so its registers need only allow
+// that block's waves (two per SIMD at d = 128): with the four-wave limit of
+// the other forms it spilled, and measured 290 vs 274 us on the GDN-1.3B
+// shape's 1024-node chain.
 template <int D, int TM, bool F32IN, bool STG, bool CMT, bool LOOP>
 __global__ __launch_bounds__((VShape<D, TM>::NW * kWave))
-__attribute__((amdgpu_waves_per_eu(VLds<D, TM, F32IN, STG>::WPE))) void verify_kernel(const VerifyArgs pa) {
+__attribute__((amdgpu_waves_per_eu(LOOP ? (VShape<D, TM>::NW + 3) / 4 : VLds<D, TM, F32IN, STG>::WPE)))
+void verify_kernel(const VerifyArgs pa) {
     using S = VShape<D, TM>;
     using L = VLds<D, TM, F32IN, STG>;
     constexpr int BV = S::BV, NW = S::NW, KS = S::KS, QKLD = S::QKLD, NBM = S::NBM, MBW = S::MBW;
