@@ -102,8 +102,9 @@ extern "C" {
  *   o         [B, T, H, dv] fp32 (written)
  *   u_out     [B, T, H, dv] fp32, the node corrections U of Eq. (2)
  *             (u_n = beta_n (v_n - a_n S_p(n) k_n)), written
- *   logp_out  [B, T, H] fp32, log P_n = sum of log a over the root-to-n path,
- *             each log a clamped below at -87 (a zero gate stays finite)
+ *   logp_out  [B, T, H] fp32, log P_n = sum of log a over the root-to-n path
+ *             (natural log), each log a clamped below at -126 ln 2 = -87.34
+ *             (a zero gate stays finite)
  *   u_out and logp_out are the factors ldv_commit_state needs; pass both or
  *   neither (NULL, NULL: no commit will follow).
  * A sequence whose parent row is invalid gets LDV_STATUS_BAD_PARENT and none

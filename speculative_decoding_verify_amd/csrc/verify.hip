@@ -60,15 +60,19 @@
 //      head's chunks in order.
 // Two workgroup barriers (after step 2 and after step 3), and two more per
 // node block when the outputs are staged (two more for step 6).
-// P_n / P_m is exp(log P_n - log P_m), evaluated only for ancestor pairs
-// (exponent <= 0 for gates in [0, 1]); log a is clamped at -87 so that a
-// zero gate gives a finite log.
+// Inside the kernel log P is kept in base 2: log2 a from the hardware's
+// log2 (clamped at -126, so that a zero gate gives a finite log), summed
+// along the path; P_n / P_m = 2^(log2 P_n - log2 P_m) from the hardware's
+// 2^x, used only for ancestor pairs (exponent <= 0 for gates in [0, 1]).
+// The natural log P is what the kernel writes out.
 #include "ldv_device.hpp"
 #include "ldv_kernels.hpp"
 
 #include "../../include/ldv.h"
 
 namespace ldv {
+
+constexpr float kLn2 = 0.693147180559945309f;  // natural log of 2
 
 // A 16 x 16 fp32 matrix held in the C layout, as bf16 operand forms: the
 // pair [hi | lo] (k-slots 8 g .. 8 g + 3 take rows 4 g .. 4 g + 3 of the hi
@@ -396,7 +400,7 @@ void verify_kernel(const VerifyArgs pa) {
             const bool valid = n < T;
             const bool bad = valid && (par < -1 || par >= n);
             const uint64_t badm = __ballot(bad);
-            const float la = valid ? fmaxf(logf(ga), -87.f) : 0.f;
+            const float la = valid ? fmaxf(__builtin_amdgcn_logf(ga), -126.f) : 0.f;  // log2 a
             // pointer doubling: (set, ls) summarise the path segment from n up to
             // (not including) jmp
             uint64_t set = valid ? (1ull << n) : 0ull;
@@ -417,7 +421,7 @@ void verify_kernel(const VerifyArgs pa) {
             if (n < TM) {
                 s_anc[n] = valid ? (set & ~(1ull << n)) : 0ull;
                 s_logp[n] = ls;
-                s_P[n] = valid ? expf(ls) : 0.f;
+                s_P[n] = valid ? __builtin_amdgcn_exp2f(ls) : 0.f;
                 s_beta[n] = valid ? gb : 0.f;
             }
             if (lane == 0) {
@@ -425,7 +429,7 @@ void verify_kernel(const VerifyArgs pa) {
                 if (badm != 0ull && p.status && h == 0 && tile == 0) atomicOr(p.status, LDV_STATUS_BAD_PARENT);
             }
             if (badm == 0ull && valid && tile == 0 && p.logp_out)
-                p.logp_out[(nb0 + n) * H + h] = ls + (p.t0 > 0 ? lbase_ld : 0.f);
+                p.logp_out[(nb0 + n) * H + h] = ls * kLn2 + (p.t0 > 0 ? lbase_ld : 0.f);
         }
         __syncthreads();
         if (s_int[0]) return;  // invalid parent row: nothing is written
@@ -436,7 +440,10 @@ void verify_kernel(const VerifyArgs pa) {
         //       X_ii = (I + G_ii)^{-1} = (I - G)(I + G^2)(I + G^4)(I + G^8)
         //     (G_ii is nilpotent: G^L = 0 for L the longest ancestor chain
         //     inside the block, so the product stops at the first power >= L).
-        for (int i = wave; i < NB; i += NW) {
+        // (the factor work is spread over the waves by the wave index read into a
+        // scalar register, so that the item loops and index searches are scalar)
+        const int wv = __builtin_amdgcn_readfirstlane(wave);
+        for (int i = wv; i < NB; i += NW) {
             floatx4 acc = {0.f, 0.f, 0.f, 0.f};
             const unsigned short* krow = s_k + (16 * i + c) * QKLD;
     #pragma unroll
@@ -449,16 +456,23 @@ void verify_kernel(const VerifyArgs pa) {
                     acc = mfma16x16x32(bkl, bk, acc);
                 }
             }
-            const int nc = 16 * i + c;
+            // rows 16 i + 4 g + r (read as vectors, with no branch: the masks
+            // select), column nc; of the two entries at most one is nonzero, so
+            // each takes one 2^x
+            const int nc = 16 * i + c, n0 = 16 * i + 4 * g;
             const uint64_t anc_c = s_anc[nc];
             const float lpc = s_logp[nc], bec = s_beta[nc];
+            const float4 lp4 = *reinterpret_cast<const float4*>(s_logp + n0);
+            const float4 be4 = *reinterpret_cast<const float4*>(s_beta + n0);
+            const float lpr[4] = {lp4.x, lp4.y, lp4.z, lp4.w}, ber[4] = {be4.x, be4.y, be4.z, be4.w};
             floatx4 G, Gt;  // G[16 i + 4 g + r][nc] and G[nc][16 i + 4 g + r]
     #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int nr = 16 * i + 4 * g + r;
-                const float lpr = s_logp[nr];
-                G[r] = ((s_anc[nr] >> nc) & 1ull) ? s_beta[nr] * expf(lpr - lpc) * acc[r] : 0.f;
-                Gt[r] = ((anc_c >> nr) & 1ull) ? bec * expf(lpc - lpr) * acc[r] : 0.f;
+                const bool below = (s_anc[n0 + r] >> nc) & 1ull;  // nc an ancestor of row n0 + r
+                const bool above = (anc_c >> (n0 + r)) & 1ull;    // row n0 + r an ancestor of nc
+                const float x = __builtin_amdgcn_exp2f(below ? lpr[r] - lpc : lpc - lpr[r]) * acc[r];
+                G[r] = below ? ber[r] * x : 0.f;
+                Gt[r] = above ? bec * x : 0.f;
             }
             const int L = __builtin_amdgcn_readfirstlane(wave_max_i(__popcll((anc_c >> (16 * i)) & 0xffffull) + 1));
             floatx4 Xt = ident_plus(Gt, -1.f, c, g);  // (I - G)^T
@@ -496,15 +510,15 @@ void verify_kernel(const VerifyArgs pa) {
         //     one take C consecutive items each, the others share the rest.
         {
             const int nneg = NB * (NB - 1) / 2, nitem = NB * NB;
-            int it0 = wave, it1 = nitem, step = NW;
+            int it0 = wv, it1 = nitem, step = NW;
             if (NW > NB) {
                 const int C = (2 * NB + nitem + NW - 1) / NW;
-                if (wave >= NB) {
-                    it0 = (wave - NB) * C;
+                if (wv >= NB) {
+                    it0 = (wv - NB) * C;
                     it1 = min(it0 + C, nitem);
                     step = 1;
                 } else {
-                    it0 = (NW - NB) * C + wave;
+                    it0 = (NW - NB) * C + wv;
                     step = NB;
                 }
             }
@@ -541,11 +555,14 @@ void verify_kernel(const VerifyArgs pa) {
                 // m on the path of n (C: n itself included; G: strict ancestors)
                 const uint64_t pathn = s_anc[n] | (isc ? (1ull << n) : 0ull);
                 const float lpn = s_logp[n], sc = isc ? 1.f : -s_beta[n];
+                const float4 lm4 = *reinterpret_cast<const float4*>(s_logp + 16 * bm + 4 * g);
+                const float lm[4] = {lm4.x, lm4.y, lm4.z, lm4.w};
                 floatx4 v;
     #pragma unroll
-                for (int r = 0; r < 4; ++r) {
+                for (int r = 0; r < 4; ++r) {  // (no branch: the mask selects)
                     const int m = 16 * bm + 4 * g + r;
-                    v[r] = ((pathn >> m) & 1ull) ? sc * expf(lpn - s_logp[m]) * acc[r] : 0.f;
+                    const float x = sc * __builtin_amdgcn_exp2f(lpn - lm[r]) * acc[r];
+                    v[r] = ((pathn >> m) & 1ull) ? x : 0.f;
                 }
                 const Frag16 fv = frag16(v);
                 slot_store(s_sl, t, lane, fv.dh);
@@ -814,7 +831,7 @@ void verify_kernel(const VerifyArgs pa) {
     #pragma unroll
                     for (int r = 0; r < 4; ++r) {
                         const int m = 16 * i + 4 * g + r;
-                        const float w = ((path >> m) & 1ull) ? expf(lpl - s_logp[m]) : 0.f;
+                        const float w = ((path >> m) & 1ull) ? __builtin_amdgcn_exp2f(lpl - s_logp[m]) : 0.f;
                         x[r] = w * (bf16_val(ub[r]) + bf16_val(ub[4 + r]));
                     }
                     uw[i] = pair16(floatx4{x[0], x[1], x[2], x[3]});
@@ -839,7 +856,7 @@ void verify_kernel(const VerifyArgs pa) {
         }
         if constexpr (LOOP)  // (the same in every lane: kept in a scalar register)
             lcarry = __int_as_float(__builtin_amdgcn_readfirstlane(
-                __float_as_int(s_logp[p.T - 1] + (p.t0 > 0 ? lbase_ld : 0.f))));
+                __float_as_int(s_logp[p.T - 1] * kLn2 + (p.t0 > 0 ? lbase_ld : 0.f))));
     }
 }
 

@@ -77,10 +77,10 @@ def check(name, gpu, ref, tol=TOL, design_tol=DESIGN_TOL, slices=None):
 
 def check_logp(name, gpu, ref):
     """log P from the library against the oracle's fp64 log of the gate
-    products.  The library clamps each log a at -87 (so a zero gate stays
-    finite); where the oracle's value is -inf (a zero gate on the path) the
-    library's must be at or below that floor, elsewhere they must agree to the
-    design bound."""
+    products.  The library clamps each log a at -126 ln 2 = -87.34 (so a
+    zero gate stays finite); where the oracle's value is -inf (a zero gate on
+    the path) the library's must be at or below -87, elsewhere they must agree
+    to the design bound."""
     g = host(gpu) if isinstance(gpu, torch.Tensor) else np.asarray(gpu, np.float64)
     assert g.shape == ref.shape, (name, g.shape, ref.shape)
     fin = np.isfinite(ref)
