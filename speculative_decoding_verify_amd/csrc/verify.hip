@@ -48,7 +48,8 @@
 //      O_j^T += U_i^T C_ji^T for j >= i; O_i^T is then complete and stored,
 //      each lane writing four consecutive values of one node (float4), or,
 //      on large grids, node block i's U^T and O^T tiles go through LDS so
-//      that every store writes whole rows of one node.
+//      that every store writes whole rows of one node (at 64 nodes all four
+//      node blocks at the end, over the dead Q/K rows and factor tiles).
 //   6. (long chains, every 64-node chunk but the last) the state at node
 //      T - 1,
 //        S = P S0 + sum_{m on its path} (P / P_m) u_m k_m^T   (Eq. (9)),
@@ -59,7 +60,8 @@
 //      launch may run several chunks: each block then runs steps 1-6 for its
 //      head's chunks in order.
 // Two workgroup barriers (after step 2 and after step 3), and two more per
-// node block when the outputs are staged (two more for step 6).
+// node block when the outputs are staged (two in all at 64 nodes; two more
+// for step 6).
 // Inside the kernel log P is kept in base 2: log2 a from the hardware's
 // log2 (clamped at -126, so that a zero gate gives a finite log), summed
 // along the path; P_n / P_m = 2^(log2 P_n - log2 P_m) from the hardware's
@@ -230,6 +232,18 @@ void verify_kernel(const VerifyArgs pa) {
     // the previous chunk, and the log P base is carried in a register, so no
     // block reads what another block wrote in the same launch.
     static_assert(!LOOP || CMT, "only chunks of a long chain loop");
+    // One round of staged 64-node blocks (the tree-64 shape: two per CU) runs
+    // in lockstep, and the older block of each CU wins the issue arbitration:
+    // it ended about 5 us before the other, which then ran alone at half
+    // occupancy.  Each wave lowers its priority as it advances (3 until the
+    // barrier after the topology, 2 until the one after the factor tiles, 1
+    // through the first two node blocks, then 0), so that issue goes to the
+    // waves that are behind (tree-64 21.9 -> 21.65 us, its step 33.3 -> 32.55
+    // us).  Only on grids of one round: where rounds overlap it held back the
+    // blocks the next round waits for.
+    constexpr int RES = (163840 / (int)L::total) < (4 * L::WPE / NW) ? (163840 / (int)L::total) : (4 * L::WPE / NW);
+    const bool lockstep = TM == 64 && STG && !CMT && gridDim.x <= (unsigned)(RES * kCus);
+    if (lockstep) __builtin_amdgcn_s_setprio(3);
     float lcarry = 0.f;  // log P at the previous chunk's last node, counted from S0
     const int nchunk = LOOP ? pa.chunks : 1;
     for (int ch = 0; ch < nchunk; ++ch) {
@@ -432,6 +446,7 @@ void verify_kernel(const VerifyArgs pa) {
                 p.logp_out[(nb0 + n) * H + h] = ls * kLn2 + (p.t0 > 0 ? lbase_ld : 0.f);
         }
         __syncthreads();
+        if (lockstep) __builtin_amdgcn_s_setprio(2);
         if (s_int[0]) return;  // invalid parent row: nothing is written
 
         // 3a. diagonal blocks: X_ii^T.  K_i K_i^T is symmetric, so one
@@ -710,6 +725,7 @@ void verify_kernel(const VerifyArgs pa) {
             }
         }
         __syncthreads();  // every factor tile written
+        if (lockstep) __builtin_amdgcn_s_setprio(1);
 
         // 5. forward substitution over node blocks; O^T block by block.  Output
         //    views: lane (c, g) stores node 16 i + c, values vrow0 + 16 mi + 4 g
@@ -721,6 +737,30 @@ void verify_kernel(const VerifyArgs pa) {
         const uint32_t ooff = ((uint32_t)c * HD + 4 * g) * 4;
         bf16x8 upr[MBW][NBM];  // U_i as pairs
         floatx4 ukeep[MBW], okeep[MBW];  // STG: the finished U^T and O^T tiles
+        // STG with four node blocks (outside long-chain chunks, whose step 6
+        // still reads K): one pass of whole-row stores for all 64 nodes after
+        // the substitution instead of one per node block, two workgroup
+        // barriers instead of eight.  Node blocks 0 and 1 go into the Q/K rows
+        // (dead for every wave after the barrier that ends step 4) as soon as
+        // they are done; block 2 waits in registers, and blocks 2 and 3 go over
+        // the factor tiles once every wave has read its last one.  With the
+        // priorities above: tree-64 verify 22.2 -> 21.85 us, its step 32.0 ->
+        // 30.9 us.
+        constexpr bool STG4 = STG && NBM == 4 && !CMT;
+        constexpr int SLOT = 2 * 16 * L::SLD;  // floats per staged node block: O rows, then U rows
+        static_assert(!STG4 || (L::qk >= 2 * SLOT * 4 && (size_t)S::NSLOT * kWave * 16 >= 2 * SLOT * 4),
+                      "two staged node blocks fit the Q/K rows and two the factor tiles");
+        float* const s_stg_qk = reinterpret_cast<float*>(smem);
+        float* const s_stg_t = reinterpret_cast<float*>(smem + L::off_t);
+        floatx4 ukeep2[MBW], okeep2[MBW];  // STG4: node block 2's tiles
+        auto stage_put = [&](float* s_so, const floatx4 (&ok)[MBW], const floatx4 (&uk)[MBW]) {
+    #pragma unroll
+            for (int mi = 0; mi < MBW; ++mi) {
+                const int v = (wave * MBW + mi) * 16 + 4 * g;
+                *reinterpret_cast<float4*>(s_so + c * L::SLD + v) = make_float4(ok[mi][0], ok[mi][1], ok[mi][2], ok[mi][3]);
+                *reinterpret_cast<float4*>(s_so + (16 + c) * L::SLD + v) = make_float4(uk[mi][0], uk[mi][1], uk[mi][2], uk[mi][3]);
+            }
+        };
         // STG: node block i's finished tiles through the staging area, then whole
         // rows of its 16 nodes (BV values each) to o and u, so that each store
         // instruction writes whole rows; nodes past T fall outside the views and
@@ -796,7 +836,36 @@ void verify_kernel(const VerifyArgs pa) {
                         for (int mi = 0; mi < MBW; ++mi) acco[mi][j] = mm16f(acco[mi][j], upr[mi][i], cdh, cdl);
                     }
                 }
-                if constexpr (STG) stage_store(i);
+                if constexpr (STG4) {
+                    if (i < 2) {
+                        stage_put(s_stg_qk + i * SLOT, okeep, ukeep);
+                    } else if (i == 2) {
+                        if (lockstep) __builtin_amdgcn_s_setprio(0);
+    #pragma unroll
+                        for (int mi = 0; mi < MBW; ++mi) {
+                            okeep2[mi] = okeep[mi];
+                            ukeep2[mi] = ukeep[mi];
+                        }
+                    }
+                } else if constexpr (STG) {
+                    stage_store(i);
+                }
+            }
+        }
+        if constexpr (STG4) {
+            __syncthreads();  // every factor tile has been read
+            stage_put(s_stg_t, okeep2, ukeep2);
+            stage_put(s_stg_t + SLOT, okeep, ukeep);  // node block 3 (block 2 again when NB = 3: past T, dropped)
+            __syncthreads();
+            const uint32_t tbytes = (span + BV) * 4;
+            const buf_t to = make_buf(p.o + hrow0 * D + tile * BV, tbytes);
+            const buf_t tu = make_buf(p.u_out ? p.u_out + hrow0 * D + tile * BV : nullptr, p.u_out ? tbytes : 0u);
+            for (int k = tid; k < NB * 16 * (BV / 4); k += NTHR) {
+                const int i = k / (16 * (BV / 4)), n = (k / (BV / 4)) % 16, v4 = 4 * (k % (BV / 4));
+                const float* s_so = (i < 2 ? s_stg_qk : s_stg_t - 2 * SLOT) + i * SLOT;
+                const uint32_t off = ((uint32_t)(16 * i + n) * HD + v4) * 4;
+                buf_st_stream(to, off, *reinterpret_cast<const float4*>(s_so + n * L::SLD + v4));
+                buf_st_stream(tu, off, *reinterpret_cast<const float4*>(s_so + (16 + n) * L::SLD + v4));
             }
         }
 
