@@ -98,6 +98,14 @@ __attribute__((amdgpu_waves_per_eu(RLds<D, TM, F32IN>::WPE))) void read_kernel(c
     constexpr int QC = (NQ * CPR + NTHR - 1) / NTHR;
     constexpr int KC = (TM * CPR + NTHR - 1) / NTHR;
     static_assert(NQ == kWave, "one query column per lane of wave 0");
+    // On grids of one round (every block resident at once) the blocks run in
+    // lockstep and each CU's older blocks win the issue arbitration; each wave
+    // lowers its priority as it advances (3, then 2 after staging, 1 once Q
+    // and K are dead, 0 for step 4), so that issue goes to the waves that are
+    // behind: tree-64 20.4 -> 19.5 us, GDN-1.3B 9.85 -> 9.55 us.
+    constexpr int RES = (163840 / (int)L::total) < (4 * L::WPE / NW) ? (163840 / (int)L::total) : (4 * L::WPE / NW);
+    const bool lockstep = gridDim.x <= (unsigned)(RES * kCus);
+    if (lockstep) __builtin_amdgcn_s_setprio(3);
 
     __shared__ __align__(16) unsigned char smem[L::total];
     unsigned short* s_q = reinterpret_cast<unsigned short*>(smem);           // [NQ][QKLD] hi, then lo
@@ -245,6 +253,7 @@ __attribute__((amdgpu_waves_per_eu(RLds<D, TM, F32IN>::WPE))) void read_kernel(c
         need |= (j >= 0 && j < T);
     }
     need = __syncthreads_or(need);  // also the barrier after staging
+    if (lockstep) __builtin_amdgcn_s_setprio(2);
     if (s_flag[0] && need) {
         if (tid == 0 && h == 0 && tile == 0 && ch == 0 && p.status) atomicOr(p.status, LDV_STATUS_BAD_PARENT);
         return;  // invalid parent row: nothing of the sequence is written
@@ -311,6 +320,7 @@ __attribute__((amdgpu_waves_per_eu(RLds<D, TM, F32IN>::WPE))) void read_kernel(c
     }
 
     __syncthreads();  // Q and K dead in every wave
+    if (lockstep) __builtin_amdgcn_s_setprio(1);
     // 3c. W^T into the Q / K area as bf16 hi and lo planes: row f, the four
     //     nodes 16 mb + 4 g .. +3 of this lane
 #pragma unroll
@@ -344,6 +354,7 @@ __attribute__((amdgpu_waves_per_eu(RLds<D, TM, F32IN>::WPE))) void read_kernel(c
         }
     }
     __syncthreads();
+    if (lockstep) __builtin_amdgcn_s_setprio(0);
 
     // 4. O^T = (S0 Q^T) diag(P_j) + U^T W
 #pragma unroll
