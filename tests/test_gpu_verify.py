@@ -170,6 +170,16 @@ def test_unsupported_sizes_raise(ldv):
         ldv.verify_chain(q, q, q, a, a, S0)
 
 
+@pytest.mark.parametrize("T", [44, 64])
+def test_verify_one_round_grid(ldv, orc, T):
+    """512 heads at 64 nodes: staged stores on a grid of one round, where the
+    waves also lower their issue priority as they advance; with three node
+    blocks in use (T = 44) and four (T = 64)."""
+    wl = WORKLOADS["tree64"].replace(B=32, H=16, D=128, T=T, seed=4500 + T)
+    x = make_inputs(wl, with_gather=False)
+    compare_verify(ldv, orc, x, "bf16", False, "one round T%d" % T)
+
+
 @pytest.mark.parametrize("T,topology,qkv", [(5, "chain", "bf16"), (13, "tree", "bf16"), (16, "tree", "f32"),
                                             (1, "chain", "bf16"), (21, "chain", "bf16"), (29, "tree", "f32"),
                                             (40, "tree", "bf16"), (36, "tree", "f32"), (57, "chain", "bf16"),
