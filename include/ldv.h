@@ -311,7 +311,7 @@ int ldv_select_accepted(int B, int T, int V, int logits_dtype, const void* logit
  * workspace, with the partial results in an array of the library instead: a
  * fixed 48 KiB (6144 entries) per GPU, reserved on each GPU the library runs
  * on until the process ends, its address resolved on the first call on that
- * GPU.  Every split the selection makes fits it; a larger one would return
+ * GPU (the GPU of `stream`, or the current GPU for the null stream).  Every split the selection makes fits it; a larger one would return
  * LDV_ERR_UNSUPPORTED.  Results are those of ldv_select_accepted.  Every call
  * on a GPU shares that GPU's array: calls that overlap on one GPU (on
  * different streams, or from different host threads) race and must be

@@ -303,7 +303,7 @@ LDV_EXPORT int ldv_select_accepted_noalloc(int B, int T, int V, int logits_dtype
     ldv::ArgPart* part = nullptr;
     if (np > 1) {
         if (rows * np > ldv::kSelectScratchParts) return LDV_ERR_UNSUPPORTED;  // beyond the array (no valid split is)
-        if (ldv::select_scratch(&part) != hipSuccess) return LDV_ERR_LAUNCH;
+        if (ldv::select_scratch(static_cast<hipStream_t>(stream), &part) != hipSuccess) return LDV_ERR_LAUNCH;
     }
     return select_launch(B, T, V, logits_dtype, logits, tokens, parent, target, accepted, accepted_len, bonus, status,
                          np, part, stream);

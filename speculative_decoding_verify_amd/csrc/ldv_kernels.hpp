@@ -115,8 +115,9 @@ int select_parts(long long rows, int V);
 // ceil(4096 / rows) parts each).
 constexpr long long kSelectScratchParts = 6144;
 
-// The current GPU's address of that workspace (resolved once per device).
-hipError_t select_scratch(ArgPart** out);
+// The address of that workspace on the GPU the stream belongs to (the
+// current GPU for the null stream), resolved once per device.
+hipError_t select_scratch(hipStream_t stream, ArgPart** out);
 
 // Each launcher assumes arguments already validated by the C ABI layer and
 // returns the HIP launch status.

@@ -91,17 +91,35 @@ ArgPart* g_scratch_ptr[kMaxDevices];  // the array's device address on each GPU 
 }  // namespace
 
 // In host code `scratch` names a host-side handle, not device memory: its
-// device address on the current GPU is resolved once per device, with that
-// device current, and only that address is handed to kernels.
-hipError_t select_scratch(ArgPart** out) {
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
+// device address is resolved once per device, with that device current, and
+// only that address is handed to kernels.  The device is the one the
+// kernels will run on: the stream's (the current device for the null
+// stream); a stream of another device makes that device current for the
+// lookup, and the caller's device is restored.
+hipError_t select_scratch(hipStream_t stream, ArgPart** out) {
+    int cur = 0;
+    hipError_t e = hipGetDevice(&cur);
     if (e != hipSuccess) return e;
+    int dev = cur;
+    if (stream) {
+        hipDevice_t sd = 0;
+        e = hipStreamGetDevice(stream, &sd);
+        if (e != hipSuccess) return e;
+        dev = sd;
+    }
     if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
     std::lock_guard<std::mutex> lock(g_scratch_mu);
     if (!g_scratch_ptr[dev]) {
+        if (dev != cur) {
+            e = hipSetDevice(dev);
+            if (e != hipSuccess) return e;
+        }
         void* p = nullptr;
         e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (dev != cur) {
+            const hipError_t r = hipSetDevice(cur);
+            if (e == hipSuccess) e = r;
+        }
         if (e != hipSuccess) return e;
         if (!p) return hipErrorInvalidSymbol;
         g_scratch_ptr[dev] = static_cast<ArgPart*>(p);

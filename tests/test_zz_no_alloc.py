@@ -77,3 +77,23 @@ def test_noalloc_rows_split_as_with_a_workspace(ldv):
         B, T, V = first[:3]
         assert ldv.select_workspace_bytes(B, T, V) > 0
         assert ldv.select_workspace_bytes(B, T, V) // 8 <= 6144
+
+
+def test_noalloc_on_a_side_stream(ldv):
+    """With a stream passed, the array's address is the one on that stream's
+    GPU (here a second stream of the current GPU): the results equal those
+    of the workspace call."""
+    lg, tok, par, sel, parent = inputs(9300, 64, 16, 151936, "bf16", "chain")
+    B, T1, V = lg.shape
+    ws = torch.empty(ldv.select_workspace_bytes(B, T1 - 1, V), dtype=torch.uint8, device="cuda")
+    ref = ldv.select_accepted(lg, tok, par, workspace=ws)
+    outs = [torch.full((B, T1), -7, dtype=torch.int32, device="cuda")] + \
+           [torch.full((B,), -7, dtype=torch.int32, device="cuda") for _ in range(3)]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    got = ldv.select_accepted_noalloc(lg, tok, outs[0], outs[1], parent=par, accepted_len=outs[2], bonus=outs[3],
+                                      stream=side)
+    side.synchronize()
+    torch.cuda.synchronize()
+    for name, r, g in zip(("target", "accepted", "accepted_len", "bonus"), ref, got):
+        assert torch.equal(r, g), name
