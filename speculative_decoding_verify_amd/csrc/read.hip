@@ -103,6 +103,8 @@ __attribute__((amdgpu_waves_per_eu(RLds<D, TM, F32IN>::WPE))) void read_kernel(c
     // lowers its priority as it advances (3, then 2 after staging, 1 once Q
     // and K are dead, 0 for step 4), so that issue goes to the waves that are
     // behind: tree-64 20.4 -> 19.5 us, GDN-1.3B 9.85 -> 9.55 us.
+    // blocks of this kernel resident per CU: what its LDS and its register
+    // bound (waves per SIMD) allow
     constexpr int RES = (163840 / (int)L::total) < (4 * L::WPE / NW) ? (163840 / (int)L::total) : (4 * L::WPE / NW);
     const bool lockstep = gridDim.x <= (unsigned)(RES * kCus);
     if (lockstep) __builtin_amdgcn_s_setprio(3);

@@ -241,6 +241,8 @@ void verify_kernel(const VerifyArgs pa) {
     // waves that are behind (tree-64 21.9 -> 21.65 us, its step 33.3 -> 32.55
     // us).  Only on grids of one round: where rounds overlap it held back the
     // blocks the next round waits for.
+    // blocks of this kernel resident per CU: what its LDS and its register
+    // bound (waves per SIMD) allow
     constexpr int RES = (163840 / (int)L::total) < (4 * L::WPE / NW) ? (163840 / (int)L::total) : (4 * L::WPE / NW);
     const bool lockstep = TM == 64 && STG && !CMT && gridDim.x <= (unsigned)(RES * kCus);
     if (lockstep) __builtin_amdgcn_s_setprio(3);
