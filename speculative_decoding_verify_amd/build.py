@@ -1,5 +1,5 @@
-"""Build the HIP library libldv.so (and the measurement probe libldv_peaks.so)
-in-tree for gfx950 with hipcc."""
+"""Build the HIP library libldv.so (and the measurement probe libldv_peaks.so
+and the test helpers libldv_checks.so) in-tree for gfx950 with hipcc."""
 from __future__ import annotations
 
 import os
@@ -16,6 +16,9 @@ SOURCES = ["verify.hip", "commit.hip", "gather.hip", "read.hip", "select.hip", "
 # that libldv.so exports exactly the calls include/ldv.h declares
 PEAKS_LIB = os.path.join(HERE, "libldv_peaks.so")
 PEAKS_SOURCES = ["peaks.hip"]
+# device helpers of the library run on caller data, for the tests only
+CHECKS_LIB = os.path.join(HERE, "libldv_checks.so")
+CHECKS_SOURCES = ["checks.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -46,9 +49,10 @@ def build(verbose: bool = False, jobs: int = 4) -> str:
         return obj
 
     with ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(compile_one, SOURCES + PEAKS_SOURCES))
-    nmain = len(SOURCES)
-    for lib, lobjs in ((LIB, objs[:nmain]), (PEAKS_LIB, objs[nmain:])):
+        objs = list(ex.map(compile_one, SOURCES + PEAKS_SOURCES + CHECKS_SOURCES))
+    nmain, npeaks = len(SOURCES), len(PEAKS_SOURCES)
+    for lib, lobjs in ((LIB, objs[:nmain]), (PEAKS_LIB, objs[nmain:nmain + npeaks]),
+                       (CHECKS_LIB, objs[nmain + npeaks:])):
         tmp = lib + ".tmp%d" % os.getpid()
         cmd = [HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC"] + lobjs + ["-o", tmp]
         if verbose:
